@@ -1,0 +1,305 @@
+"""Thin ctypes binding of libfsd.so (include/fsd.h).
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+libfsd.so.  Tensors must live on the GPU; each call enqueues on torch's
+current stream.  The library is loaded on first use and a missing or
+unloadable library raises FsdError — there is no fallback of any kind.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "FsdError", "library_path", "lib", "abi_version", "lora_merge", "workspace_bytes",
+    "lora_down", "lora_up", "lora_linear", "renoise", "euler_step", "token_embed",
+    "token_head", "EPI_NONE", "EPI_SWIGLU",
+]
+
+EPI_NONE = 0
+EPI_SWIGLU = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libfsd.so")
+_lib = None
+
+_STATUS = {0: "FSD_OK", 1: "FSD_EINVAL", 2: "FSD_EALIGN", 3: "FSD_EUNSUPPORTED",
+           4: "FSD_EWORKSPACE", 5: "FSD_EHIP"}
+
+
+class FsdError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {_STATUS.get(status, status)}")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+_c_void_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_f32 = ctypes.c_float
+_int = ctypes.c_int
+
+_SIGS = {
+    "fsd_abi_version": ([], _int),
+    "fsd_status_str": ([_int], ctypes.c_char_p),
+    "fsd_lora_merge": ([_int, ctypes.POINTER(_c_void_p), ctypes.POINTER(_c_void_p),
+                        ctypes.POINTER(_i64), _c_void_p, _i64, _i64, _c_void_p, _c_void_p,
+                        _c_void_p], _int),
+    "fsd_lora_linear_workspace_bytes": ([_i64, _i64], ctypes.c_size_t),
+    "fsd_lora_down": ([_c_void_p, _i64, _c_void_p, _f32, _c_void_p, _i64, _i64, _i64, _i64,
+                       _c_void_p], _int),
+    "fsd_lora_up": ([_c_void_p, _i64, _c_void_p, _c_void_p, _i64, _c_void_p, _c_void_p,
+                     _c_void_p, _i64, _c_void_p, _i64, _i64, _i64, _i64, _i64, _int,
+                     _c_void_p], _int),
+    "fsd_lora_linear": ([_c_void_p, _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                         _c_void_p, _i64, _f32, _c_void_p, _i64, _i64, _i64, _i64, _i64, _int,
+                         _c_void_p, ctypes.c_size_t, _c_void_p], _int),
+    "fsd_renoise": ([_c_void_p, _c_void_p, _f32, _c_void_p, _i64, _c_void_p], _int),
+    "fsd_euler_step": ([_c_void_p, _c_void_p, _f32, _f32, _i64, _c_void_p], _int),
+    "fsd_token_embed": ([_c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64, _i64, _c_void_p],
+                        _int),
+    "fsd_token_head": ([_c_void_p, _i64, _c_void_p, _c_void_p, _i64, _i64, _i64, _c_void_p],
+                       _int),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """Load libfsd.so (once).  Raises FsdError-like RuntimeError when absent."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"HIP library not built: {_LIB_PATH} is missing "
+                               "(run __graft_entry__.build())")
+        L = ctypes.CDLL(_LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = L
+    return _lib
+
+
+def abi_version() -> int:
+    return lib().fsd_abi_version()
+
+
+# ------------------------------------------------------------------ helpers
+def _check(fn: str, status: int):
+    if status != 0:
+        raise FsdError(fn, status)
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t: torch.Tensor, name: str, dtype, dims=2):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != dims:
+        raise ValueError(f"{name} must be {dims}-D")
+    if dims == 2 and t.stride(1) != 1:
+        raise ValueError(f"{name} must have unit column stride")
+    if dims == 1 and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _ld(t: torch.Tensor) -> int:
+    return t.stride(0) if t.size(0) > 1 else max(t.stride(0), t.size(1))
+
+
+# ------------------------------------------------------------------ a0 merge
+def lora_merge(A_list, B_list, scales=None, out_A=None, out_B=None):
+    """Rank-axis merge of fp32 adapters into bf16 A [R, K] and B [N, R]."""
+    n = len(A_list)
+    if n == 0 or len(B_list) != n:
+        raise ValueError("need matching, non-empty adapter lists")
+    K = A_list[0].shape[1]
+    N = B_list[0].shape[0]
+    ranks = [a.shape[0] for a in A_list]
+    for a, b, r in zip(A_list, B_list, ranks):
+        _need(a, "A_i", torch.float32)
+        _need(b, "B_i", torch.float32)
+        if not (a.is_contiguous() and b.is_contiguous()):
+            raise ValueError("adapter factors must be contiguous")
+        if a.shape[1] != K or b.shape != (N, r):
+            raise ValueError("inconsistent adapter shapes")
+    R = sum(ranks)
+    dev = A_list[0].device
+    if out_A is None:
+        out_A = torch.empty((R, K), dtype=torch.bfloat16, device=dev)
+    if out_B is None:
+        out_B = torch.empty((N, R), dtype=torch.bfloat16, device=dev)
+    ap = (_c_void_p * n)(*[a.data_ptr() for a in A_list])
+    bp = (_c_void_p * n)(*[b.data_ptr() for b in B_list])
+    rk = (_i64 * n)(*ranks)
+    sc = None
+    if scales is not None:
+        sc_arr = (ctypes.c_float * n)(*[float(s) for s in scales])
+        sc = ctypes.cast(sc_arr, _c_void_p)
+    st = lib().fsd_lora_merge(n, ap, bp, rk, sc, K, N, _ptr(out_A), _ptr(out_B),
+                              _stream(out_A))
+    _check("fsd_lora_merge", st)
+    return out_A, out_B
+
+
+# ------------------------------------------------------------ LoRA linear
+def workspace_bytes(M: int, r: int) -> int:
+    return int(lib().fsd_lora_linear_workspace_bytes(M, r))
+
+
+def lora_down(X, A, scale=1.0, T=None):
+    """Phase A: T = bf16(scale · X·Aᵀ)."""
+    _need(X, "X", torch.bfloat16)
+    _need(A, "A", torch.bfloat16)
+    M, K = X.shape
+    r = A.shape[0]
+    if T is None:
+        T = torch.empty((M, r), dtype=torch.bfloat16, device=X.device)
+    _need(T, "T", torch.bfloat16)
+    st = lib().fsd_lora_down(_ptr(X), _ld(X), _ptr(A), float(scale), _ptr(T), _ld(T), M, K, r,
+                             _stream(X))
+    _check("fsd_lora_down", st)
+    return T
+
+
+def _out_cols(N, epilogue):
+    return N // 2 if epilogue == EPI_SWIGLU else N
+
+
+def _epi(epilogue):
+    if isinstance(epilogue, str):
+        return {"none": EPI_NONE, "swiglu": EPI_SWIGLU}[epilogue]
+    return int(epilogue)
+
+
+def lora_up(X, W0, T, B, bias=None, residual=None, epilogue=EPI_NONE, out=None):
+    """Phase B: Y = epi([X | T]·[W0 | B]ᵀ + bias) (+ residual)."""
+    epilogue = _epi(epilogue)
+    _need(X, "X", torch.bfloat16)
+    _need(W0, "W0", torch.bfloat16)
+    M, K = X.shape
+    N = W0.shape[0]
+    r = 0 if B is None else B.shape[1]
+    if r:
+        _need(T, "T", torch.bfloat16)
+        _need(B, "B", torch.bfloat16)
+    if bias is not None:
+        _need(bias, "bias", torch.float32, dims=1)
+    if residual is not None:
+        _need(residual, "residual", torch.bfloat16)
+    if out is None:
+        out = torch.empty((M, _out_cols(N, epilogue)), dtype=torch.bfloat16, device=X.device)
+    _need(out, "out", torch.bfloat16)
+    st = lib().fsd_lora_up(_ptr(X), _ld(X), _ptr(W0), _ptr(T) if r else None,
+                           _ld(T) if r else 0, _ptr(B) if r else None, _ptr(bias),
+                           _ptr(residual), _ld(residual) if residual is not None else 0,
+                           _ptr(out), _ld(out), M, N, K, r, epilogue, _stream(X))
+    _check("fsd_lora_up", st)
+    return out
+
+
+def lora_linear(X, W0, A, B, scale=1.0, bias=None, residual=None, epilogue=EPI_NONE,
+                out=None, workspace=None):
+    """Y = epi(X·W0ᵀ + scale·(X·Aᵀ)·Bᵀ + bias) (+ residual), phase A then phase B."""
+    epilogue = _epi(epilogue)
+    _need(X, "X", torch.bfloat16)
+    _need(W0, "W0", torch.bfloat16)
+    M, K = X.shape
+    N = W0.shape[0]
+    r = 0 if A is None else A.shape[0]
+    if r:
+        _need(A, "A", torch.bfloat16)
+        _need(B, "B", torch.bfloat16)
+    if bias is not None:
+        _need(bias, "bias", torch.float32, dims=1)
+    if residual is not None:
+        _need(residual, "residual", torch.bfloat16)
+    if out is None:
+        out = torch.empty((M, _out_cols(N, epilogue)), dtype=torch.bfloat16, device=X.device)
+    _need(out, "out", torch.bfloat16)
+    if workspace is None and r:
+        workspace = torch.empty(max(workspace_bytes(M, r), 16), dtype=torch.uint8,
+                                device=X.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().fsd_lora_linear(_ptr(X), _ld(X), _ptr(W0), _ptr(A) if r else None,
+                               _ptr(B) if r else None, _ptr(bias), _ptr(residual),
+                               _ld(residual) if residual is not None else 0, float(scale),
+                               _ptr(out), _ld(out), M, N, K, r, epilogue, _ptr(workspace),
+                               ws_bytes, _stream(X))
+    _check("fsd_lora_linear", st)
+    return out
+
+
+# ------------------------------------------------------------ sampler
+def renoise(u, eps, sigma, out=None):
+    """z = (1 - sigma)·u + sigma·eps (fp32, any shape, contiguous)."""
+    for t, nm in ((u, "u"), (eps, "eps")):
+        if t.device.type != "cuda" or t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError(f"{nm} must be a contiguous fp32 GPU tensor")
+    if u.shape != eps.shape:
+        raise ValueError("u and eps shapes differ")
+    if out is None:
+        out = torch.empty_like(u)
+    if out.shape != u.shape or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous fp32 tensor shaped like u")
+    st = lib().fsd_renoise(_ptr(u), _ptr(eps), float(sigma), _ptr(out), u.numel(), _stream(u))
+    _check("fsd_renoise", st)
+    return out
+
+
+def euler_step(z, v, sigma, sigma_next):
+    """z <- z + (sigma_next - sigma)·v, in place."""
+    for t, nm in ((z, "z"), (v, "v")):
+        if t.device.type != "cuda" or t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError(f"{nm} must be a contiguous fp32 GPU tensor")
+    if z.numel() != v.numel():
+        raise ValueError("z and v sizes differ")
+    st = lib().fsd_euler_step(_ptr(z), _ptr(v), float(sigma), float(sigma_next), z.numel(),
+                              _stream(z))
+    _check("fsd_euler_step", st)
+    return z
+
+
+# ------------------------------------------------------------ stand-in
+def token_embed(z, E, out=None):
+    """X = bf16(z·Eᵀ): z fp32 [M, C], E bf16 [D, C] -> X bf16 [M, D]."""
+    if z.device.type != "cuda" or z.dtype != torch.float32 or not z.is_contiguous() or z.dim() != 2:
+        raise ValueError("z must be a contiguous fp32 [M, C] GPU tensor")
+    _need(E, "E", torch.bfloat16)
+    M, C = z.shape
+    D = E.shape[0]
+    if out is None:
+        out = torch.empty((M, D), dtype=torch.bfloat16, device=z.device)
+    _need(out, "out", torch.bfloat16)
+    st = lib().fsd_token_embed(_ptr(z), _ptr(E), _ptr(out), _ld(out), M, C, D, _stream(z))
+    _check("fsd_token_embed", st)
+    return out
+
+
+def token_head(H, P, out=None):
+    """v = H·Pᵀ: H bf16 [M, D], P bf16 [C, D] -> v fp32 [M, C]."""
+    _need(H, "H", torch.bfloat16)
+    _need(P, "P", torch.bfloat16)
+    M, D = H.shape
+    C = P.shape[0]
+    if out is None:
+        out = torch.empty((M, C), dtype=torch.float32, device=H.device)
+    if out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous fp32 tensor")
+    st = lib().fsd_token_head(_ptr(H), _ld(H), _ptr(P), _ptr(out), M, D, C, _stream(H))
+    _check("fsd_token_head", st)
+    return out

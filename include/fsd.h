@@ -1,0 +1,203 @@
+/*
+ * fsd.h — C ABI of the hot path of a three-step video refiner on AMD MI355X
+ * (gfx950): the LoRA-fused linear that every refinement step evaluates, and
+ * the renoise / Euler arithmetic on the latent around it.
+ *
+ * Sources (the method's definition):
+ *   [EN]  "Open-H3-Regenerate-2K: High-Resolution Video Refinement with
+ *          Few-Step Diffusion" (agientry.com, English article)
+ *   [CW]  "Open-H3-Regenerate-2K：MiniMax H3 的开源 4K 精修方案"
+ *          (comfyui-wiki.com news page)
+ *
+ * Conventions shared by every entry point
+ *   - All data pointers are DEVICE pointers (hipMalloc'd or equivalent), except
+ *     where a parameter says "host".  The caller owns every buffer, including
+ *     the workspace; the library never allocates, frees or synchronises and
+ *     keeps no state between calls (calls are reentrant).
+ *   - bf16 means IEEE binary32 truncated to its top 16 bits (bfloat16), stored
+ *     as 2-byte little-endian words.  fp32 is IEEE binary32.
+ *   - Matrices are row-major.  "ld" is the row stride in ELEMENTS.
+ *   - Every bf16 matrix pointer must be 16-byte aligned and every ld a
+ *     multiple of 8 elements, so each row starts on a 16-byte boundary;
+ *     fp32 vectors of the sampler must be 16-byte aligned.
+ *   - stream is a hipStream_t; NULL means the default stream.  Calls enqueue
+ *     and return.  The returned status covers argument validation (done before
+ *     any HIP call) and the launch itself (FSD_EHIP if the launch failed).
+ *     Faults inside a kernel surface at the caller's next synchronisation.
+ *   - Nothing is printed and no exception crosses the boundary.
+ *   - All kernels are deterministic: the same inputs give bitwise-identical
+ *     outputs (no atomics, no split reductions whose order varies).
+ */
+#ifndef FSD_H
+#define FSD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FSD_ABI_VERSION 1
+
+typedef enum {
+  FSD_OK = 0,
+  FSD_EINVAL = 1,        /* null pointer, bad size, bad ld, illegal aliasing, non-finite sigma */
+  FSD_EALIGN = 2,        /* pointer or ld not 16-byte aligned                                   */
+  FSD_EUNSUPPORTED = 3,  /* valid request that this build does not implement                    */
+  FSD_EWORKSPACE = 4,    /* workspace null or too small                                         */
+  FSD_EHIP = 5           /* the HIP runtime reported an error when launching                    */
+} fsd_status;
+
+typedef enum {
+  FSD_EPI_NONE = 0,      /* Y = acc (+ bias) (+ residual)                                   */
+  FSD_EPI_SWIGLU = 1     /* Y[:, j] = silu(acc[:, j]) * acc[:, F + j], F = N / 2 (see below) */
+} fsd_epilogue;
+
+/* Version of this header's ABI (FSD_ABI_VERSION). */
+int fsd_abi_version(void);
+
+/* Static, NUL-terminated name of a status code ("FSD_OK", ...); never NULL. */
+const char* fsd_status_str(int status);
+
+/* ------------------------------------------------------------------------ *
+ * a0. Rank-axis merge of several LoRA adapters into one                      *
+ * ------------------------------------------------------------------------ *
+ * [CW] section "三个步如何完成工作": the refiner (rank 384), the Turbo
+ * adapter (rank 128) and the Sharp adapter (rank 64) are merged into one
+ * rank-576 LoRA by concatenating their factors along the rank axis, stored in
+ * fp32.  Concatenation along rank makes B·A equal the sum of the adapters'
+ * B_i·A_i, which is what the merge check on that page verifies.
+ *
+ *   A = [A_0; A_1; ...]              (rows stacked)      -> bf16 [R, K]
+ *   B = [s_0·B_0 | s_1·B_1 | ...]    (columns stacked)   -> bf16 [N, R]
+ *   R = sum of ranks[i]
+ *
+ * A_list, B_list, ranks, scales: HOST arrays of n_adapters entries.
+ *   A_list[i]: device fp32 [ranks[i], K] row-major (ld = K).
+ *   B_list[i]: device fp32 [N, ranks[i]] row-major (ld = ranks[i]).
+ *   scales:    per-adapter strength s_i folded into B_i; NULL means all 1.
+ * A_out: device bf16 [R, K]; B_out: device bf16 [N, R].
+ * Each output element is s_i·b rounded once to fp32 (exact when s_i = 1) and
+ * then to bf16 by round-to-nearest-even: the result is bit-exact.
+ * Requirements: 1 <= n_adapters <= 16, ranks[i] >= 1, K >= 1, N >= 1,
+ * A_out/B_out 16-byte aligned; outputs must not overlap inputs.
+ */
+int fsd_lora_merge(int n_adapters, const float* const* A_list,
+                   const float* const* B_list, const int64_t* ranks,
+                   const float* scales, int64_t K, int64_t N,
+                   void* A_out, void* B_out, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * a2 + a3 (+ a4). LoRA-fused linear                                         *
+ * ------------------------------------------------------------------------ *
+ * [CW] section "三个步如何完成工作": each of the transformer's adapted linear
+ * layers carries the merged rank-576 LoRA; [EN] section "Three steps instead
+ * of dozens": every refinement step is one call of that transformer.  A linear
+ * layer with a LoRA computes
+ *
+ *   Y = X·W0ᵀ + s·(X·Aᵀ)·Bᵀ (+ bias) (+ residual)
+ *
+ * evaluated here as two kernels:
+ *   phase A (fsd_lora_down):  T = bf16(s · X·Aᵀ)                [M, r]
+ *   phase B (fsd_lora_up):    Y = [X | T]·[W0 | B]ᵀ + bias ...  one MFMA
+ *                             K-loop over K + r columns, then the epilogue.
+ * T is the only intermediate; it lives in the caller's workspace.
+ *
+ * Operands (all bf16 unless noted):
+ *   X   [M, K]  row stride ldx >= K            (tokens x in_features)
+ *   W0  [N, K]  row stride K                   (out_features x in_features)
+ *   A   [r, K]  row stride K                   (merged down-projection)
+ *   B   [N, r]  row stride r                   (merged up-projection)
+ *   bias fp32 [N] or NULL
+ *   residual [M, Nout] row stride ldr, or NULL; may be the SAME pointer as Y
+ *            with ldr == ldy (in-place residual add).  Not allowed with SWIGLU.
+ *   Y   [M, Nout] row stride ldy >= Nout;  Nout = N, or N/2 with SWIGLU.
+ *   scale: s (fp32, finite).  Applied to T before T is rounded to bf16.
+ *   epilogue FSD_EPI_SWIGLU: the N accumulator columns are read as [G | U]
+ *            halves (gate first, F = N/2) and Y = silu(G)·U elementwise,
+ *            silu(g) = g / (1 + exp(-g)); bias is added to both halves before
+ *            the activation.
+ * Accumulation is fp32; Y is rounded to bf16 (round-to-nearest-even).
+ * Sizes: M >= 0 (M == 0 is a no-op), K >= 8, N >= 8, r >= 0 (r == 0 gives the
+ * plain GEMM), K, N, r multiples of 8, SWIGLU needs N a multiple of 16.
+ * Aliasing: Y must not overlap X, W0, A, B, bias or the workspace.
+ */
+
+/* Bytes of workspace phase A needs for M rows at rank r (M*r*2). */
+size_t fsd_lora_linear_workspace_bytes(int64_t M, int64_t r);
+
+/* Phase A alone.  T: bf16 [M, r] with row stride ldt >= r. */
+int fsd_lora_down(const void* X, int64_t ldx, const void* A, float scale,
+                  void* T, int64_t ldt, int64_t M, int64_t K, int64_t r,
+                  void* stream);
+
+/* Phase B alone: Y = epi([X | T]·[W0 | B]ᵀ + bias) (+ residual), T as written
+ * by fsd_lora_down (ldt >= r).  With r == 0, T and B are ignored. */
+int fsd_lora_up(const void* X, int64_t ldx, const void* W0, const void* T,
+                int64_t ldt, const void* B, const float* bias,
+                const void* residual, int64_t ldr, void* Y, int64_t ldy,
+                int64_t M, int64_t N, int64_t K, int64_t r, int epilogue,
+                void* stream);
+
+/* Phase A then phase B, chunked over M so that T fits in the workspace.
+ * workspace_bytes must hold at least min(M, 256) rows of T
+ * (fsd_lora_linear_workspace_bytes(min(M, 256), r)); more lets the chunks be
+ * larger (one chunk when it holds all M rows).  With r == 0 the workspace
+ * may be NULL. */
+int fsd_lora_linear(const void* X, int64_t ldx, const void* W0, const void* A,
+                    const void* B, const float* bias, const void* residual,
+                    int64_t ldr, float scale, void* Y, int64_t ldy, int64_t M,
+                    int64_t N, int64_t K, int64_t r, int epilogue,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * a1. Partial renoise                                                        *
+ * ------------------------------------------------------------------------ *
+ * [EN] section "Three steps instead of dozens", renoise equation: the
+ * upscaled latent is re-noised to sigma_0 with standard Gaussian noise,
+ *   z = (1 - sigma)·u + sigma·eps        (elementwise, fp32, n elements)
+ * u, eps, z: fp32 [n], 16-byte aligned.  z may be the same pointer as u or
+ * eps; no other overlap.  sigma finite.  n >= 0 (0 is a no-op).
+ */
+int fsd_renoise(const float* u, const float* eps, float sigma, float* z,
+                int64_t n, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * a5. One Euler step of the sampler                                          *
+ * ------------------------------------------------------------------------ *
+ * [EN] section "Three steps instead of dozens", schedule and update:
+ *   z <- z + (sigma_next - sigma)·v      (in place, fp32, n elements)
+ * with sigma 0.909 -> 0.857 -> 0.667 -> 0 passed by the caller.  The step
+ * (sigma_next - sigma) is formed in fp32.  z, v: fp32 [n], 16-byte aligned;
+ * v must not partially overlap z.  sigma, sigma_next finite.  n >= 0.
+ */
+int fsd_euler_step(float* z, const float* v, float sigma, float sigma_next,
+                   int64_t n, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * Token embed / head of the velocity stand-in (2K three-step sweep)          *
+ * ------------------------------------------------------------------------ *
+ * The pages give neither the transformer's widths nor its input and output
+ * projections; these two calls carry a synthetic stand-in's projections
+ * between the 24-channel latent (channel-last, one token per latent voxel;
+ * [EN] section "Why upscaling happens in latent space", shape equation) and
+ * the model width D.
+ *
+ * fsd_token_embed:  X[m, n] = bf16( sum_c z[m, c]·E[n, c] ),  fp32 sums.
+ *   z fp32 [M, C] (row stride C), E bf16 [D, C] (row stride C),
+ *   X bf16 [M, D] row stride ldx >= D.  1 <= C <= 64, D multiple of 8.
+ * fsd_token_head:   v[m, c] = sum_n H[m, n]·P[c, n],  fp32 sums, fp32 out.
+ *   H bf16 [M, D] row stride ldh >= D, P bf16 [C, D] (row stride D),
+ *   v fp32 [M, C] (row stride C).  1 <= C <= 32, D multiple of 64.
+ */
+int fsd_token_embed(const float* z, const void* E, void* X, int64_t ldx,
+                    int64_t M, int64_t C, int64_t D, void* stream);
+int fsd_token_head(const void* H, int64_t ldh, const void* P, float* v,
+                   int64_t M, int64_t D, int64_t C, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FSD_H */
