@@ -1,0 +1,240 @@
+"""Benchmark of the refiner's hot path on one MI355X.
+
+One step = the whole hot path over the 2K grid: renoise a 24-channel
+37x90x160 latent (532,800 tokens) at sigma 0.909, then three times
+[velocity stand-in = embed, QKV, O(V)+res, gate/up+SwiGLU, down+res, head —
+every linear a LoRA-fused linear with the merged rank-576 adapter — then one
+Euler update], sigma 0.909 -> 0.857 -> 0.667 -> 0.
+
+Prints ONE JSON line on stdout (everything else goes to stderr):
+  value      algorithmic TFLOP/s of the whole step (inputs resident in HBM)
+  roofline   the dominant kernel (phase B of the gate/up linear, SwiGLU
+             epilogue): its algorithmic flops per launch / its mean launch
+             time from HIP events on its stream, against 2500 TFLOP/s bf16
+  kernels    the same for every kernel of the step
+  elementwise  renoise / Euler GB/s at the 2K and 4K latents, cache-cold
+             (a 1 GiB write between repetitions), 12 bytes per element
+  cpu_baseline the fp64 oracle on a bounded sample of tokens on host cores
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+DOMINANT = "gate_up.up"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-elementwise", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target host time of the oracle sample")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="run one 1 GiB device copy first (a known-size kernel for counters)")
+    ap.add_argument("--traffic", type=str, default=None,
+                    help="JSON file with measured HBM bytes per launch of the dominant kernel")
+    return ap.parse_args()
+
+
+def kernel_times(events):
+    """Per-name list of durations (ms) between consecutive marks."""
+    out = {}
+    for (name, a), (_, b) in zip(events[:-1], events[1:]):
+        out.setdefault(name, []).append(a.elapsed_time(b))
+    return out
+
+
+def elementwise(torch, fsd, inputs):
+    """Cold renoise / Euler bandwidth at the 2K and 4K latents."""
+    dev = torch.device("cuda:0")
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    res = {}
+    for wid, tag in ((2, "2k"), (3, "4k")):
+        n = inputs.WORKLOADS[wid].latent_elems
+        u = torch.randn(n, device=dev)
+        e = torch.randn(n, device=dev)
+        z = torch.empty(n, device=dev)
+        for name in ("renoise", "euler"):
+            ts = []
+            for rep in range(12):
+                flush.fill_(rep & 0xff)
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record()
+                if name == "renoise":
+                    fsd.renoise(u, e, 0.909, out=z)
+                else:
+                    fsd.euler_step(z, e, 0.909, 0.857)
+                b.record()
+                torch.cuda.synchronize()
+                if rep >= 2:
+                    ts.append(a.elapsed_time(b))
+            med = statistics.median(ts)
+            gbs = 12.0 * n / (med * 1e-3) / 1e9
+            res[f"{name}_{tag}"] = {"us": round(med * 1e3, 2), "GB/s": round(gbs, 1),
+                                    "frac_hbm": round(gbs / PEAK_HBM_GBS, 3),
+                                    "bytes": 12 * n}
+        del u, e, z
+    del flush
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(model_flops_per_token, target_s):
+    """The fp64 oracle on a bounded sample of tokens of the same step."""
+    import numpy as np
+    import oracle
+    from few_step_diffusion_amd import inputs
+    layers = []
+    for L in inputs.standin_layers(4):
+        Ab, Bb = oracle.merge_bf16([a.numpy() for a in L["A_list"]],
+                                   [b.numpy() for b in L["B_list"]])
+        layers.append({"W0": L["W0"].float().numpy(),
+                       "A": oracle.bf16_value(Ab).reshape(Ab.shape),
+                       "B": oracle.bf16_value(Bb).reshape(Bb.shape)})
+    E, P = inputs.standin_projections(4)
+    E, P = E.float().numpy(), P.float().numpy()
+    u, eps = inputs.latent(4, tokens=4096)
+    u, eps = u.numpy(), eps.numpy()
+    threads = oracle.default_threads()
+    # calibrate on one token per thread, then size the sample to the target time
+    t0 = time.perf_counter()
+    oracle.standin_refine(u[:threads], eps[:threads], E, P, layers, nthreads=threads)
+    t1 = time.perf_counter() - t0
+    tokens = int(max(threads, min(4096, threads * max(1.0, target_s / max(t1, 1e-3)))))
+    tokens = (tokens // threads) * threads
+    t0 = time.perf_counter()
+    oracle.standin_refine(u[:tokens], eps[:tokens], E, P, layers, nthreads=threads)
+    dt = time.perf_counter() - t0
+    tflops = tokens * model_flops_per_token / dt / 1e12
+    return {"value": round(tflops, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{tokens} of 532,800 tokens of the same step (renoise + 3 stand-in "
+                      f"velocity evaluations + Euler), fp64, {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        sys.exit("bench.py runs on one GPU only: this build has no multi-GPU path "
+                 "(each GPU would take a contiguous token range; see DESIGN.md)")
+    import torch
+    import few_step_diffusion_amd as fsd
+    from few_step_diffusion_amd import inputs
+    from few_step_diffusion_amd.refine import StandinRefiner
+
+    dev = torch.device("cuda:0")
+    fsd.lib()
+    wl = inputs.WORKLOADS[4]
+    M = wl.tokens
+    if args.calib_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    log(f"building the stand-in for {M} tokens ...")
+    model = StandinRefiner(M, device=dev)
+    u, eps = inputs.latent(4)
+    u, eps = u.to(dev), eps.to(dev)
+    torch.cuda.synchronize()
+    for w in range(args.warmup):
+        model.refine(u, eps)
+        torch.cuda.synchronize()
+        log(f"warmup {w + 1}/{args.warmup} done")
+    per_kernel = {}
+    step_ms = []
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for s in range(args.steps):
+        model.events = []
+        model.refine(u, eps)
+        torch.cuda.synchronize()
+        ev = model.events
+        step_ms.append(ev[0][1].elapsed_time(ev[-1][1]))
+        for k, v in kernel_times(ev).items():
+            per_kernel.setdefault(k, []).extend(v)
+        log(f"step {s + 1}/{args.steps}: {step_ms[-1]:.2f} ms")
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t_start) / args.steps * 1e3
+    model.events = None
+
+    flops = model.flops_per_step()
+    total_flops = sum(flops.values())
+    ms = statistics.mean(step_ms)
+    value = total_flops / (ms * 1e-3) / 1e12
+    steps_per_refine = 3
+    kernels = {}
+    for name, ts in per_kernel.items():
+        mean = statistics.mean(ts)
+        ent = {"launches_per_step": len(ts) // args.steps, "mean_us": round(mean * 1e3, 1)}
+        if name in flops:
+            per_launch = flops[name] / steps_per_refine
+            ent["tflops"] = round(per_launch / (mean * 1e-3) / 1e12, 1)
+            ent["frac_peak"] = round(ent["tflops"] / PEAK_BF16_TFLOPS, 4)
+        if name in ("renoise", "euler"):
+            ent["GB/s"] = round(12.0 * model.M * model.C / (mean * 1e-3) / 1e9, 1)
+        kernels[name] = ent
+    lora_flops = sum(v for k, v in flops.items() if k.endswith(".down") or k.endswith(".up"))
+    lora_ms = sum(statistics.mean(per_kernel[k]) * len(per_kernel[k]) / args.steps
+                  for k in per_kernel if k.endswith(".down") or k.endswith(".up"))
+    dom = kernels[DOMINANT]
+    L = model.layers[2]
+    dom_flops = 2 * M * (L["K"] + model.R) * L["N"]
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        with open(args.traffic) as f:
+            traffic = json.load(f).get("bytes_per_launch")
+    roofline = {"kernel": "lora_up (phase B) of the gate/up linear, SwiGLU epilogue: "
+                          f"M={M} K={L['K']}+{model.R} N={L['N']}",
+                "bound": "mfma", "achieved": round(dom_flops / (dom["mean_us"] * 1e-6) / 1e12, 1),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(dom_flops / (dom["mean_us"] * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic, "flops_per_launch": dom_flops}
+    out = {
+        "metric": "LoRA-linear TFLOP/s & % bf16 MFMA peak at 2K grid; renoise/Euler HBM GB/s",
+        "value": round(value, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 3), "wall_ms_per_step": round(wall, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "2K three-step sweep: renoise + 3 x (4-layer LoRA stand-in "
+                               "d=3072 ffn=8192 r=576=384|128|64 + Euler) over a 24x37x90x160 "
+                               "latent", "tokens": M, "global_batch": M, "seq_len": M,
+                   "parallelism": "single GPU"},
+        "lora_linear": {"tflops": round(lora_flops / (lora_ms * 1e-3) / 1e12, 1),
+                        "frac_peak": round(lora_flops / (lora_ms * 1e-3) / 1e12 /
+                                           PEAK_BF16_TFLOPS, 4),
+                        "ms_per_step": round(lora_ms, 3)},
+        "roofline": roofline,
+        "kernels": kernels,
+    }
+    del model
+    torch.cuda.empty_cache()
+    if not args.no_elementwise:
+        log("elementwise cold-cache timing ...")
+        out["elementwise"] = elementwise(torch, fsd, inputs)
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        out["cpu_baseline"] = cpu_baseline(total_flops / M, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

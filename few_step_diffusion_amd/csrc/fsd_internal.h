@@ -1,0 +1,49 @@
+// Internal declarations shared by the HIP translation units of libfsd.so.
+// Not part of the public ABI (include/fsd.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fsd {
+
+typedef uint16_t bf16_t;   // bfloat16 storage word
+
+// One MFMA GEMM launch: Y = epi(alpha · [A0 | A1]·[B0 | B1]ᵀ + bias) (+ res).
+// Segment 0 runs over K0 columns of (A0, B0), segment 1 over K1 columns of
+// (A1, B1); K1 == 0 disables segment 1.  A* are [M, K*] with row stride lda*,
+// B* are [N, K*] with row stride ldb*.  With SwiGLU the N accumulator columns
+// are [gate | up] halves and Y has N/2 columns.
+struct GemmParams {
+  const bf16_t* A0; int64_t lda0;
+  const bf16_t* B0; int64_t ldb0;
+  const bf16_t* A1; int64_t lda1;
+  const bf16_t* B1; int64_t ldb1;
+  int64_t M, N, K0, K1;
+  float alpha;
+  const float* bias;
+  const bf16_t* res; int64_t ldr;
+  bf16_t* Y; int64_t ldy;
+};
+
+enum GemmKind {
+  GEMM_DOWN = 0,     // phase A: T = bf16(alpha · X·Aᵀ), N = rank (tile 256 x 192)
+  GEMM_UP = 1,       // phase B, plain / bias / residual epilogue (tile 256 x 256)
+  GEMM_UP_SWIGLU = 2 // phase B with the SwiGLU epilogue
+};
+
+hipError_t launch_gemm(GemmKind kind, const GemmParams& p, hipStream_t s);
+
+hipError_t launch_renoise(const float* u, const float* eps, float sigma, float* z,
+                          int64_t n, hipStream_t s);
+hipError_t launch_euler(float* z, const float* v, float dsigma, int64_t n, hipStream_t s);
+hipError_t launch_merge_rows(const float* src, int64_t rows, int64_t cols, bf16_t* dst,
+                             int64_t ld_dst, hipStream_t s);
+hipError_t launch_merge_cols(const float* src, int64_t rows, int64_t cols, float scale,
+                             bf16_t* dst, int64_t ld_dst, hipStream_t s);
+hipError_t launch_embed(const float* z, const bf16_t* E, bf16_t* X, int64_t ldx, int64_t M,
+                        int C, int64_t D, hipStream_t s);
+hipError_t launch_head(const bf16_t* H, int64_t ldh, const bf16_t* P, float* v, int64_t M,
+                       int64_t D, int C, hipStream_t s);
+
+}  // namespace fsd

@@ -1,0 +1,107 @@
+"""The three-step refine loop over a 2K latent with a synthetic 4-layer velocity
+stand-in whose linears all carry the merged rank-576 LoRA.
+
+Method ("Open-H3-Regenerate-2K: High-Resolution Video Refinement with Few-Step
+Diffusion", agientry.com, section "Three steps instead of dozens"): re-noise
+the upscaled latent to sigma_0 = 0.909, then one velocity evaluation and one
+Euler update per step along 0.909 -> 0.857 -> 0.667 -> 0, classifier-free
+guidance off.  The real transformer's widths and weights are not available;
+the stand-in per token is
+
+    x = z·Eᵀ;  q = L_qkv(x);  h = x + L_o(q[:, 2D:3D]);
+    h = h + L_down(SwiGLU(L_gu(h)));  v = h·Pᵀ
+
+with every L_* the LoRA-fused linear.  Every call below is one HIP kernel of
+libfsd.so (through the ctypes binding); torch only allocates device memory
+and supplies the stream.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import binding as fsd
+from . import inputs
+
+SIGMAS = (0.909, 0.857, 0.667, 0.0)
+
+
+class StandinRefiner:
+    """Device-resident weights and activation buffers for M tokens."""
+
+    LAYER_NAMES = ("qkv", "o", "gate_up", "down")
+
+    def __init__(self, M: int, device="cuda:0", wid: int = 4, D: int = inputs.STANDIN_D,
+                 F: int = inputs.STANDIN_F, ranks=inputs.RANKS, C: int = inputs.LATENT_C,
+                 scale: float = 1.0):
+        dev = torch.device(device)
+        self.M, self.D, self.F, self.C, self.dev = M, D, F, C, dev
+        self.R = sum(ranks)
+        self.scale = scale
+        self.layers = []
+        for L in inputs.standin_layers(wid, D, F, ranks):
+            A, B = fsd.lora_merge([a.to(dev) for a in L["A_list"]],
+                                  [b.to(dev) for b in L["B_list"]])
+            self.layers.append({"W0": L["W0"].to(dev), "A": A, "B": B,
+                                "K": L["K"], "N": L["N"]})
+        E, P = inputs.standin_projections(wid, C, D)
+        self.E, self.P = E.to(dev), P.to(dev)
+        bf = torch.bfloat16
+        self.h = torch.empty((M, D), dtype=bf, device=dev)            # residual stream
+        self.qkv = torch.empty((M, 3 * D), dtype=bf, device=dev)
+        self.g = torch.empty((M, F), dtype=bf, device=dev)            # SwiGLU output
+        self.T = torch.empty((M, self.R), dtype=bf, device=dev)      # LoRA down output
+        self.v = torch.empty((M, C), dtype=torch.float32, device=dev)
+        self.z = torch.empty((M, C), dtype=torch.float32, device=dev)
+        self.events = None
+
+    # one LoRA linear = phase A + phase B (two kernels)
+    def _linear(self, idx, X, out, residual=None, epilogue=fsd.EPI_NONE):
+        L = self.layers[idx]
+        T = self.T[: X.shape[0]]
+        self._mark(f"{self.LAYER_NAMES[idx]}.down")
+        fsd.lora_down(X, L["A"], self.scale, T)
+        self._mark(f"{self.LAYER_NAMES[idx]}.up")
+        fsd.lora_up(X, L["W0"], T, L["B"], residual=residual, epilogue=epilogue, out=out)
+
+    def _mark(self, name):
+        if self.events is not None:
+            ev = torch.cuda.Event(enable_timing=True)
+            ev.record()
+            self.events.append((name, ev))
+
+    def velocity(self):
+        """v = stand-in(z) for the current latent self.z."""
+        D = self.D
+        self._mark("embed")
+        fsd.token_embed(self.z, self.E, out=self.h)
+        self._linear(0, self.h, self.qkv)
+        self._linear(1, self.qkv[:, 2 * D:3 * D], self.h, residual=self.h)
+        self._linear(2, self.h, self.g, epilogue=fsd.EPI_SWIGLU)
+        self._linear(3, self.g, self.h, residual=self.h)
+        self._mark("head")
+        fsd.token_head(self.h, self.P, out=self.v)
+        return self.v
+
+    def refine(self, u, eps, sigmas=SIGMAS):
+        """Renoise u with eps at sigmas[0], then one Euler step per sigma pair."""
+        self._mark("renoise")
+        fsd.renoise(u, eps, sigmas[0], out=self.z)
+        for k in range(len(sigmas) - 1):
+            self.velocity()
+            self._mark("euler")
+            fsd.euler_step(self.z, self.v, sigmas[k], sigmas[k + 1])
+        self._mark("end")
+        return self.z
+
+    def flops_per_step(self) -> dict:
+        """Algorithmic flops of one refine (all sigma steps): 2M(KN + Kr + rN) per linear."""
+        M, D, F, C, r = self.M, self.D, self.F, self.C, self.R
+        steps = len(SIGMAS) - 1
+        out = {}
+        for L, name in zip(self.layers, self.LAYER_NAMES):
+            K, N = L["K"], L["N"]
+            out[name + ".down"] = 2 * M * K * r * steps
+            out[name + ".up"] = 2 * M * (K + r) * N * steps
+        out["embed"] = 2 * M * C * D * steps
+        out["head"] = 2 * M * D * C * steps
+        return out

@@ -186,7 +186,7 @@ int fsd_euler_step(float* z, const float* v, float sigma, float sigma_next,
  *
  * fsd_token_embed:  X[m, n] = bf16( sum_c z[m, c]·E[n, c] ),  fp32 sums.
  *   z fp32 [M, C] (row stride C), E bf16 [D, C] (row stride C),
- *   X bf16 [M, D] row stride ldx >= D.  1 <= C <= 64, D multiple of 8.
+ *   X bf16 [M, D] row stride ldx >= D.  1 <= C <= 32, D multiple of 8.
  * fsd_token_head:   v[m, c] = sum_n H[m, n]·P[c, n],  fp32 sums, fp32 out.
  *   H bf16 [M, D] row stride ldh >= D, P bf16 [C, D] (row stride D),
  *   v fp32 [M, C] (row stride C).  1 <= C <= 32, D multiple of 64.

@@ -69,7 +69,11 @@ def lib():
             ctypes.c_int, F64P, ctypes.c_int]
         L.oracle_lora_linear_drows.argtypes = [
             F64P, ctypes.c_int64, ctypes.c_int64, F32P, F32P, F32P, ctypes.c_double,
-            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, F64P]
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, F64P, ctypes.c_int]
+        L.oracle_embed_rows.argtypes = [F32P, ctypes.c_int64, F32P, ctypes.c_int64,
+                                        ctypes.c_int64, F64P]
+        L.oracle_head_rows.argtypes = [F32P, ctypes.c_int64, ctypes.c_int64, F32P,
+                                       ctypes.c_int64, ctypes.c_int64, F64P]
         L.oracle_renoise.argtypes = [F32P, F32P, ctypes.c_double, F64P, ctypes.c_int64]
         L.oracle_euler_step.argtypes = [F64P, F64P, ctypes.c_double, ctypes.c_double,
                                         ctypes.c_int64]
@@ -96,6 +100,18 @@ def _f64(a) -> np.ndarray:
 
 def _p(a, t):
     return None if a is None else a.ctypes.data_as(t)
+
+
+def default_threads() -> int:
+    """Host threads for the oracle: OMP_NUM_THREADS if set, else min(cores, 16)."""
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        return int(env)
+    return max(1, min(os.cpu_count() or 1, 16))
+
+
+def _nt(n):
+    return int(n) if n and n > 0 else default_threads()
 
 
 def bf16_bits(x) -> np.ndarray:
@@ -181,11 +197,11 @@ def lora_linear_rows(X, W0, A, B, scale=1.0, bias=None, residual=None, rows=None
         X.ctypes.data_as(F32P), X.shape[1], _p(rows_a, I64P), nrows, W0.ctypes.data_as(F32P),
         A.ctypes.data_as(F32P), B.ctypes.data_as(F32P), _p(bias, F32P), _p(residual, F32P),
         0 if residual is None else residual.shape[1], float(scale), N, K, r, int(bool(swiglu)),
-        Y.ctypes.data_as(F64P), int(nthreads))
+        Y.ctypes.data_as(F64P), _nt(nthreads))
     return Y
 
 
-def lora_linear_drows(Xd, W0, A, B, scale=1.0):
+def lora_linear_drows(Xd, W0, A, B, scale=1.0, nthreads=0):
     """The linear map (no bias) applied to float64 rows Xd [n, K]."""
     Xd = _f64(np.atleast_2d(Xd))
     W0 = _f32(W0)
@@ -197,8 +213,32 @@ def lora_linear_drows(Xd, W0, A, B, scale=1.0):
     lib().oracle_lora_linear_drows(Xd.ctypes.data_as(F64P), K, Xd.shape[0],
                                    W0.ctypes.data_as(F32P), A.ctypes.data_as(F32P),
                                    B.ctypes.data_as(F32P), float(scale), N, K, r,
-                                   Y.ctypes.data_as(F64P))
+                                   Y.ctypes.data_as(F64P), _nt(nthreads))
     return Y
+
+
+def embed_rows(z, E):
+    """x = z·Eᵀ for fp32 latent rows z [T, C] and E [D, C]; float64 [T, D]."""
+    z = _f32(np.atleast_2d(z))
+    E = _f32(E)
+    T, C = z.shape
+    D = E.shape[0]
+    x = np.empty((T, D), np.float64)
+    lib().oracle_embed_rows(z.ctypes.data_as(F32P), T, E.ctypes.data_as(F32P), C, D,
+                            x.ctypes.data_as(F64P))
+    return x
+
+
+def head_rows(H, P):
+    """v = H·Pᵀ for rows H [T, D] and P [C, D]; float64 [T, C]."""
+    H = _f32(np.atleast_2d(H))
+    P = _f32(P)
+    T, D = H.shape
+    C = P.shape[0]
+    v = np.empty((T, C), np.float64)
+    lib().oracle_head_rows(H.ctypes.data_as(F32P), T, D, P.ctypes.data_as(F32P), C, D,
+                           v.ctypes.data_as(F64P))
+    return v
 
 
 # ------------------------------------------------------------ sampler
@@ -273,7 +313,7 @@ def standin_refine(x0, eps, E, P, layers, sigmas=SIGMAS, nthreads=0):
     lib().oracle_standin_refine(x0.ctypes.data_as(F32P), eps.ctypes.data_as(F32P), T,
                                 s.ctypes.data_as(F64P), len(s), E.ctypes.data_as(F32P),
                                 P.ctypes.data_as(F32P), C, D, F, arr, z.ctypes.data_as(F64P),
-                                v.ctypes.data_as(F64P), int(nthreads))
+                                v.ctypes.data_as(F64P), _nt(nthreads))
     return z, v
 
 

@@ -238,16 +238,25 @@ void oracle_lora_linear_rows(const float* X, int64_t ldx, const int64_t* rows,
 }
 
 /* Same linear map applied to double-precision rows (used to evaluate
-   Freivalds' identity w·Y = (w·X)·W0ᵀ + s((w·X)·Aᵀ)·Bᵀ + (Σw)·bias on a
-   row that is itself a combination of input rows). */
+   Freivalds' identity w·Y = (w·X)·W0ᵀ + s((w·X)·Aᵀ)·Bᵀ on a row that is
+   itself a combination of input rows; no bias). */
+typedef struct {
+  const double* X; int64_t ldx;
+  const float *W0, *A, *B; double s; int64_t N, K, r; double* Y;
+} lora_drows_ctx;
+
+static void lora_drows_one(int64_t i, void* p, double* scratch) {
+  lora_drows_ctx* c = (lora_drows_ctx*)p;
+  lora_row(c->X + i * c->ldx, c->K, c->W0, c->A, c->B, NULL, c->s, c->N, c->r, scratch,
+           c->Y + i * c->N);
+}
+
 void oracle_lora_linear_drows(const double* X, int64_t ldx, int64_t nrows,
                               const float* W0, const float* A, const float* B,
                               double scale, int64_t N, int64_t K, int64_t r,
-                              double* Y_out) {
-  double* t = (double*)malloc(sizeof(double) * (size_t)(r > 0 ? r : 1));
-  for (int64_t i = 0; i < nrows; ++i)
-    lora_row(X + i * ldx, K, W0, A, B, NULL, scale, N, r, t, Y_out + i * N);
-  free(t);
+                              double* Y_out, int nthreads) {
+  lora_drows_ctx c = {X, ldx, W0, A, B, scale, N, K, r, Y_out};
+  parallel_for(nrows, nthreads, r > 0 ? r : 1, lora_drows_one, &c);
 }
 
 /* ------------------------------------------------------------------ */
@@ -303,6 +312,44 @@ void oracle_sampler_exact_velocity(const float* x0, const float* eps,
 /* Pins: zero sublayers collapse it to v = z·(P·E)ᵀ; tokens are          */
 /* independent (row permutation).                                        */
 /* ------------------------------------------------------------------ */
+/* Stand-in projections between the C-channel latent and width D:
+   embed x[n] = sum_c z[c]·E[n, c] (E [D, C]); head v[c] = sum_n h[n]·P[c, n]
+   (P [C, D]).  Pins: zero sublayers reduce the stand-in to z·(P·E)ᵀ. */
+static void embed_row(const double* z, const float* E, int64_t C, int64_t D, double* x) {
+  for (int64_t n = 0; n < D; ++n) {
+    double acc = 0.0;
+    for (int64_t ch = 0; ch < C; ++ch) acc += z[ch] * (double)E[n * C + ch];
+    x[n] = acc;
+  }
+}
+
+static void head_row(const double* h, const float* P, int64_t C, int64_t D, double* v) {
+  for (int64_t ch = 0; ch < C; ++ch) {
+    double acc = 0.0;
+    for (int64_t n = 0; n < D; ++n) acc += h[n] * (double)P[ch * D + n];
+    v[ch] = acc;
+  }
+}
+
+void oracle_embed_rows(const float* z, int64_t ntok, const float* E, int64_t C, int64_t D,
+                       double* x_out) {
+  double zr[64];
+  for (int64_t i = 0; i < ntok; ++i) {
+    for (int64_t ch = 0; ch < C && ch < 64; ++ch) zr[ch] = (double)z[i * C + ch];
+    embed_row(zr, E, C, D, x_out + i * D);
+  }
+}
+
+void oracle_head_rows(const float* H, int64_t ntok, int64_t ldh, const float* P, int64_t C,
+                      int64_t D, double* v_out) {
+  double* h = (double*)malloc(sizeof(double) * (size_t)D);
+  for (int64_t i = 0; i < ntok; ++i) {
+    for (int64_t n = 0; n < D; ++n) h[n] = (double)H[i * ldh + n];
+    head_row(h, P, C, D, v_out + i * C);
+  }
+  free(h);
+}
+
 typedef struct {
   const float *W0, *A, *B, *bias;
   int64_t N, K, r;
@@ -329,11 +376,7 @@ static void standin_velocity(const standin_ctx* c, const double* z, double* v,
   double* gu = o + D;             /* 2F  */
   double* g = gu + 2 * F;         /* F   */
   double* t = g + F;              /* max r */
-  for (int64_t n = 0; n < D; ++n) {
-    double acc = 0.0;
-    for (int64_t ch = 0; ch < C; ++ch) acc += z[ch] * (double)c->E[n * C + ch];
-    x[n] = acc;
-  }
+  embed_row(z, c->E, C, D, x);
   const oracle_lora_layer* L = c->L;
   lora_row(x, D, L[0].W0, L[0].A, L[0].B, L[0].bias, L[0].scale, 3 * D, L[0].r, t, q);
   lora_row(q + 2 * D, D, L[1].W0, L[1].A, L[1].B, L[1].bias, L[1].scale, D, L[1].r, t, o);
@@ -342,11 +385,7 @@ static void standin_velocity(const standin_ctx* c, const double* z, double* v,
   swiglu_row(gu, F, g);
   lora_row(g, F, L[3].W0, L[3].A, L[3].B, L[3].bias, L[3].scale, D, L[3].r, t, o);
   for (int64_t n = 0; n < D; ++n) h[n] = h[n] + o[n];
-  for (int64_t ch = 0; ch < C; ++ch) {
-    double acc = 0.0;
-    for (int64_t n = 0; n < D; ++n) acc += h[n] * (double)c->P[ch * D + n];
-    v[ch] = acc;
-  }
+  head_row(h, c->P, C, D, v);
 }
 
 static void standin_token(int64_t i, void* p, double* ws) {

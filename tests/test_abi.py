@@ -1,0 +1,149 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/fsd.h declares, and rejects invalid arguments with the documented
+status before making any HIP call.  Pointers here are plain addresses that
+are never dereferenced (validation only looks at their values)."""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+import few_step_diffusion_amd as fsd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fsd.h")
+
+OK, EINVAL, EALIGN, EUNSUP, EWS = 0, 1, 2, 3, 4
+P = ctypes.c_void_p
+
+
+def declared():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(fsd_\w+)\s*\(", txt, re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(fsd.library_path()):
+        from few_step_diffusion_amd import build
+        build.build()
+    return fsd.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared()
+    assert len(names) >= 10
+    out = subprocess.run(["nm", "-D", "--defined-only", fsd.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (fsd_\w+)", out))
+    for n in names:
+        assert n in exported, n
+        assert getattr(L, n) is not None
+
+
+def test_version_and_status_strings(L):
+    assert L.fsd_abi_version() == 1
+    assert L.fsd_status_str(0) == b"FSD_OK"
+    assert L.fsd_status_str(4) == b"FSD_EWORKSPACE"
+    assert L.fsd_status_str(99) == b"FSD_UNKNOWN"
+    assert L.fsd_lora_linear_workspace_bytes(532800, 576) == 532800 * 576 * 2
+    assert L.fsd_lora_linear_workspace_bytes(0, 576) == 0
+
+
+BASE = 0x100000000
+
+
+def a(i):
+    return P(BASE + i * 0x10000000)
+
+
+def up(L, **kw):
+    args = dict(X=a(1), ldx=1024, W0=a(2), T=a(3), ldt=576, B=a(4), bias=None, res=None,
+                ldr=0, Y=a(5), ldy=1024, M=1200, N=1024, K=1024, r=576, epi=0)
+    args.update(kw)
+    return L.fsd_lora_up(args["X"], args["ldx"], args["W0"], args["T"], args["ldt"], args["B"],
+                         args["bias"], args["res"], args["ldr"], args["Y"], args["ldy"],
+                         args["M"], args["N"], args["K"], args["r"], args["epi"], None)
+
+
+def test_lora_up_validation(L):
+    assert up(L, X=None) == EINVAL
+    assert up(L, X=P(BASE + 0x10000008)) == EALIGN
+    assert up(L, K=1020, ldx=1020) == EINVAL
+    assert up(L, N=1004) == EINVAL
+    assert up(L, r=20, ldt=24) == EINVAL
+    assert up(L, ldx=1000) == EINVAL                      # ld < K
+    assert up(L, epi=7) == EINVAL
+    assert up(L, epi=1, N=1032) == EINVAL                 # SwiGLU needs N % 16 == 0
+    assert up(L, epi=1, res=a(6), ldr=512) == EUNSUP      # no residual with SwiGLU
+    assert up(L, Y=P(BASE + 0x10000000 + 4096)) == EINVAL  # Y overlaps X
+    assert up(L, res=P(BASE + 5 * 0x10000000 + 4096), ldr=1024) == EINVAL  # partial overlap
+    assert up(L, M=-1) == EINVAL
+    assert up(L, M=0) == OK                               # empty: no launch
+    assert up(L, M=0, res=a(5), ldr=1024) == OK           # in-place residual is legal
+    assert up(L, N=65536, K=32768, ldx=32768, ldy=65536) == EUNSUP   # > 32-bit offsets
+
+
+def test_lora_linear_workspace(L):
+    def lin(ws, wsb, M=1200, r=576, A=a(3)):
+        return L.fsd_lora_linear(a(1), 1024, a(2), A, a(4), None, None, 0, ctypes.c_float(1.0),
+                                 a(5), 1024, M, 1024, 1024, r, 0, ws, wsb, None)
+    assert lin(None, 0) == EWS
+    assert lin(a(7), 256 * 576 * 2 - 2) == EWS
+    assert lin(a(7), 256 * 576 * 2, M=0) == OK
+    assert lin(None, 0, M=0, r=0, A=None) == OK
+    assert lin(P(BASE + 7 * 0x10000000 + 8), 10 ** 9) == EALIGN
+    assert lin(P(BASE + 5 * 0x10000000), 10 ** 9) == EINVAL   # workspace == Y
+    assert L.fsd_lora_linear(a(1), 1024, a(2), a(3), a(4), None, None, 0,
+                             ctypes.c_float(math.nan), a(5), 1024, 16, 1024, 1024, 576, 0,
+                             a(7), 10 ** 9, None) == EINVAL
+
+
+def test_lora_down_validation(L):
+    def down(**kw):
+        args = dict(X=a(1), ldx=1024, A=a(2), s=1.0, T=a(3), ldt=576, M=100, K=1024, r=576)
+        args.update(kw)
+        return L.fsd_lora_down(args["X"], args["ldx"], args["A"], ctypes.c_float(args["s"]),
+                               args["T"], args["ldt"], args["M"], args["K"], args["r"], None)
+    assert down(r=0) == EINVAL
+    assert down(T=None) == EINVAL
+    assert down(s=math.inf) == EINVAL
+    assert down(T=P(BASE + 3 * 0x10000000 + 2)) == EALIGN
+    assert down(T=P(BASE + 0x10000000 + 64)) == EINVAL    # T overlaps X
+    assert down(M=0) == OK
+
+
+def test_sampler_validation(L):
+    f = ctypes.c_float
+    assert L.fsd_renoise(a(1), a(2), f(0.909), a(3), 0, None) == OK
+    assert L.fsd_renoise(a(1), a(2), f(math.nan), a(3), 10, None) == EINVAL
+    assert L.fsd_renoise(a(1), a(2), f(0.5), P(BASE + 3 * 0x10000000 + 4), 10, None) == EALIGN
+    assert L.fsd_renoise(a(1), a(2), f(0.5), P(BASE + 0x10000000 + 16), 100, None) == EINVAL
+    assert L.fsd_renoise(None, a(2), f(0.5), a(3), 10, None) == EINVAL
+    assert L.fsd_renoise(a(1), a(2), f(0.5), a(3), -1, None) == EINVAL
+    assert L.fsd_euler_step(a(1), a(2), f(0.909), f(math.inf), 10, None) == EINVAL
+    assert L.fsd_euler_step(a(1), P(BASE + 0x10000000 + 16), f(0.9), f(0.8), 100, None) == EINVAL
+    assert L.fsd_euler_step(a(1), a(2), f(0.9), f(0.8), 0, None) == OK
+
+
+def test_standin_and_merge_validation(L):
+    assert L.fsd_token_embed(a(1), a(2), a(3), 3072, 10, 33, 3072, None) == EINVAL
+    assert L.fsd_token_embed(a(1), a(2), a(3), 3070, 10, 24, 3072, None) == EINVAL
+    assert L.fsd_token_embed(a(1), a(2), a(3), 3072, 0, 24, 3072, None) == OK
+    assert L.fsd_token_head(a(1), 3072, a(2), a(3), 10, 3000, 24, None) == EINVAL
+    assert L.fsd_token_head(a(1), 3072, a(2), P(BASE + 3 * 0x10000000 + 2), 10, 3072, 24,
+                            None) == EALIGN
+    arr = (P * 1)(a(1))
+    rk = (ctypes.c_int64 * 1)(8)
+    assert L.fsd_lora_merge(0, arr, arr, rk, None, 16, 16, a(2), a(3), None) == EINVAL
+    assert L.fsd_lora_merge(1, arr, arr, rk, None, 16, 16, P(BASE + 2 * 0x10000000 + 8), a(3),
+                            None) == EALIGN
+    assert L.fsd_lora_merge(1, arr, arr, rk, None, 16, 16, a(2), a(2), None) == EINVAL
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        fsd.renoise(torch.zeros(8), torch.zeros(8), 0.5)

@@ -1,0 +1,356 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Small cases compare every output element; full-size cases (768P, 2K, one 4K
+chunk, the 2K three-step stand-in) compare sampled rows exactly and, for the
+linear layers without SwiGLU, every 256-row tile through Freivalds' identity
+w_bᵀY_b = (w_bᵀX_b)·W0ᵀ + s((w_bᵀX_b)·Aᵀ)·Bᵀ + (Σw_b)·bias evaluated by the
+oracle.  Gates: bf16 GEMM outputs max-over-rows rel-L2 and rel-max <= 2e-2;
+fp32 sampler per-token rel-L2 <= 1e-5; merge bit-exact.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import few_step_diffusion_amd as fsd
+import oracle
+from oracle import metrics
+from few_step_diffusion_amd import inputs
+from few_step_diffusion_amd.refine import StandinRefiner
+
+pytestmark = pytest.mark.gpu
+
+TOL = metrics.GEMM_TOL
+
+
+def say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def f32(t):
+    return t.detach().float().cpu().numpy()
+
+
+def bits(t):
+    return t.detach().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def merged(wid, K, N, dev, layer=0, ranks=inputs.RANKS, scales=None):
+    """Merged adapters on the device (HIP merge) and their oracle float values."""
+    A_l, B_l = inputs.adapters(wid, K, N, layer=layer, ranks=ranks)
+    A, B = fsd.lora_merge([a.to(dev) for a in A_l], [b.to(dev) for b in B_l], scales)
+    Ab, Bb = oracle.merge_bf16([a.numpy() for a in A_l], [b.numpy() for b in B_l], scales)
+    return A, B, oracle.bf16_value(Ab).reshape(Ab.shape), oracle.bf16_value(Bb).reshape(Bb.shape)
+
+
+def assert_gemm(Y, ref, what):
+    ok, err = metrics.gemm_ok(Y, ref)
+    say(f"{what}: rel_l2 {err[0]:.3e} rel_max {err[1]:.3e}")
+    assert ok, (what, err)
+
+
+def freivalds_tiles(X, Y, W0f, Af, Bf, bias=None, scale=1.0, seed=0, block=256, what=""):
+    """Check every `block`-row tile of Y = X·W0ᵀ + s(X·Aᵀ)·Bᵀ + bias."""
+    dev = X.device
+    M, K = X.shape
+    N = Y.shape[1]
+    nb = (M + block - 1) // block
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    w = torch.randn(M, generator=g, device=dev, dtype=torch.float64)
+    xt = torch.zeros((nb, K), dtype=torch.float64, device=dev)
+    yt = torch.zeros((nb, N), dtype=torch.float64, device=dev)
+    ws = torch.zeros(nb, dtype=torch.float64, device=dev)
+    step = 64 * block
+    for r0 in range(0, M, step):
+        r1 = min(M, r0 + step)
+        idx = torch.arange(r0, r1, device=dev) // block
+        wc = w[r0:r1, None]
+        xt.index_add_(0, idx, wc * X[r0:r1].double())
+        yt.index_add_(0, idx, wc * Y[r0:r1].double())
+        ws.index_add_(0, idx, w[r0:r1])
+    exp = oracle.lora_linear_drows(xt.cpu().numpy(), W0f, Af, Bf, scale=scale)
+    if bias is not None:
+        exp = exp + ws.cpu().numpy()[:, None] * bias.astype(np.float64)[None, :]
+    assert_gemm(yt.cpu().numpy(), exp, f"{what} Freivalds over {nb} tiles")
+
+
+# ----------------------------------------------------------------- merge
+def test_merge_bit_exact(gpu):
+    say("merge K=N=1024 ranks 384|128|64, scales 1, 0.7, 1.3")
+    for scales in (None, [1.0, 0.7, 1.3]):
+        A_l, B_l = inputs.adapters(0, 1024, 1024)
+        A, B = fsd.lora_merge([a.to(gpu) for a in A_l], [b.to(gpu) for b in B_l], scales)
+        Ab, Bb = oracle.merge_bf16([a.numpy() for a in A_l], [b.numpy() for b in B_l], scales)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(A), Ab)
+        assert np.array_equal(bits(B), Bb)
+
+
+# ------------------------------------------------------------ small GEMMs
+def test_lora_linear_tiny_all_rows(gpu):
+    wl = inputs.WORKLOADS[0]
+    _, K, N, _ = wl.linears[0]
+    M = wl.tokens
+    say(f"tiny workload M={M} K={K} N={N} r=576 bias")
+    X = inputs.activations(0, M, K)
+    W0 = inputs.base_weight(0, K, N)
+    bias = inputs.bias(0, N)
+    A, B, Af, Bf = merged(0, K, N, gpu)
+    Y = fsd.lora_linear(X.to(gpu), W0.to(gpu), A, B, bias=bias.to(gpu))
+    ref = oracle.lora_linear_rows(f32(X), f32(W0), Af, Bf, bias=bias.numpy())
+    assert_gemm(f32(Y), ref, "tiny")
+
+
+@pytest.mark.parametrize("M", [1, 17, 255, 256, 257, 300, 513])
+@pytest.mark.parametrize("r,scale", [(64, 1.0), (0, 1.0), (576, 0.5)])
+def test_lora_linear_tails(gpu, M, r, scale):
+    K, N = 256, 320
+    say(f"tails M={M} K={K} N={N} r={r} scale={scale}")
+    X = inputs.normal((M, K), 1.0, 11 + M, dtype=torch.bfloat16)
+    W0 = inputs.normal((N, K), 0.05, 12, dtype=torch.bfloat16)
+    bias = inputs.normal((N,), 0.1, 13)
+    if r:
+        ranks = (r // 2, r // 4, r // 4)
+        A, B, Af, Bf = merged(7, K, N, gpu, ranks=ranks)
+    else:
+        A = B = Af = Bf = None
+    Y = fsd.lora_linear(X.to(gpu), W0.to(gpu), A, B, scale=scale, bias=bias.to(gpu))
+    ref = oracle.lora_linear_rows(f32(X), f32(W0), Af, Bf, scale=scale, bias=bias.numpy())
+    assert_gemm(f32(Y), ref, f"tails M={M} r={r}")
+
+
+@pytest.mark.parametrize("M,F", [(300, 320), (257, 128), (1, 64)])
+def test_swiglu(gpu, M, F):
+    K = 512
+    say(f"swiglu M={M} K={K} F={F} r=576 bias")
+    X = inputs.normal((M, K), 1.0, 21, dtype=torch.bfloat16)
+    W0 = inputs.normal((2 * F, K), 0.05, 22, dtype=torch.bfloat16)
+    bias = inputs.normal((2 * F,), 0.1, 23)
+    A, B, Af, Bf = merged(8, K, 2 * F, gpu)
+    H = fsd.lora_linear(X.to(gpu), W0.to(gpu), A, B, bias=bias.to(gpu), epilogue="swiglu")
+    ref = oracle.lora_linear_rows(f32(X), f32(W0), Af, Bf, bias=bias.numpy(), swiglu=True)
+    assert H.shape == (M, F)
+    assert_gemm(f32(H), ref, f"swiglu M={M} F={F}")
+
+
+def test_residual_separate_and_in_place(gpu):
+    M, K, N = 600, 384, 256
+    say(f"residual M={M} K={K} N={N}")
+    X = inputs.normal((M, K), 1.0, 31, dtype=torch.bfloat16)
+    W0 = inputs.normal((N, K), 0.05, 32, dtype=torch.bfloat16)
+    R = inputs.normal((M, N), 1.0, 33, dtype=torch.bfloat16)
+    A, B, Af, Bf = merged(9, K, N, gpu, ranks=(32, 16, 16))
+    ref = oracle.lora_linear_rows(f32(X), f32(W0), Af, Bf, residual=f32(R))
+    Y = fsd.lora_linear(X.to(gpu), W0.to(gpu), A, B, residual=R.to(gpu))
+    assert_gemm(f32(Y), ref, "residual separate")
+    Rd = R.to(gpu)
+    Y2 = fsd.lora_linear(X.to(gpu), W0.to(gpu), A, B, residual=Rd, out=Rd)
+    assert Y2.data_ptr() == Rd.data_ptr()
+    assert torch.equal(Y2.cpu(), Y.cpu())
+
+
+def test_strided_input_slice(gpu):
+    M, D = 300, 256
+    say(f"V-slice input M={M} D={D} ld=3D")
+    QKV = inputs.normal((M, 3 * D), 1.0, 41, dtype=torch.bfloat16)
+    W0 = inputs.normal((D, D), 0.05, 42, dtype=torch.bfloat16)
+    A, B, Af, Bf = merged(10, D, D, gpu, ranks=(64, 32, 32))
+    Qd = QKV.to(gpu)
+    Y = fsd.lora_linear(Qd[:, 2 * D:], W0.to(gpu), A, B)
+    ref = oracle.lora_linear_rows(f32(QKV[:, 2 * D:]), f32(W0), Af, Bf)
+    assert_gemm(f32(Y), ref, "V slice")
+
+
+def test_lora_down_alone(gpu):
+    M, K = 700, 1024
+    say(f"phase A M={M} K={K} r=576 scale=0.75")
+    X = inputs.activations(0, M, K)
+    A, _, Af, _ = merged(0, K, 64, gpu)
+    T = fsd.lora_down(X.to(gpu), A, 0.75)
+    ref = 0.75 * oracle.lora_linear_rows(f32(X), Af, None, None)   # X·Aᵀ as a plain linear
+    assert_gemm(f32(T), ref, "phase A")
+
+
+def test_chunked_workspace_is_bitwise_identical(gpu):
+    M, K, N = 1300, 512, 512
+    say(f"chunking M={M} with 256- and 512-row workspaces")
+    X = inputs.normal((M, K), 1.0, 51, dtype=torch.bfloat16).to(gpu)
+    W0 = inputs.normal((N, K), 0.05, 52, dtype=torch.bfloat16).to(gpu)
+    A, B, _, _ = merged(11, K, N, gpu)
+    full = fsd.lora_linear(X, W0, A, B)
+    for rows in (256, 512, 700):
+        ws = torch.empty(rows * 576 * 2, dtype=torch.uint8, device=gpu)
+        part = fsd.lora_linear(X, W0, A, B, workspace=ws)
+        assert torch.equal(part, full), rows
+
+
+def test_determinism(gpu):
+    M, K, N = 4099, 1024, 2048
+    say(f"determinism M={M} K={K} N={N}")
+    X = inputs.normal((M, K), 1.0, 61, dtype=torch.bfloat16).to(gpu)
+    W0 = inputs.normal((N, K), 0.02, 62, dtype=torch.bfloat16).to(gpu)
+    A, B, _, _ = merged(12, K, N, gpu)
+    a = fsd.lora_linear(X, W0, A, B)
+    b = fsd.lora_linear(X, W0, A, B)
+    c = fsd.lora_linear(X, W0, A, B, epilogue="swiglu")
+    d = fsd.lora_linear(X, W0, A, B, epilogue="swiglu")
+    assert torch.equal(a, b) and torch.equal(c, d)
+
+
+def test_nan_propagates_to_its_row_only(gpu):
+    M, K, N = 300, 256, 256
+    say("NaN row propagation")
+    X = inputs.normal((M, K), 1.0, 71, dtype=torch.bfloat16)
+    X[5, 17] = float("nan")
+    W0 = inputs.normal((N, K), 0.05, 72, dtype=torch.bfloat16)
+    A, B, _, _ = merged(13, K, N, gpu, ranks=(32, 16, 16))
+    Y = fsd.lora_linear(X.to(gpu), W0.to(gpu), A, B).cpu()
+    assert torch.isnan(Y[5]).all()
+    rest = torch.cat([Y[:5], Y[6:]])
+    assert torch.isfinite(rest).all()
+
+
+# ---------------------------------------------------------------- sampler
+def _sampler(gpu, x0, eps, in_place=False):
+    xd, ed = x0.to(gpu), eps.to(gpu)
+    if in_place:
+        z = xd.clone()
+        fsd.renoise(z, ed, oracle.SIGMAS[0], out=z)
+    else:
+        z = fsd.renoise(xd, ed, oracle.SIGMAS[0])
+    hist = [z.cpu().clone()]
+    v = ed - xd           # the exact flow-matching velocity, an input of the Euler step
+    for k in range(3):
+        fsd.euler_step(z, v, oracle.SIGMAS[k], oracle.SIGMAS[k + 1])
+        hist.append(z.cpu().clone())
+    return hist
+
+
+@pytest.mark.parametrize("wid", [0, 1, 2, 3])
+def test_sampler_full_latent(gpu, wid):
+    wl = inputs.WORKLOADS[wid]
+    say(f"sampler {wl.name}: {wl.latent_elems} elements")
+    x0, eps = inputs.latent(wid)
+    hist = _sampler(gpu, x0, eps, in_place=(wid == 0))
+    ref = oracle.sampler_exact_velocity(x0.numpy(), eps.numpy())
+    for k in range(4):
+        e = metrics.token_error(hist[k].numpy(), ref[k])
+        say(f"  sigma={oracle.SIGMAS[k]} token err {e:.2e}")
+        assert e <= metrics.SAMPLER_TOL, (k, e)
+    # closed form: the last step lands on x0
+    assert float((hist[-1] - x0).abs().max()) <= 1e-5
+
+
+@pytest.mark.parametrize("n", [0, 1, 3, 4, 5, 7, 1023, 4099])
+def test_sampler_ragged_lengths(gpu, n):
+    say(f"sampler flat n={n}")
+    u = inputs.normal((n,), 1.0, 81)
+    e = inputs.normal((n,), 1.0, 82)
+    z = fsd.renoise(u.to(gpu), e.to(gpu), 0.909)
+    v = (e - u).to(gpu)
+    fsd.euler_step(z, v, 0.909, 0.857)
+    ref = oracle.euler_step(oracle.renoise(u.numpy(), e.numpy(), 0.909),
+                            e.numpy().astype(np.float64) - u.numpy(), 0.909, 0.857)
+    got = z.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(got - ref) <= 1e-6 * np.maximum(1.0, np.abs(ref)))
+
+
+def test_sampler_nan_propagates(gpu):
+    u = torch.zeros(64)
+    u[10] = float("nan")
+    z = fsd.renoise(u.to(gpu), torch.ones(64, device=gpu), 0.909).cpu()
+    assert math.isnan(float(z[10])) and torch.isfinite(torch.cat([z[:10], z[11:]])).all()
+
+
+# ---------------------------------------------------------- embed / head
+def test_embed_and_head(gpu):
+    M, C, D = 1000, 24, 3072
+    say(f"embed/head M={M} C={C} D={D}")
+    z = inputs.normal((M, C), 1.0, 91)
+    E, P = inputs.standin_projections(4, C, D)
+    X = fsd.token_embed(z.to(gpu), E.to(gpu))
+    assert_gemm(f32(X), oracle.embed_rows(z.numpy(), f32(E)), "embed")
+    H = inputs.normal((M, D), 1.0, 92, dtype=torch.bfloat16)
+    v = fsd.token_head(H.to(gpu), P.to(gpu))
+    assert_gemm(v.cpu().numpy(), oracle.head_rows(f32(H), f32(P)), "head")
+
+
+# ------------------------------------------------------- full-size shapes
+def _full_linear(gpu, wid, label, K, N, layer=0, M=None, rows=384):
+    M = inputs.WORKLOADS[wid].tokens if M is None else M
+    say(f"{inputs.WORKLOADS[wid].name}: {label} M={M} K={K} N={N} r=576")
+    X = inputs.activations(wid, M, K, device=gpu, layer=layer)
+    W0 = inputs.base_weight(wid, K, N, layer=layer)
+    A, B, Af, Bf = merged(wid, K, N, gpu, layer=layer)
+    W0d = W0.to(gpu)
+    Y = fsd.lora_linear(X, W0d, A, B)
+    torch.cuda.synchronize()
+    sel = inputs.sample_rows(M, rows, seed=wid * 10 + layer)
+    seli = torch.from_numpy(sel).to(gpu)
+    ref = oracle.lora_linear_rows(f32(X[seli]), f32(W0), Af, Bf)
+    assert_gemm(f32(Y[seli]), ref, f"{label} sampled rows")
+    freivalds_tiles(X, Y, f32(W0), Af, Bf, seed=wid, what=label)
+    del X, Y
+    torch.cuda.empty_cache()
+
+
+def test_full_768p(gpu):
+    _, K, N, _ = inputs.WORKLOADS[1].linears[0]
+    _full_linear(gpu, 1, "768P linear", K, N)
+
+
+def test_full_2k_qkv_and_o(gpu):
+    for layer, (label, K, N, _) in enumerate(inputs.WORKLOADS[2].linears):
+        _full_linear(gpu, 2, f"2K {label}", K, N, layer=layer)
+
+
+def test_full_4k_chunk_gate_up_swiglu_then_down(gpu):
+    wl = inputs.WORKLOADS[3]
+    Mc = wl.tokens // wl.chunks
+    (_, K1, N1, _), (_, K2, N2, _) = wl.linears
+    say(f"{wl.name}: chunk M={Mc} gate/up {K1}->{N1} SwiGLU, down {K2}->{N2}")
+    X = inputs.activations(3, Mc, K1, device=gpu)
+    W1 = inputs.base_weight(3, K1, N1, layer=1)
+    W2 = inputs.base_weight(3, K2, N2, layer=2)
+    A1, B1, A1f, B1f = merged(3, K1, N1, gpu, layer=1)
+    A2, B2, A2f, B2f = merged(3, K2, N2, gpu, layer=2)
+    H = fsd.lora_linear(X, W1.to(gpu), A1, B1, epilogue="swiglu")
+    Y = fsd.lora_linear(H, W2.to(gpu), A2, B2)
+    torch.cuda.synchronize()
+    sel = inputs.sample_rows(Mc, 160, seed=3)
+    seli = torch.from_numpy(sel).to(gpu)
+    Href = oracle.lora_linear_rows(f32(X[seli]), f32(W1), A1f, B1f, swiglu=True)
+    assert_gemm(f32(H[seli]), Href, "4K gate/up SwiGLU sampled rows")
+    # the chain from X in fp64: the oracle's H (not the GPU's) feeds its down projection
+    Yref = oracle.lora_linear_drows(Href, f32(W2), A2f, B2f)
+    assert_gemm(f32(Y[seli]), Yref, "4K down (chained) sampled rows")
+    del X, H, Y
+    torch.cuda.empty_cache()
+
+
+def test_full_2k_standin_three_steps(gpu):
+    wl = inputs.WORKLOADS[4]
+    M = wl.tokens
+    say(f"{wl.name}: M={M}, 3 steps")
+    ref_model = StandinRefiner(M, device=gpu)
+    u, eps = inputs.latent(4)
+    z = ref_model.refine(u.to(gpu), eps.to(gpu)).cpu().numpy()
+    assert np.all(np.isfinite(z))
+    sel = inputs.sample_rows(M, 24, seed=4)
+    layers = []
+    for L in inputs.standin_layers(4):
+        Ab, Bb = oracle.merge_bf16([a.numpy() for a in L["A_list"]],
+                                   [b.numpy() for b in L["B_list"]])
+        layers.append({"W0": f32(L["W0"]), "A": oracle.bf16_value(Ab).reshape(Ab.shape),
+                       "B": oracle.bf16_value(Bb).reshape(Bb.shape)})
+    E, P = inputs.standin_projections(4)
+    zh, vh = oracle.standin_refine(u.numpy()[sel], eps.numpy()[sel], f32(E), f32(P), layers)
+    e = metrics.token_error(z[sel], zh[-1])
+    say(f"  final latent token err {e:.3e}")
+    assert e <= TOL
+    # the velocity of the last step, against the oracle's (bf16-path tolerance)
+    assert_gemm(ref_model.v.cpu().numpy()[sel], vh[-1], "stand-in velocity, step 3")
+    del ref_model
+    torch.cuda.empty_cache()
