@@ -49,9 +49,32 @@ def parse():
                     help="target host time of the oracle sample")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 1 GiB device copy first (a known-size kernel for counters)")
-    ap.add_argument("--traffic", type=str, default=None,
-                    help="JSON file with measured HBM bytes per launch of the dominant kernel")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_swiglu_2k_pmc_traffic.md")
+GEMM_SOURCE = os.path.join(ROOT, "few_step_diffusion_amd", "csrc", "gemm.hip")
+
+
+def measured_traffic():
+    """HBM-side bytes per launch of the dominant kernel from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary, or None when the GEMM source has
+    changed since those counters were taken."""
+    import hashlib
+    try:
+        fields = {}
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                key, sep, val = line.strip().partition(": ")
+                if sep and key in ("source_sha256", "bytes_per_launch"):
+                    fields[key] = val.strip()
+        with open(GEMM_SOURCE, "rb") as f:
+            cur = hashlib.sha256(f.read()).hexdigest()
+        if fields.get("source_sha256") != cur:
+            return None
+        return int(float(fields["bytes_per_launch"]))
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def kernel_times(events):
@@ -198,10 +221,7 @@ def main():
     dom = kernels[DOMINANT]
     L = model.layers[2]
     dom_flops = 2 * M * (L["K"] + model.R) * L["N"]
-    traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        with open(args.traffic) as f:
-            traffic = json.load(f).get("bytes_per_launch")
+    traffic = measured_traffic()
     roofline = {"kernel": "lora_up (phase B) of the gate/up linear, SwiGLU epilogue: "
                           f"M={M} K={L['K']}+{model.R} N={L['N']}",
                 "bound": "mfma", "achieved": round(dom_flops / (dom["mean_us"] * 1e-6) / 1e12, 1),

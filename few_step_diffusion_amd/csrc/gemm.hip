@@ -9,21 +9,34 @@
 // Shazeer, "GLU Variants Improve Transformer" (2020).
 //
 // Kernel shape (one workgroup = 4 waves of 64 lanes, one output tile):
-//   * tile BM x BN = 256 x (64·WN), K staged through LDS in steps of 64;
-//     each wave owns a (32·WM) x (32·WN) sub-tile = WM x WN blocks of the
-//     32x32x16 bf16 MFMA (v_mfma_f32_32x32x16_bf16), fp32 accumulators.
-//   * operands are K-contiguous rows (X row-major, W0 in out x in layout), so
-//     a lane's MFMA fragment (8 consecutive k of one row) is one 16-byte
-//     chunk.  Global -> LDS moves 16-byte chunks with buffer loads whose
-//     range check returns zeros for rows past M or N; a K tail is zeroed by
-//     pushing the offset out of range.
-//   * LDS holds two stages (double buffer, one barrier per K step).  Each
-//     128-byte tile row stores its eight chunks XOR-swizzled by
-//     (row ^ row>>3) & 7, so the 16-byte fragment reads of 8 or 16
-//     consecutive rows hit distinct banks.
+//   * tile BM x BN = 256 x (64·WN); each wave owns a (32·WM) x (32·WN)
+//     sub-tile = WM x WN blocks of v_mfma_f32_32x32x16_bf16 (fp32
+//     accumulators, 256 of them per lane at WM = WN = 4).  The W fragment is
+//     the MFMA's first operand, so a lane ends up owning 4 consecutive output
+//     columns of one token.
+//   * operands are K-contiguous rows (X row-major, W0 in out x in layout): a
+//     lane's MFMA fragment (8 consecutive k of one row) is one 16-byte chunk.
+//   * K is staged through a ring of NSTAGE LDS stages of BK = 32 columns.
+//     Global -> LDS uses 16-byte LDS-DMA buffer loads (buffer_load ... lds):
+//     no VGPR staging, and the buffer range check turns rows past M or N (and,
+//     by pushing the offset out of range, a K tail) into zeros.  Loads run
+//     NSTAGE-1 steps ahead, so about 96 KB per CU are in flight against the
+//     ~1 us latency of L2 misses.
+//   * each 64-byte tile row stores its four chunks XOR-swizzled by
+//     ((row>>1) ^ (row>>3)) & 3: fragment reads of 8 or 16 consecutive rows
+//     then hit distinct banks (no bank conflicts in either a 32- or 64-bank
+//     model).
+//   * one barrier per K step (a partial vmcnt wait keeps the younger stages in
+//     flight); the fragments of the next 16-k sub-step are read while the 16
+//     MFMAs of the current one run, pinned by scheduling groups.
 //   * workgroup ids are remapped so that each XCD (ids round-robin over 8)
 //     gets a contiguous run of tiles, ordered in groups of 4 tile-rows: the
-//     32 tiles an XCD runs at once share 4 X-tiles and 8 W-tiles in its L2.
+//     32 tiles an XCD runs at once share 4 X tiles and 8 W tiles in its L2.
+//   * epilogue: each wave stages its bf16 results (and the residual) through
+//     LDS and writes whole row segments with 16-byte non-temporal stores: the
+//     output is written once and not re-read by this kernel, so it should not
+//     evict the X and W lines that other tiles are re-reading from L2 and the
+//     Infinity Cache.
 #include "fsd_internal.h"
 
 namespace fsd {
@@ -32,40 +45,70 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 constexpr int kThreads = 256;
-constexpr int BK = 64;
-constexpr int kChunks = BK / 8;          // 16-byte chunks per tile row and stage
-constexpr int kRowsPerPass = kThreads / kChunks;   // 32 tile rows per load pass
+constexpr int BK = 32;              // k per LDS stage
+constexpr int ROWB = BK * 2;        // bytes per tile row per stage (4 chunks)
+constexpr int NSTAGE = 4;           // LDS ring depth
 constexpr int kGroupM = 4;
 constexpr uint32_t kOutOfRange = 0x80000000u;
-
-__device__ __forceinline__ int lds_slot(int r, int c) {
-  return r * kChunks + (c ^ ((r ^ (r >> 3)) & 7));
-}
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
                                            0x00020000);
 }
 
-__device__ __forceinline__ float bf16_to_f32(bf16_t h) {
-  return __uint_as_float((uint32_t)h << 16);
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
 }
-__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  return __builtin_bit_cast(bf16_t, (__bf16)f);
+
+// Physical 16-byte chunk of logical chunk c in tile row `row` (an involution).
+__device__ __forceinline__ int swz(int row, int c) { return c ^ (((row >> 1) ^ (row >> 3)) & 3); }
+
+// s_waitcnt with vmcnt <= n (n < 64), lgkmcnt = 0, expcnt untouched.
+template <int n>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(n >= 0 && n < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (0 << 8) | ((n >> 4) << 14));
+}
+
+// Scheduling groups of one half K-step: an LDS read after each of the first
+// NREAD MFMAs, then NLOAD global->LDS loads spread over the remaining MFMAs.
+template <int NMFMA, int NREAD, int NLOAD, int J>
+__device__ __forceinline__ void pin_groups() {
+  if constexpr (J < NMFMA) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA
+    if constexpr (J < NREAD) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                // LDS read
+    } else {
+      constexpr int span = NMFMA - NREAD, t = J - NREAD;
+      constexpr int nl = ((t + 1) * NLOAD) / span - (t * NLOAD) / span;
+      if constexpr (nl > 0) __builtin_amdgcn_sched_group_barrier(0x020, nl, 0);  // loads
+    }
+    pin_groups<NMFMA, NREAD, NLOAD, J + 1>();
+  } else {
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
 template <int WM, int WN, bool SWIGLU>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_kernel(GemmParams p) {
   constexpr int BM = 64 * WM;
   constexpr int BN = 64 * WN;
-  constexpr int A_LOADS = BM / kRowsPerPass;
-  constexpr int B_LOADS = BN / kRowsPerPass;
-  constexpr int STAGE = (BM + BN) * kChunks;
+  constexpr int A_INS = BM / 64;            // 16-byte LDS-DMA loads per wave per stage (A)
+  constexpr int B_INS = BN / 64;            // ... (B)
+  constexpr int NL = A_INS + B_INS;
+  constexpr int A_STAGE = BM * ROWB;        // bytes of one A stage
+  constexpr int B_STAGE = BN * ROWB;
+  constexpr int B_BASE = NSTAGE * A_STAGE;  // LDS: [A stages | B stages]
+  constexpr int LDS_BYTES = NSTAGE * (A_STAGE + B_STAGE);
   static_assert(!SWIGLU || (WN % 2 == 0), "SwiGLU pairs gate and up blocks within a wave");
-  __shared__ u32x4 lds[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
 
   // ---- which tile ---------------------------------------------------------
   const int64_t M = p.M;
@@ -91,12 +134,9 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
   const int64_t m0 = (int64_t)tm * BM;
   const int64_t rows_valid = (M - m0) < BM ? (M - m0) : BM;
 
-  const int t = threadIdx.x;
-  const int lane = t & 63;
-  const int wave = t >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int ld_row = t >> 3;
-  const int ld_chunk = t & 7;
 
   // ---- buffer resources ------------------------------------------------------
   const __amdgpu_buffer_rsrc_t rA0 = make_rsrc(p.A0 + m0 * p.lda0, rows_valid * p.lda0 * 2);
@@ -106,8 +146,11 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
       has1 ? make_rsrc(p.A1 + m0 * p.lda1, rows_valid * p.lda1 * 2) : rA0;
   const __amdgpu_buffer_rsrc_t rB1 = has1 ? make_rsrc(p.B1, N * p.ldb1 * 2) : rB0;
 
-  // global row (of B) held by tile row rt
-  auto b_row = [&](int rt) -> int64_t {
+  // ---- global -> LDS assignment ------------------------------------------------
+  // Load i of this wave fills tile rows q·16 .. q·16+15 (q = wave·INS + i): lane l
+  // writes LDS row q·16 + l/4, physical chunk l%4, fetching logical chunk
+  // swz(row, l%4).  A wave's INS·16 rows are consecutive tile rows.
+  auto b_row = [&](int rt) -> int64_t {   // global row of B held by tile row rt
     if constexpr (SWIGLU) {
       constexpr int WNC = WN * 32, HALFC = WNC / 2;
       const int wn_ = rt / WNC, within = rt % WNC;
@@ -118,45 +161,85 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
       return (int64_t)tn * TN + rt; // rows past N read as zeros
     }
   };
-  uint32_t b_off0[B_LOADS], b_off1[B_LOADS];
+  const int lane_row = lane >> 2;
+  // A wave's rows lie inside one (wave column, gate/up half) block, so the
+  // global row is affine in the load index: n = n(lane) + 16·i.
+  const int64_t b_n = b_row(wave * B_INS * 16 + lane_row);
+  const uint32_t b_lane0 = (uint32_t)(b_n * p.ldb0 * 2);
+  const uint32_t b_lane1 = (uint32_t)(b_n * p.ldb1 * 2);
+  const uint32_t a_lane0 = (uint32_t)((wave * A_INS * 16 + lane_row) * p.lda0 * 2);
+  const uint32_t a_lane1 = (uint32_t)((wave * A_INS * 16 + lane_row) * p.lda1 * 2);
+  uint32_t a_cx[A_INS], b_cx[B_INS];     // byte offset of the fetched logical chunk
 #pragma unroll
-  for (int i = 0; i < B_LOADS; ++i) {
-    const int64_t n = b_row(ld_row + kRowsPerPass * i);
-    b_off0[i] = (uint32_t)(n * p.ldb0 * 2);
-    b_off1[i] = (uint32_t)(n * p.ldb1 * 2);
-  }
+  for (int i = 0; i < A_INS; ++i)
+    a_cx[i] = (uint32_t)(swz((wave * A_INS + i) * 16 + lane_row, lane & 3) * 16);
+#pragma unroll
+  for (int i = 0; i < B_INS; ++i)
+    b_cx[i] = (uint32_t)(swz((wave * B_INS + i) * 16 + lane_row, lane & 3) * 16);
 
-  const int nk0 = (int)((p.K0 + BK - 1) / BK);
-  const int nk1 = (int)((p.K1 + BK - 1) / BK);
+  // per-segment scalars, read once (selected by value inside the loop)
+  const int K0 = __builtin_amdgcn_readfirstlane((int)p.K0);
+  const int K1 = __builtin_amdgcn_readfirstlane((int)p.K1);
+  const uint32_t a_step0 = __builtin_amdgcn_readfirstlane((uint32_t)(32 * p.lda0));
+  const uint32_t a_step1 = __builtin_amdgcn_readfirstlane((uint32_t)(32 * p.lda1));
+  const uint32_t b_step0 = __builtin_amdgcn_readfirstlane((uint32_t)(32 * p.ldb0));
+  const uint32_t b_step1 = __builtin_amdgcn_readfirstlane((uint32_t)(32 * p.ldb1));
+  const int nk0 = (K0 + BK - 1) / BK;
+  const int nk1 = (K1 + BK - 1) / BK;
   const int nk = nk0 + nk1;
 
-  u32x4 ra[A_LOADS], rb[B_LOADS];
-  auto gload = [&](int kt) {
+  // Issue the NL LDS-DMA loads of K-step kt into LDS stage st.  Branch-free so
+  // the loads can be interleaved with MFMAs: chunks past the segment's K (a
+  // partial last step) and every chunk of a step past the end (kt >= nk) take
+  // an out-of-range offset and land as zeros without touching memory.
+  auto issue_loads = [&](int kt, int st) {
     const bool seg1 = kt >= nk0;
-    const int64_t kbase = (int64_t)(seg1 ? kt - nk0 : kt) * BK + ld_chunk * 8;
-    const int64_t kseg = seg1 ? p.K1 : p.K0;
-    const uint32_t koff = kbase < kseg ? (uint32_t)(kbase * 2) : kOutOfRange;
-    const int64_t lda = seg1 ? p.lda1 : p.lda0;
+    const int kbase = (seg1 ? kt - nk0 : kt) * BK;
+    const int kseg = seg1 ? K1 : K0;
+    const int kleft = kt < nk ? kseg - kbase : 0;
+    const uint32_t climit = (uint32_t)(kleft >= BK ? BK * 2 : kleft * 2);  // valid bytes
+    const uint32_t kb = (uint32_t)(kbase * 2);
+    const uint32_t a_step = seg1 ? a_step1 : a_step0;
+    const uint32_t b_step = seg1 ? b_step1 : b_step0;
     const __amdgpu_buffer_rsrc_t rA = seg1 ? rA1 : rA0;
     const __amdgpu_buffer_rsrc_t rB = seg1 ? rB1 : rB0;
+    const uint32_t a_lane = seg1 ? a_lane1 : a_lane0;
+    const uint32_t b_lane = seg1 ? b_lane1 : b_lane0;
+    char* a_dst = lds + st * A_STAGE + wave * A_INS * 1024;
+    char* b_dst = lds + B_BASE + st * B_STAGE + wave * B_INS * 1024;
 #pragma unroll
-    for (int i = 0; i < A_LOADS; ++i) {
-      const uint32_t off = (uint32_t)((ld_row + kRowsPerPass * i) * lda * 2) + koff;
-      ra[i] = __builtin_amdgcn_raw_buffer_load_b128(rA, off, 0, 0);
+    for (int i = 0; i < A_INS; ++i) {
+      const uint32_t off = a_cx[i] < climit ? a_lane + (i * a_step + kb) + a_cx[i] : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_ptr_t)(a_dst + i * 1024), 16, off, 0, 0,
+                                               0);
     }
 #pragma unroll
-    for (int i = 0; i < B_LOADS; ++i) {
-      const uint32_t off = (seg1 ? b_off1[i] : b_off0[i]) + koff;
-      rb[i] = __builtin_amdgcn_raw_buffer_load_b128(rB, off, 0, 0);
+    for (int i = 0; i < B_INS; ++i) {
+      const uint32_t off = b_cx[i] < climit ? b_lane + (i * b_step + kb) + b_cx[i] : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_ptr_t)(b_dst + i * 1024), 16, off, 0, 0,
+                                               0);
     }
   };
-  auto lstore = [&](int stage) {
-    u32x4* base = lds + stage * STAGE;
+
+  // ---- LDS -> MFMA fragments -----------------------------------------------------
+  // Fragment (32 rows x 16 k) of block row base rb (a multiple of 32) in
+  // sub-step ks: lane l reads row rb + l%32, logical chunk 2·ks + l/32.  For
+  // such rows the swizzle key ((l>>1) ^ (l>>3)) & 3 does not depend on rb, so
+  // one lane offset per sub-step serves every block.
+  const int key_lane = ((lane >> 1) ^ (lane >> 3)) & 3;
+  uint32_t frag_lane[2];
 #pragma unroll
-    for (int i = 0; i < A_LOADS; ++i) base[lds_slot(ld_row + kRowsPerPass * i, ld_chunk)] = ra[i];
+  for (int ks = 0; ks < 2; ++ks)
+    frag_lane[ks] = (uint32_t)((lane & 31) * ROWB + (((2 * ks + (lane >> 5)) ^ key_lane) * 16));
+  const uint32_t a_wave = (uint32_t)(wm * WM * 32 * ROWB);
+  const uint32_t b_wave = (uint32_t)(B_BASE + wn * WN * 32 * ROWB);
+  auto read_frags = [&](int st, int ks, bf16x8 (&a)[WM], bf16x8 (&b)[WN]) {
+    const uint32_t ao = frag_lane[ks] + a_wave + st * A_STAGE;
+    const uint32_t bo = frag_lane[ks] + b_wave + st * B_STAGE;
 #pragma unroll
-    for (int i = 0; i < B_LOADS; ++i)
-      base[BM * kChunks + lds_slot(ld_row + kRowsPerPass * i, ld_chunk)] = rb[i];
+    for (int bi = 0; bi < WM; ++bi) a[bi] = *(const bf16x8*)(lds + ao + bi * 32 * ROWB);
+#pragma unroll
+    for (int bj = 0; bj < WN; ++bj) b[bj] = *(const bf16x8*)(lds + bo + bj * 32 * ROWB);
   };
 
   f32x16 acc[WM][WN];
@@ -167,84 +250,165 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[bi][bj][v] = 0.0f;
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
+  auto mfmas = [&](const bf16x8 (&a)[WM], const bf16x8 (&b)[WN]) {
+#pragma unroll
+    for (int bi = 0; bi < WM; ++bi)
+#pragma unroll
+      for (int bj = 0; bj < WN; ++bj)
+        acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[bj], a[bi], acc[bi][bj], 0, 0, 0);
+  };
 
-  const int frag_row = lane & 31;
-  const int frag_chunk = lane >> 5;
+  // ---- main loop -----------------------------------------------------------------
+  // Step kt computes on stage kt % NSTAGE while the loads of step kt+NSTAGE-1
+  // fill the stage consumed at step kt-1.  Sub-step 0 runs its MFMAs on
+  // fragments read earlier while reading sub-step 1's and issuing the loads;
+  // then (partial vmcnt wait + barrier) step kt+1's stage is complete and every
+  // wave has finished reading stage kt; sub-step 1's MFMAs run while the first
+  // fragments of step kt+1 are read.  Each half is a scheduling region of its
+  // own (sched_barrier) in which groups pin the MFMA / read / load interleave:
+  // reads follow the first MFMAs, loads are spread over the rest.
+  constexpr int NREAD = WM + WN;
+  constexpr int NMFMA = WM * WN;
+  static_assert(NREAD < NMFMA, "need MFMAs to hide the fragment reads");
+  bf16x8 fa[2][WM], fb[2][WN];
+#pragma unroll
+  for (int s = 0; s < NSTAGE - 1; ++s) issue_loads(s, s);
+  wait_vm_lgkm0<(NSTAGE - 2) * NL>();
+  __builtin_amdgcn_s_barrier();
+  read_frags(0, 0, fa[0], fb[0]);
   for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-    const u32x4* As = lds + cur * STAGE;
-    const u32x4* Bs = As + BM * kChunks;
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8 a[WM], b[WN];
-#pragma unroll
-      for (int bi = 0; bi < WM; ++bi) {
-        const int r = wm * WM * 32 + bi * 32 + frag_row;
-        a[bi] = __builtin_bit_cast(bf16x8, As[lds_slot(r, 2 * ks + frag_chunk)]);
-      }
-#pragma unroll
-      for (int bj = 0; bj < WN; ++bj) {
-        const int r = wn * WN * 32 + bj * 32 + frag_row;
-        b[bj] = __builtin_bit_cast(bf16x8, Bs[lds_slot(r, 2 * ks + frag_chunk)]);
-      }
-#pragma unroll
-      for (int bi = 0; bi < WM; ++bi)
-#pragma unroll
-        for (int bj = 0; bj < WN; ++bj)
-          acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[bi], b[bj], acc[bi][bj], 0, 0, 0);
-    }
-    if (kt + 1 < nk) lstore(cur ^ 1);
-    __syncthreads();
+    const int st = kt % NSTAGE;
+    const int ld_step = kt + NSTAGE - 1;
+    __builtin_amdgcn_sched_barrier(0);
+    issue_loads(ld_step, ld_step % NSTAGE);
+    read_frags(st, 1, fa[1], fb[1]);
+    mfmas(fa[0], fb[0]);
+    pin_groups<NMFMA, NREAD, NL, 0>();
+    wait_vm_lgkm0<(NSTAGE - 2) * NL>();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags((kt + 1) % NSTAGE, 0, fa[0], fb[0]);
+    mfmas(fa[1], fb[1]);
+    pin_groups<NMFMA, NREAD, 0, 0>();
   }
+  // all LDS-DMA writes (including the out-of-range tail loads) have landed and
+  // every wave is done with the ring before LDS is reused below
+  wait_vm_lgkm0<0>();
+  __builtin_amdgcn_s_barrier();
 
   // ---- epilogue ---------------------------------------------------------------
-  // Accumulator v of block (bi, bj) holds row 8·(v/4) + 4·(lane/32) + v%4 and
-  // column lane%32 of that 32x32 block.
+  // Block (bi, bj) holds the transposed 32x32 output: lane l owns token
+  // bi·32 + l%32 of the wave and, in accumulator group g (elements 4g .. 4g+3),
+  // the four consecutive output columns bj·32 + 8g + 4·(l/32) + 0..3.  Each
+  // wave stages its (token x column) bf16 tile in its own LDS region, adding
+  // the residual (loaded into the same place first) before the single
+  // rounding, then writes whole row segments with 16-byte stores.  Staged rows
+  // keep their 16-byte chunks XOR-swizzled (power-of-two chunk counts) or are
+  // padded by 16 bytes, so the 8-byte writes of 16 consecutive tokens hit
+  // distinct banks.
+  constexpr int OC = SWIGLU ? WN * 16 : WN * 32;    // output columns per wave
+  constexpr int ORB = OC * 2;                       // bytes of one staged row
+  constexpr int OCH = ORB / 16;                     // 16-byte chunks per row
+  constexpr bool POW2 = (OCH & (OCH - 1)) == 0;
+  constexpr int PITCH = POW2 ? ORB : ORB + 16;
+  constexpr int RP = POW2 ? (256 / ORB > 0 ? 256 / ORB : 1) : 1;   // staged rows per 256 B
+  constexpr int OROWS = WM * 32;                    // tokens per wave
+  static_assert(4 * OROWS * PITCH <= LDS_BYTES, "epilogue staging must fit in LDS");
+  char* ow = lds + wave * OROWS * PITCH;
+  auto pchunk = [&](int row, int c) -> int {      // physical chunk of logical chunk c
+    if constexpr (POW2) return c ^ ((row / RP) & (OCH - 1));
+    else return c;
+  };
+  const int64_t col0 = (int64_t)tn * TN + wn * OC;     // first output column of the wave
+  const int64_t tok0 = (int64_t)wm * OROWS;            // first tile row of the wave
   const float alpha = p.alpha;
-  const int col_in_block = lane & 31;
-  const int row_in_block = 4 * (lane >> 5);
+
+  if (p.res) {
+    // residual tile -> LDS (same layout), one 16-byte chunk per lane
+    for (int idx = lane; idx < OROWS * OCH; idx += 64) {
+      const int row = idx / OCH, pc = idx % OCH;
+      const int lc = pchunk(row, pc);               // pchunk is an involution
+      const int64_t c = col0 + lc * 8;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (tok0 + row < rows_valid && c < Nout)
+        v = __builtin_nontemporal_load((const u32x4*)(p.res + (m0 + tok0 + row) * p.ldr + c));
+      *(u32x4*)(ow + row * PITCH + pc * 16) = v;
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+  }
+
+  const int tok = lane & 31;
+  const int c4 = 4 * (lane >> 5);
+  auto slot = [&](int row, int oc) -> char* {
+    return ow + row * PITCH + pchunk(row, oc >> 3) * 16 + (oc & 7) * 2;
+  };
+  auto bias4 = [&](int64_t n, bool ok) -> f32x4 {
+    f32x4 b = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (p.bias && ok) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) b[k] = p.bias[n + k];
+    }
+    return b;
+  };
   if constexpr (SWIGLU) {
     constexpr int HALF = WN / 2;
 #pragma unroll
-    for (int bj = 0; bj < HALF; ++bj) {
-      const int64_t j = (int64_t)tn * TN + wn * HALF * 32 + bj * 32 + col_in_block;
-      const bool col_ok = j < F;
-      const float bg = (p.bias && col_ok) ? p.bias[j] : 0.0f;
-      const float bu = (p.bias && col_ok) ? p.bias[F + j] : 0.0f;
+    for (int bj = 0; bj < HALF; ++bj)
 #pragma unroll
-      for (int bi = 0; bi < WM; ++bi)
+      for (int g = 0; g < 4; ++g) {
+        const int oc = bj * 32 + 8 * g + c4;
+        const int64_t j = col0 + oc;
+        const f32x4 bg = bias4(j, j < F);
+        const f32x4 bu = bias4(F + j, j < F);
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int i = wm * WM * 32 + bi * 32 + 8 * (v >> 2) + row_in_block + (v & 3);
-          if (col_ok && i < rows_valid) {
-            const float g = acc[bi][bj][v] * alpha + bg;
-            const float u = acc[bi][bj + HALF][v] * alpha + bu;
-            const float h = g / (1.0f + __expf(-g)) * u;
-            p.Y[(m0 + i) * p.ldy + j] = f32_to_bf16(h);
+        for (int bi = 0; bi < WM; ++bi) {
+          float h[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const float gt = acc[bi][bj][4 * g + k] * alpha + bg[k];
+            const float up = acc[bi][bj + HALF][4 * g + k] * alpha + bu[k];
+            h[k] = gt / (1.0f + __expf(-gt)) * up;
           }
+          u32x2 pk;
+          pk.x = f32_to_bf16(h[0]) | (f32_to_bf16(h[1]) << 16);
+          pk.y = f32_to_bf16(h[2]) | (f32_to_bf16(h[3]) << 16);
+          *(u32x2*)slot(bi * 32 + tok, oc) = pk;
         }
-    }
+      }
   } else {
 #pragma unroll
-    for (int bj = 0; bj < WN; ++bj) {
-      const int64_t n = (int64_t)tn * TN + wn * WN * 32 + bj * 32 + col_in_block;
-      const bool col_ok = n < N;
-      const float bn = (p.bias && col_ok) ? p.bias[n] : 0.0f;
+    for (int bj = 0; bj < WN; ++bj)
 #pragma unroll
-      for (int bi = 0; bi < WM; ++bi)
+      for (int g = 0; g < 4; ++g) {
+        const int oc = bj * 32 + 8 * g + c4;
+        const f32x4 bn = bias4(col0 + oc, col0 + oc < Nout);
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int i = wm * WM * 32 + bi * 32 + 8 * (v >> 2) + row_in_block + (v & 3);
-          if (col_ok && i < rows_valid) {
-            float y = acc[bi][bj][v] * alpha + bn;
-            if (p.res) y += bf16_to_f32(p.res[(m0 + i) * p.ldr + n]);
-            p.Y[(m0 + i) * p.ldy + n] = f32_to_bf16(y);
+        for (int bi = 0; bi < WM; ++bi) {
+          char* s = slot(bi * 32 + tok, oc);
+          float y[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) y[k] = acc[bi][bj][4 * g + k] * alpha + bn[k];
+          if (p.res) {
+            const u32x2 rv = *(const u32x2*)s;
+            y[0] += __uint_as_float(rv.x << 16);
+            y[1] += __uint_as_float(rv.x & 0xffff0000u);
+            y[2] += __uint_as_float(rv.y << 16);
+            y[3] += __uint_as_float(rv.y & 0xffff0000u);
           }
+          u32x2 pk;
+          pk.x = f32_to_bf16(y[0]) | (f32_to_bf16(y[1]) << 16);
+          pk.y = f32_to_bf16(y[2]) | (f32_to_bf16(y[3]) << 16);
+          *(u32x2*)s = pk;
         }
+      }
+  }
+  __builtin_amdgcn_s_waitcnt(0);   // the wave's staged tile is complete (its own region)
+  for (int idx = lane; idx < OROWS * OCH; idx += 64) {
+    const int row = idx / OCH, pc = idx % OCH;
+    const int64_t c = col0 + pchunk(row, pc) * 8;
+    if (tok0 + row < rows_valid && c < Nout) {
+      const u32x4 v = *(const u32x4*)(ow + row * PITCH + pc * 16);
+      __builtin_nontemporal_store(v, (u32x4*)(p.Y + (m0 + tok0 + row) * p.ldy + c));
     }
   }
 }
