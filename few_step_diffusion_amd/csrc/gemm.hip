@@ -50,7 +50,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-constexpr int kThreads = 256;
+constexpr int kWaveRows = 4;        // waves along M
+constexpr int kWaveCols = 2;        // waves along N
+constexpr int kWaves = kWaveRows * kWaveCols;
+constexpr int kThreads = 64 * kWaves;
 constexpr int BK = 32;              // k per LDS stage
 constexpr int ROWB = BK * 2;        // bytes per tile row per stage (4 chunks)
 constexpr int NSTAGE = 4;           // LDS ring depth
@@ -96,13 +99,18 @@ __device__ __forceinline__ void pin_groups() {
 }
 
 template <int WM, int WN, bool SWIGLU>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_kernel(GemmParams p) {
-  constexpr int BM = 64 * WM;
-  constexpr int BN = 64 * WN;
-  constexpr int A_INS = BM / 64;            // 16-byte LDS-DMA loads per wave per stage (A)
-  constexpr int B_INS = BN / 64;            // ... (B)
+  constexpr int BM = kWaveRows * WM * 32;
+  constexpr int BN = kWaveCols * WN * 32;
+  constexpr int A_TOT = BM / 16;            // 16-row LDS-DMA loads per stage (A)
+  constexpr int B_TOT = BN / 16;            // ... (B)
+  constexpr int A_INS = (A_TOT + kWaves - 1) / kWaves;   // per wave (the last round may be partial)
+  constexpr int B_INS = (B_TOT + kWaves - 1) / kWaves;
   constexpr int NL = A_INS + B_INS;
+  // loads every wave issues per stage (waves past a partial last round issue one
+  // fewer); the stage waits use this count, which can only over-wait
+  constexpr int NLW = A_TOT / kWaves + B_TOT / kWaves;
   constexpr int A_STAGE = BM * ROWB;        // bytes of one A stage
   constexpr int B_STAGE = BN * ROWB;
   constexpr int B_BASE = NSTAGE * A_STAGE;  // LDS: [A stages | B stages]
@@ -136,7 +144,7 @@ void gemm_kernel(GemmParams p) {
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / kWaveCols, wn = wave % kWaveCols;
 
   // ---- buffer resources ------------------------------------------------------
   const __amdgpu_buffer_rsrc_t rA0 = make_rsrc(p.A0 + m0 * p.lda0, rows_valid * p.lda0 * 2);
@@ -147,9 +155,10 @@ void gemm_kernel(GemmParams p) {
   const __amdgpu_buffer_rsrc_t rB1 = has1 ? make_rsrc(p.B1, N * p.ldb1 * 2) : rB0;
 
   // ---- global -> LDS assignment ------------------------------------------------
-  // Load i of this wave fills tile rows q·16 .. q·16+15 (q = wave·INS + i): lane l
+  // The stage's 16-row loads are dealt round-robin to the waves: load i of this
+  // wave is q = i·kWaves + wave (skipped when q is past the tile).  Lane l
   // writes LDS row q·16 + l/4, physical chunk l%4, fetching logical chunk
-  // swz(row, l%4).  A wave's INS·16 rows are consecutive tile rows.
+  // swz(row, l%4).
   auto b_row = [&](int rt) -> int64_t {   // global row of B held by tile row rt
     if constexpr (SWIGLU) {
       constexpr int WNC = WN * 32, HALFC = WNC / 2;
@@ -162,34 +171,34 @@ void gemm_kernel(GemmParams p) {
     }
   };
   const int lane_row = lane >> 2;
-  // A wave's rows lie inside one (wave column, gate/up half) block, so the
-  // global row is affine in the load index: n = n(lane) + 16·i.
-  const int64_t b_n = b_row(wave * B_INS * 16 + lane_row);
-  const uint32_t b_lane0 = (uint32_t)(b_n * p.ldb0 * 2);
-  const uint32_t b_lane1 = (uint32_t)(b_n * p.ldb1 * 2);
-  const uint32_t a_lane0 = (uint32_t)((wave * A_INS * 16 + lane_row) * p.lda0 * 2);
-  const uint32_t a_lane1 = (uint32_t)((wave * A_INS * 16 + lane_row) * p.lda1 * 2);
-  uint32_t a_cx[A_INS], b_cx[B_INS];     // byte offset of the fetched logical chunk
+  uint32_t a_off0[A_INS], a_off1[A_INS], a_cx[A_INS];   // row byte offset (per segment), chunk
+  uint32_t b_off0[B_INS], b_off1[B_INS], b_cx[B_INS];
 #pragma unroll
-  for (int i = 0; i < A_INS; ++i)
-    a_cx[i] = (uint32_t)(swz((wave * A_INS + i) * 16 + lane_row, lane & 3) * 16);
+  for (int i = 0; i < A_INS; ++i) {
+    const int row = (i * kWaves + wave) * 16 + lane_row;
+    a_off0[i] = (uint32_t)(row * p.lda0 * 2);
+    a_off1[i] = (uint32_t)(row * p.lda1 * 2);
+    a_cx[i] = (uint32_t)(swz(row, lane & 3) * 16);
+  }
 #pragma unroll
-  for (int i = 0; i < B_INS; ++i)
-    b_cx[i] = (uint32_t)(swz((wave * B_INS + i) * 16 + lane_row, lane & 3) * 16);
+  for (int i = 0; i < B_INS; ++i) {
+    const int row = (i * kWaves + wave) * 16 + lane_row;
+    const int64_t n = b_row(row);
+    b_off0[i] = (uint32_t)(n * p.ldb0 * 2);
+    b_off1[i] = (uint32_t)(n * p.ldb1 * 2);
+    b_cx[i] = (uint32_t)(swz(row, lane & 3) * 16);
+  }
 
   // per-segment scalars, read once (selected by value inside the loop)
   const int K0 = __builtin_amdgcn_readfirstlane((int)p.K0);
   const int K1 = __builtin_amdgcn_readfirstlane((int)p.K1);
-  const uint32_t a_step0 = __builtin_amdgcn_readfirstlane((uint32_t)(32 * p.lda0));
-  const uint32_t a_step1 = __builtin_amdgcn_readfirstlane((uint32_t)(32 * p.lda1));
-  const uint32_t b_step0 = __builtin_amdgcn_readfirstlane((uint32_t)(32 * p.ldb0));
-  const uint32_t b_step1 = __builtin_amdgcn_readfirstlane((uint32_t)(32 * p.ldb1));
   const int nk0 = (K0 + BK - 1) / BK;
   const int nk1 = (K1 + BK - 1) / BK;
   const int nk = nk0 + nk1;
 
-  // Issue the NL LDS-DMA loads of K-step kt into LDS stage st.  Branch-free so
-  // the loads can be interleaved with MFMAs: chunks past the segment's K (a
+  // Issue this wave's LDS-DMA loads of K-step kt into LDS stage st.
+  // Branch-free (but for the wave-uniform check of a partial last round) so the
+  // loads can be interleaved with MFMAs: chunks past the segment's K (a
   // partial last step) and every chunk of a step past the end (kt >= nk) take
   // an out-of-range offset and land as zeros without touching memory.
   auto issue_loads = [&](int kt, int st) {
@@ -199,25 +208,25 @@ void gemm_kernel(GemmParams p) {
     const int kleft = kt < nk ? kseg - kbase : 0;
     const uint32_t climit = (uint32_t)(kleft >= BK ? BK * 2 : kleft * 2);  // valid bytes
     const uint32_t kb = (uint32_t)(kbase * 2);
-    const uint32_t a_step = seg1 ? a_step1 : a_step0;
-    const uint32_t b_step = seg1 ? b_step1 : b_step0;
     const __amdgpu_buffer_rsrc_t rA = seg1 ? rA1 : rA0;
     const __amdgpu_buffer_rsrc_t rB = seg1 ? rB1 : rB0;
-    const uint32_t a_lane = seg1 ? a_lane1 : a_lane0;
-    const uint32_t b_lane = seg1 ? b_lane1 : b_lane0;
-    char* a_dst = lds + st * A_STAGE + wave * A_INS * 1024;
-    char* b_dst = lds + B_BASE + st * B_STAGE + wave * B_INS * 1024;
 #pragma unroll
     for (int i = 0; i < A_INS; ++i) {
-      const uint32_t off = a_cx[i] < climit ? a_lane + (i * a_step + kb) + a_cx[i] : kOutOfRange;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_ptr_t)(a_dst + i * 1024), 16, off, 0, 0,
-                                               0);
+      const int q = i * kWaves + wave;
+      if (A_TOT % kWaves != 0 && q >= A_TOT) continue;
+      const uint32_t row_off = seg1 ? a_off1[i] : a_off0[i];
+      const uint32_t off = a_cx[i] < climit ? row_off + kb + a_cx[i] : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rA, (lds_ptr_t)(lds + st * A_STAGE + q * 1024), 16, off, 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < B_INS; ++i) {
-      const uint32_t off = b_cx[i] < climit ? b_lane + (i * b_step + kb) + b_cx[i] : kOutOfRange;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_ptr_t)(b_dst + i * 1024), 16, off, 0, 0,
-                                               0);
+      const int q = i * kWaves + wave;
+      if (B_TOT % kWaves != 0 && q >= B_TOT) continue;
+      const uint32_t row_off = seg1 ? b_off1[i] : b_off0[i];
+      const uint32_t off = b_cx[i] < climit ? row_off + kb + b_cx[i] : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rB, (lds_ptr_t)(lds + B_BASE + st * B_STAGE + q * 1024), 16, off, 0, 0, 0);
     }
   };
 
@@ -273,7 +282,7 @@ void gemm_kernel(GemmParams p) {
   bf16x8 fa[2][WM], fb[2][WN];
 #pragma unroll
   for (int s = 0; s < NSTAGE - 1; ++s) issue_loads(s, s);
-  wait_vm_lgkm0<(NSTAGE - 2) * NL>();
+  wait_vm_lgkm0<(NSTAGE - 2) * NLW>();
   __builtin_amdgcn_s_barrier();
   read_frags(0, 0, fa[0], fb[0]);
   for (int kt = 0; kt < nk; ++kt) {
@@ -284,7 +293,7 @@ void gemm_kernel(GemmParams p) {
     read_frags(st, 1, fa[1], fb[1]);
     mfmas(fa[0], fb[0]);
     pin_groups<NMFMA, NREAD, NL, 0>();
-    wait_vm_lgkm0<(NSTAGE - 2) * NL>();
+    wait_vm_lgkm0<(NSTAGE - 2) * NLW>();
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     read_frags((kt + 1) % NSTAGE, 0, fa[0], fb[0]);
@@ -313,7 +322,7 @@ void gemm_kernel(GemmParams p) {
   constexpr int PITCH = POW2 ? ORB : ORB + 16;
   constexpr int RP = POW2 ? (256 / ORB > 0 ? 256 / ORB : 1) : 1;   // staged rows per 256 B
   constexpr int OROWS = WM * 32;                    // tokens per wave
-  static_assert(4 * OROWS * PITCH <= LDS_BYTES, "epilogue staging must fit in LDS");
+  static_assert(kWaves * OROWS * PITCH <= LDS_BYTES, "epilogue staging must fit in LDS");
   char* ow = lds + wave * OROWS * PITCH;
   auto pchunk = [&](int row, int c) -> int {      // physical chunk of logical chunk c
     if constexpr (POW2) return c ^ ((row / RP) & (OCH - 1));
@@ -415,8 +424,8 @@ void gemm_kernel(GemmParams p) {
 
 template <int WM, int WN, bool SWIGLU>
 hipError_t launch(const GemmParams& p, hipStream_t s) {
-  constexpr int BM = 64 * WM;
-  constexpr int TN = SWIGLU ? 32 * WN : 64 * WN;
+  constexpr int BM = kWaveRows * WM * 32;
+  constexpr int TN = (SWIGLU ? 16 : 32) * kWaveCols * WN;
   const int64_t nout = SWIGLU ? p.N / 2 : p.N;
   const int64_t tiles = ((p.M + BM - 1) / BM) * ((nout + TN - 1) / TN);
   if (tiles <= 0) return hipSuccess;
@@ -430,9 +439,9 @@ hipError_t launch(const GemmParams& p, hipStream_t s) {
 
 hipError_t launch_gemm(GemmKind kind, const GemmParams& p, hipStream_t s) {
   switch (kind) {
-    case GEMM_DOWN: return launch<4, 3, false>(p, s);
-    case GEMM_UP: return launch<4, 4, false>(p, s);
-    case GEMM_UP_SWIGLU: return launch<4, 4, true>(p, s);
+    case GEMM_DOWN: return launch<2, 3, false>(p, s);
+    case GEMM_UP: return launch<2, 4, false>(p, s);
+    case GEMM_UP_SWIGLU: return launch<2, 4, true>(p, s);
   }
   return hipErrorInvalidValue;
 }
