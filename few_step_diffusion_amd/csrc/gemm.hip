@@ -54,9 +54,12 @@ constexpr int kWaveRows = 4;        // waves along M
 constexpr int kWaveCols = 2;        // waves along N
 constexpr int kWaves = kWaveRows * kWaveCols;
 constexpr int kThreads = 64 * kWaves;
-constexpr int BK = 32;              // k per LDS stage
-constexpr int ROWB = BK * 2;        // bytes per tile row per stage (4 chunks)
-constexpr int NSTAGE = 4;           // LDS ring depth
+constexpr int BK = 64;              // k per LDS stage
+constexpr int ROWB = BK * 2;        // bytes per tile row per stage: one 128-byte L2 line
+constexpr int CPR = ROWB / 16;      // 16-byte chunks per tile row (8)
+constexpr int RPL = 64 / CPR;       // tile rows per 64-lane LDS-DMA load (8)
+constexpr int KS = BK / 16;         // MFMA sub-steps per stage (4)
+constexpr int NSTAGE = 2;           // LDS stages (double buffer)
 constexpr int kGroupM = 4;
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
@@ -70,7 +73,10 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
 }
 
 // Physical 16-byte chunk of logical chunk c in tile row `row` (an involution).
-__device__ __forceinline__ int swz(int row, int c) { return c ^ (((row >> 1) ^ (row >> 3)) & 3); }
+// Rows are 128 bytes, so two rows share one 256-byte bank line; XOR-ing the
+// chunk with bits 1..3 of the row spreads 16 consecutive rows over all 16
+// chunk slots of the line.
+__device__ __forceinline__ int swz(int row, int c) { return c ^ ((row >> 1) & (CPR - 1)); }
 
 // s_waitcnt with vmcnt <= n (n < 64), lgkmcnt = 0, expcnt untouched.
 template <int n>
@@ -79,19 +85,15 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
   __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (0 << 8) | ((n >> 4) << 14));
 }
 
-// Scheduling groups of one half K-step: an LDS read after each of the first
-// NREAD MFMAs, then NLOAD global->LDS loads spread over the remaining MFMAs.
+// Scheduling groups of one MFMA sub-step: an LDS read after each of the first
+// NREAD MFMAs and NLOAD global->LDS loads spread evenly over all of them.
 template <int NMFMA, int NREAD, int NLOAD, int J>
 __device__ __forceinline__ void pin_groups() {
   if constexpr (J < NMFMA) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA
-    if constexpr (J < NREAD) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                // LDS read
-    } else {
-      constexpr int span = NMFMA - NREAD, t = J - NREAD;
-      constexpr int nl = ((t + 1) * NLOAD) / span - (t * NLOAD) / span;
-      if constexpr (nl > 0) __builtin_amdgcn_sched_group_barrier(0x020, nl, 0);  // loads
-    }
+    if constexpr (J < NREAD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+    constexpr int nl = ((J + 1) * NLOAD) / NMFMA - (J * NLOAD) / NMFMA;
+    if constexpr (nl > 0) __builtin_amdgcn_sched_group_barrier(0x020, nl, 0);     // loads
     pin_groups<NMFMA, NREAD, NLOAD, J + 1>();
   } else {
     __builtin_amdgcn_sched_barrier(0);
@@ -103,14 +105,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 void gemm_kernel(GemmParams p) {
   constexpr int BM = kWaveRows * WM * 32;
   constexpr int BN = kWaveCols * WN * 32;
-  constexpr int A_TOT = BM / 16;            // 16-row LDS-DMA loads per stage (A)
-  constexpr int B_TOT = BN / 16;            // ... (B)
+  constexpr int A_TOT = BM / RPL;           // LDS-DMA loads per stage (A)
+  constexpr int B_TOT = BN / RPL;           // ... (B)
   constexpr int A_INS = (A_TOT + kWaves - 1) / kWaves;   // per wave (the last round may be partial)
   constexpr int B_INS = (B_TOT + kWaves - 1) / kWaves;
   constexpr int NL = A_INS + B_INS;
-  // loads every wave issues per stage (waves past a partial last round issue one
-  // fewer); the stage waits use this count, which can only over-wait
-  constexpr int NLW = A_TOT / kWaves + B_TOT / kWaves;
   constexpr int A_STAGE = BM * ROWB;        // bytes of one A stage
   constexpr int B_STAGE = BN * ROWB;
   constexpr int B_BASE = NSTAGE * A_STAGE;  // LDS: [A stages | B stages]
@@ -155,10 +154,12 @@ void gemm_kernel(GemmParams p) {
   const __amdgpu_buffer_rsrc_t rB1 = has1 ? make_rsrc(p.B1, N * p.ldb1 * 2) : rB0;
 
   // ---- global -> LDS assignment ------------------------------------------------
-  // The stage's 16-row loads are dealt round-robin to the waves: load i of this
+  // The stage's 8-row loads are dealt round-robin to the waves: load i of this
   // wave is q = i·kWaves + wave (skipped when q is past the tile).  Lane l
-  // writes LDS row q·16 + l/4, physical chunk l%4, fetching logical chunk
-  // swz(row, l%4).
+  // writes LDS row q·8 + l/8, physical chunk l%8, fetching logical chunk
+  // swz(row, l%8), so the eight lanes of a row fetch one whole 128-byte line.
+  // Since q·8 ≡ wave·8 (mod 64), the swizzle depends on the lane and the wave
+  // only, and the A row offset is a per-lane base plus i times a scalar stride.
   auto b_row = [&](int rt) -> int64_t {   // global row of B held by tile row rt
     if constexpr (SWIGLU) {
       constexpr int WNC = WN * 32, HALFC = WNC / 2;
@@ -170,23 +171,18 @@ void gemm_kernel(GemmParams p) {
       return (int64_t)tn * TN + rt; // rows past N read as zeros
     }
   };
-  const int lane_row = lane >> 2;
-  uint32_t a_off0[A_INS], a_off1[A_INS], a_cx[A_INS];   // row byte offset (per segment), chunk
-  uint32_t b_off0[B_INS], b_off1[B_INS], b_cx[B_INS];
-#pragma unroll
-  for (int i = 0; i < A_INS; ++i) {
-    const int row = (i * kWaves + wave) * 16 + lane_row;
-    a_off0[i] = (uint32_t)(row * p.lda0 * 2);
-    a_off1[i] = (uint32_t)(row * p.lda1 * 2);
-    a_cx[i] = (uint32_t)(swz(row, lane & 3) * 16);
-  }
+  const int my_row = wave * RPL + lane / CPR;          // tile row of load i = 0
+  const uint32_t cx = (uint32_t)(swz(my_row, lane % CPR) * 16);
+  const uint32_t a_base0 = (uint32_t)(my_row * p.lda0 * 2);
+  const uint32_t a_base1 = (uint32_t)(my_row * p.lda1 * 2);
+  const uint32_t a_step0 = (uint32_t)(kWaves * RPL * p.lda0 * 2);
+  const uint32_t a_step1 = (uint32_t)(kWaves * RPL * p.lda1 * 2);
+  uint32_t b_off0[B_INS], b_off1[B_INS];
 #pragma unroll
   for (int i = 0; i < B_INS; ++i) {
-    const int row = (i * kWaves + wave) * 16 + lane_row;
-    const int64_t n = b_row(row);
+    const int64_t n = b_row(i * kWaves * RPL + my_row);
     b_off0[i] = (uint32_t)(n * p.ldb0 * 2);
     b_off1[i] = (uint32_t)(n * p.ldb1 * 2);
-    b_cx[i] = (uint32_t)(swz(row, lane & 3) * 16);
   }
 
   // per-segment scalars, read once (selected by value inside the loop)
@@ -196,49 +192,59 @@ void gemm_kernel(GemmParams p) {
   const int nk1 = (K1 + BK - 1) / BK;
   const int nk = nk0 + nk1;
 
-  // Issue this wave's LDS-DMA loads of K-step kt into LDS stage st.
-  // Branch-free (but for the wave-uniform check of a partial last round) so the
-  // loads can be interleaved with MFMAs: chunks past the segment's K (a
-  // partial last step) and every chunk of a step past the end (kt >= nk) take
-  // an out-of-range offset and land as zeros without touching memory.
-  auto issue_loads = [&](int kt, int st) {
-    const bool seg1 = kt >= nk0;
+  // This wave's LDS-DMA loads of K-step kt: j < A_INS loads A rows, the rest
+  // B rows.  Branch-free (but for the wave-uniform check of a partial last
+  // round) so the loads can be interleaved with MFMAs: chunks past the
+  // segment's K (a partial last step) and every chunk of a step past the end
+  // (kt >= nk) take an out-of-range offset and land as zeros without touching
+  // memory.
+  auto step_scalars = [&](int kt, bool& seg1, uint32_t& kb, bool& in_k) {
+    seg1 = kt >= nk0;
     const int kbase = (seg1 ? kt - nk0 : kt) * BK;
     const int kseg = seg1 ? K1 : K0;
     const int kleft = kt < nk ? kseg - kbase : 0;
     const uint32_t climit = (uint32_t)(kleft >= BK ? BK * 2 : kleft * 2);  // valid bytes
-    const uint32_t kb = (uint32_t)(kbase * 2);
-    const __amdgpu_buffer_rsrc_t rA = seg1 ? rA1 : rA0;
-    const __amdgpu_buffer_rsrc_t rB = seg1 ? rB1 : rB0;
-#pragma unroll
-    for (int i = 0; i < A_INS; ++i) {
-      const int q = i * kWaves + wave;
-      if (A_TOT % kWaves != 0 && q >= A_TOT) continue;
-      const uint32_t row_off = seg1 ? a_off1[i] : a_off0[i];
-      const uint32_t off = a_cx[i] < climit ? row_off + kb + a_cx[i] : kOutOfRange;
+    kb = (uint32_t)(kbase * 2) + cx;
+    in_k = cx < climit;
+  };
+  auto load_one = [&](__amdgpu_buffer_rsrc_t rA, __amdgpu_buffer_rsrc_t rB, bool seg1,
+                      uint32_t a_base, uint32_t a_step, uint32_t kb, bool in_k, int j, int st) {
+    if (j < A_INS) {
+      const int q = j * kWaves + wave;
+      if (A_TOT % kWaves != 0 && q >= A_TOT) return;
+      const uint32_t off = in_k ? a_base + j * a_step + kb : kOutOfRange;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rA, (lds_ptr_t)(lds + st * A_STAGE + q * 1024), 16, off, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < B_INS; ++i) {
+    } else {
+      const int i = j - A_INS;
       const int q = i * kWaves + wave;
-      if (B_TOT % kWaves != 0 && q >= B_TOT) continue;
-      const uint32_t row_off = seg1 ? b_off1[i] : b_off0[i];
-      const uint32_t off = b_cx[i] < climit ? row_off + kb + b_cx[i] : kOutOfRange;
+      if (B_TOT % kWaves != 0 && q >= B_TOT) return;
+      const uint32_t off = in_k ? (seg1 ? b_off1[i] : b_off0[i]) + kb : kOutOfRange;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rB, (lds_ptr_t)(lds + B_BASE + st * B_STAGE + q * 1024), 16, off, 0, 0, 0);
     }
+  };
+  auto issue_loads = [&](int kt, int st) {
+    bool seg1, in_k;
+    uint32_t kb;
+    step_scalars(kt, seg1, kb, in_k);
+    const __amdgpu_buffer_rsrc_t rA = seg1 ? rA1 : rA0;
+    const __amdgpu_buffer_rsrc_t rB = seg1 ? rB1 : rB0;
+    const uint32_t a_base = seg1 ? a_base1 : a_base0;
+    const uint32_t a_step = seg1 ? a_step1 : a_step0;
+#pragma unroll
+    for (int j = 0; j < NL; ++j) load_one(rA, rB, seg1, a_base, a_step, kb, in_k, j, st);
   };
 
   // ---- LDS -> MFMA fragments -----------------------------------------------------
   // Fragment (32 rows x 16 k) of block row base rb (a multiple of 32) in
   // sub-step ks: lane l reads row rb + l%32, logical chunk 2·ks + l/32.  For
-  // such rows the swizzle key ((l>>1) ^ (l>>3)) & 3 does not depend on rb, so
-  // one lane offset per sub-step serves every block.
-  const int key_lane = ((lane >> 1) ^ (lane >> 3)) & 3;
-  uint32_t frag_lane[2];
+  // such rows the swizzle key (l>>1) & 7 does not depend on rb, so one lane
+  // offset per sub-step serves every block.
+  const int key_lane = (lane >> 1) & (CPR - 1);
+  uint32_t frag_lane[KS];
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
+  for (int ks = 0; ks < KS; ++ks)
     frag_lane[ks] = (uint32_t)((lane & 31) * ROWB + (((2 * ks + (lane >> 5)) ^ key_lane) * 16));
   const uint32_t a_wave = (uint32_t)(wm * WM * 32 * ROWB);
   const uint32_t b_wave = (uint32_t)(B_BASE + wn * WN * 32 * ROWB);
@@ -249,6 +255,28 @@ void gemm_kernel(GemmParams p) {
     for (int bi = 0; bi < WM; ++bi) a[bi] = *(const bf16x8*)(lds + ao + bi * 32 * ROWB);
 #pragma unroll
     for (int bj = 0; bj < WN; ++bj) b[bj] = *(const bf16x8*)(lds + bo + bj * 32 * ROWB);
+  };
+  // The same fragment reads with step kt's loads into stage st interleaved in
+  // program order (read j, load j): the compiler cannot tell the DMA's LDS
+  // writes from the reads apart, so this order is what lets the scheduling
+  // groups pair each MFMA with one read and one load.
+  auto read_and_load = [&](int st_r, int ks, bf16x8 (&a)[WM], bf16x8 (&b)[WN], int kt, int st) {
+    const uint32_t ao = frag_lane[ks] + a_wave + st_r * A_STAGE;
+    const uint32_t bo = frag_lane[ks] + b_wave + st_r * B_STAGE;
+    bool seg1, in_k;
+    uint32_t kb;
+    step_scalars(kt, seg1, kb, in_k);
+    const __amdgpu_buffer_rsrc_t rA = seg1 ? rA1 : rA0;
+    const __amdgpu_buffer_rsrc_t rB = seg1 ? rB1 : rB0;
+    const uint32_t a_base = seg1 ? a_base1 : a_base0;
+    const uint32_t a_step = seg1 ? a_step1 : a_step0;
+    constexpr int NJ = (WM + WN) > NL ? (WM + WN) : NL;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      if (j < WM) a[j] = *(const bf16x8*)(lds + ao + j * 32 * ROWB);
+      else if (j < WM + WN) b[j - WM] = *(const bf16x8*)(lds + bo + (j - WM) * 32 * ROWB);
+      if (j < NL) load_one(rA, rB, seg1, a_base, a_step, kb, in_k, j, st);
+    }
   };
 
   f32x16 acc[WM][WN];
@@ -268,40 +296,42 @@ void gemm_kernel(GemmParams p) {
   };
 
   // ---- main loop -----------------------------------------------------------------
-  // Step kt computes on stage kt % NSTAGE while the loads of step kt+NSTAGE-1
-  // fill the stage consumed at step kt-1.  Sub-step 0 runs its MFMAs on
-  // fragments read earlier while reading sub-step 1's and issuing the loads;
-  // then (partial vmcnt wait + barrier) step kt+1's stage is complete and every
-  // wave has finished reading stage kt; sub-step 1's MFMAs run while the first
-  // fragments of step kt+1 are read.  Each half is a scheduling region of its
-  // own (sched_barrier) in which groups pin the MFMA / read / load interleave:
-  // reads follow the first MFMAs, loads are spread over the rest.
+  // Double-buffered: step kt computes on stage kt & 1.  Each of its KS MFMA
+  // sub-steps runs on fragments read during the previous one.  Before the
+  // last sub-step a full wait + barrier makes stage kt+1 (loaded during step
+  // kt-1) visible and retires every read of stage kt; the loads of step kt+2
+  // then refill stage kt & 1 while the last sub-step runs and the first
+  // fragments of step kt+1 are read, so a load has one whole step to land.
+  // Each sub-step is a scheduling region of its own (sched_barrier) in which
+  // groups pin the MFMA / read / load interleave.
   constexpr int NREAD = WM + WN;
   constexpr int NMFMA = WM * WN;
   static_assert(NREAD < NMFMA, "need MFMAs to hide the fragment reads");
+  static_assert(KS % 2 == 0, "fragment double buffer parity");
   bf16x8 fa[2][WM], fb[2][WN];
-#pragma unroll
-  for (int s = 0; s < NSTAGE - 1; ++s) issue_loads(s, s);
-  wait_vm_lgkm0<(NSTAGE - 2) * NLW>();
+  issue_loads(0, 0);
+  wait_vm_lgkm0<0>();
   __builtin_amdgcn_s_barrier();
+  issue_loads(1, 1);
   read_frags(0, 0, fa[0], fb[0]);
   for (int kt = 0; kt < nk; ++kt) {
-    const int st = kt % NSTAGE;
-    const int ld_step = kt + NSTAGE - 1;
-    __builtin_amdgcn_sched_barrier(0);
-    issue_loads(ld_step, ld_step % NSTAGE);
-    read_frags(st, 1, fa[1], fb[1]);
-    mfmas(fa[0], fb[0]);
-    pin_groups<NMFMA, NREAD, NL, 0>();
-    wait_vm_lgkm0<(NSTAGE - 2) * NLW>();
+    const int st = kt & 1;
+#pragma unroll
+    for (int ks = 0; ks < KS - 1; ++ks) {
+      __builtin_amdgcn_sched_barrier(0);
+      read_frags(st, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+      mfmas(fa[ks & 1], fb[ks & 1]);
+      pin_groups<NMFMA, NREAD, 0, 0>();
+    }
+    wait_vm_lgkm0<0>();
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    read_frags((kt + 1) % NSTAGE, 0, fa[0], fb[0]);
+    read_and_load(st ^ 1, 0, fa[0], fb[0], kt + 2, st);
     mfmas(fa[1], fb[1]);
-    pin_groups<NMFMA, NREAD, 0, 0>();
+    pin_groups<NMFMA, NREAD, NL, 0>();
   }
-  // all LDS-DMA writes (including the out-of-range tail loads) have landed and
-  // every wave is done with the ring before LDS is reused below
+  // all LDS-DMA writes (including the out-of-range loads past the end) have
+  // landed and every wave is done with the ring before LDS is reused below
   wait_vm_lgkm0<0>();
   __builtin_amdgcn_s_barrier();
 
