@@ -37,6 +37,8 @@
 //     output is written once and not re-read by this kernel, so it should not
 //     evict the X and W lines that other tiles are re-reading from L2 and the
 //     Infinity Cache.
+#include <type_traits>
+
 #include "fsd_internal.h"
 
 namespace fsd {
@@ -59,7 +61,8 @@ constexpr int ROWB = BK * 2;        // bytes per tile row per stage: one 128-byt
 constexpr int CPR = ROWB / 16;      // 16-byte chunks per tile row (8)
 constexpr int RPL = 64 / CPR;       // tile rows per 64-lane LDS-DMA load (8)
 constexpr int KS = BK / 16;         // MFMA sub-steps per stage (4)
-constexpr int NSTAGE = 2;           // LDS stages (double buffer)
+constexpr int NSLOT_A = 3;          // LDS slots of the A ring (loads spread over a step)
+constexpr int NSLOT_B = 2;          // LDS slots of the B ring
 constexpr int kGroupM = 4;
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
@@ -112,8 +115,9 @@ void gemm_kernel(GemmParams p) {
   constexpr int NL = A_INS + B_INS;
   constexpr int A_STAGE = BM * ROWB;        // bytes of one A stage
   constexpr int B_STAGE = BN * ROWB;
-  constexpr int B_BASE = NSTAGE * A_STAGE;  // LDS: [A stages | B stages]
-  constexpr int LDS_BYTES = NSTAGE * (A_STAGE + B_STAGE);
+  constexpr int B_BASE = NSLOT_A * A_STAGE; // LDS: [A slots | B slots]
+  constexpr int LDS_BYTES = NSLOT_A * A_STAGE + NSLOT_B * B_STAGE;
+  static_assert(LDS_BYTES <= 160 * 1024, "gfx950 has 160 KB of LDS per CU");
   static_assert(!SWIGLU || (WN % 2 == 0), "SwiGLU pairs gate and up blocks within a wave");
   __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
 
@@ -192,12 +196,11 @@ void gemm_kernel(GemmParams p) {
   const int nk1 = (K1 + BK - 1) / BK;
   const int nk = nk0 + nk1;
 
-  // This wave's LDS-DMA loads of K-step kt: j < A_INS loads A rows, the rest
-  // B rows.  Branch-free (but for the wave-uniform check of a partial last
-  // round) so the loads can be interleaved with MFMAs: chunks past the
-  // segment's K (a partial last step) and every chunk of a step past the end
-  // (kt >= nk) take an out-of-range offset and land as zeros without touching
-  // memory.
+  // This wave's LDS-DMA loads of one operand for K-step kt.  Branch-free (but
+  // for the wave-uniform check of a partial last round) so the loads can be
+  // interleaved with MFMAs: chunks past the segment's K (a partial last step)
+  // and every chunk of a step past the end (kt >= nk) take an out-of-range
+  // offset and land as zeros without touching memory.
   auto step_scalars = [&](int kt, bool& seg1, uint32_t& kb, bool& in_k) {
     seg1 = kt >= nk0;
     const int kbase = (seg1 ? kt - nk0 : kt) * BK;
@@ -207,33 +210,39 @@ void gemm_kernel(GemmParams p) {
     kb = (uint32_t)(kbase * 2) + cx;
     in_k = cx < climit;
   };
-  auto load_one = [&](__amdgpu_buffer_rsrc_t rA, __amdgpu_buffer_rsrc_t rB, bool seg1,
-                      uint32_t a_base, uint32_t a_step, uint32_t kb, bool in_k, int j, int st) {
-    if (j < A_INS) {
-      const int q = j * kWaves + wave;
-      if (A_TOT % kWaves != 0 && q >= A_TOT) return;
-      const uint32_t off = in_k ? a_base + j * a_step + kb : kOutOfRange;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rA, (lds_ptr_t)(lds + st * A_STAGE + q * 1024), 16, off, 0, 0, 0);
-    } else {
-      const int i = j - A_INS;
-      const int q = i * kWaves + wave;
-      if (B_TOT % kWaves != 0 && q >= B_TOT) return;
-      const uint32_t off = in_k ? (seg1 ? b_off1[i] : b_off0[i]) + kb : kOutOfRange;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rB, (lds_ptr_t)(lds + B_BASE + st * B_STAGE + q * 1024), 16, off, 0, 0, 0);
-    }
+  auto load_a = [&](__amdgpu_buffer_rsrc_t r, uint32_t base, uint32_t stp, uint32_t kb,
+                    bool in_k, int i, int slot) {
+    const int q = i * kWaves + wave;
+    if (A_TOT % kWaves != 0 && q >= A_TOT) return;
+    const uint32_t off = in_k ? base + i * stp + kb : kOutOfRange;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (lds_ptr_t)(lds + slot * A_STAGE + q * 1024), 16, off, 0, 0, 0);
   };
-  auto issue_loads = [&](int kt, int st) {
+  auto load_b = [&](__amdgpu_buffer_rsrc_t r, bool seg1, uint32_t kb, bool in_k, int i,
+                    int slot) {
+    const int q = i * kWaves + wave;
+    if (B_TOT % kWaves != 0 && q >= B_TOT) return;
+    const uint32_t off = in_k ? (seg1 ? b_off1[i] : b_off0[i]) + kb : kOutOfRange;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (lds_ptr_t)(lds + B_BASE + slot * B_STAGE + q * 1024), 16, off, 0, 0, 0);
+  };
+  auto issue_a = [&](int kt, int slot) {
     bool seg1, in_k;
     uint32_t kb;
     step_scalars(kt, seg1, kb, in_k);
-    const __amdgpu_buffer_rsrc_t rA = seg1 ? rA1 : rA0;
-    const __amdgpu_buffer_rsrc_t rB = seg1 ? rB1 : rB0;
-    const uint32_t a_base = seg1 ? a_base1 : a_base0;
-    const uint32_t a_step = seg1 ? a_step1 : a_step0;
+    const __amdgpu_buffer_rsrc_t r = seg1 ? rA1 : rA0;
+    const uint32_t base = seg1 ? a_base1 : a_base0;
+    const uint32_t stp = seg1 ? a_step1 : a_step0;
 #pragma unroll
-    for (int j = 0; j < NL; ++j) load_one(rA, rB, seg1, a_base, a_step, kb, in_k, j, st);
+    for (int i = 0; i < A_INS; ++i) load_a(r, base, stp, kb, in_k, i, slot);
+  };
+  auto issue_b = [&](int kt, int slot) {
+    bool seg1, in_k;
+    uint32_t kb;
+    step_scalars(kt, seg1, kb, in_k);
+    const __amdgpu_buffer_rsrc_t r = seg1 ? rB1 : rB0;
+#pragma unroll
+    for (int i = 0; i < B_INS; ++i) load_b(r, seg1, kb, in_k, i, slot);
   };
 
   // ---- LDS -> MFMA fragments -----------------------------------------------------
@@ -248,21 +257,25 @@ void gemm_kernel(GemmParams p) {
     frag_lane[ks] = (uint32_t)((lane & 31) * ROWB + (((2 * ks + (lane >> 5)) ^ key_lane) * 16));
   const uint32_t a_wave = (uint32_t)(wm * WM * 32 * ROWB);
   const uint32_t b_wave = (uint32_t)(B_BASE + wn * WN * 32 * ROWB);
-  auto read_frags = [&](int st, int ks, bf16x8 (&a)[WM], bf16x8 (&b)[WN]) {
-    const uint32_t ao = frag_lane[ks] + a_wave + st * A_STAGE;
-    const uint32_t bo = frag_lane[ks] + b_wave + st * B_STAGE;
+  auto read_frags = [&](int sa, int sb, int ks, bf16x8 (&a)[WM], bf16x8 (&b)[WN]) {
+    const uint32_t ao = frag_lane[ks] + a_wave + sa * A_STAGE;
+    const uint32_t bo = frag_lane[ks] + b_wave + sb * B_STAGE;
 #pragma unroll
     for (int bi = 0; bi < WM; ++bi) a[bi] = *(const bf16x8*)(lds + ao + bi * 32 * ROWB);
 #pragma unroll
     for (int bj = 0; bj < WN; ++bj) b[bj] = *(const bf16x8*)(lds + bo + bj * 32 * ROWB);
   };
-  // The same fragment reads with step kt's loads into stage st interleaved in
-  // program order (read j, load j): the compiler cannot tell the DMA's LDS
-  // writes from the reads apart, so this order is what lets the scheduling
-  // groups pair each MFMA with one read and one load.
-  auto read_and_load = [&](int st_r, int ks, bf16x8 (&a)[WM], bf16x8 (&b)[WN], int kt, int st) {
-    const uint32_t ao = frag_lane[ks] + a_wave + st_r * A_STAGE;
-    const uint32_t bo = frag_lane[ks] + b_wave + st_r * B_STAGE;
+  // Fragment reads with loads interleaved in program order (read j, load j):
+  // the compiler cannot tell the DMA's LDS writes from the reads apart, so
+  // this order is what lets the scheduling groups pair each MFMA with one
+  // read and its share of the loads.  IS_B selects the B loads of step kt
+  // (all of them) or A loads [lo, hi) of step kt.
+  auto read_and_load = [&](int sa, int sb, int ks, bf16x8 (&a)[WM], bf16x8 (&b)[WN], int kt,
+                           int slot, auto is_b, auto lo, auto hi) {
+    constexpr bool IS_B = decltype(is_b)::value;
+    constexpr int LO = decltype(lo)::value, HI = decltype(hi)::value;
+    const uint32_t ao = frag_lane[ks] + a_wave + sa * A_STAGE;
+    const uint32_t bo = frag_lane[ks] + b_wave + sb * B_STAGE;
     bool seg1, in_k;
     uint32_t kb;
     step_scalars(kt, seg1, kb, in_k);
@@ -270,12 +283,16 @@ void gemm_kernel(GemmParams p) {
     const __amdgpu_buffer_rsrc_t rB = seg1 ? rB1 : rB0;
     const uint32_t a_base = seg1 ? a_base1 : a_base0;
     const uint32_t a_step = seg1 ? a_step1 : a_step0;
-    constexpr int NJ = (WM + WN) > NL ? (WM + WN) : NL;
+    constexpr int NLD = HI - LO;
+    constexpr int NJ = (WM + WN) > NLD ? (WM + WN) : NLD;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       if (j < WM) a[j] = *(const bf16x8*)(lds + ao + j * 32 * ROWB);
       else if (j < WM + WN) b[j - WM] = *(const bf16x8*)(lds + bo + (j - WM) * 32 * ROWB);
-      if (j < NL) load_one(rA, rB, seg1, a_base, a_step, kb, in_k, j, st);
+      if (j < NLD) {
+        if constexpr (IS_B) load_b(rB, seg1, kb, in_k, LO + j, slot);
+        else load_a(rA, a_base, a_step, kb, in_k, LO + j, slot);
+      }
     }
   };
 
@@ -296,42 +313,65 @@ void gemm_kernel(GemmParams p) {
   };
 
   // ---- main loop -----------------------------------------------------------------
-  // Double-buffered: step kt computes on stage kt & 1.  Each of its KS MFMA
-  // sub-steps runs on fragments read during the previous one.  Before the
-  // last sub-step a full wait + barrier makes stage kt+1 (loaded during step
-  // kt-1) visible and retires every read of stage kt; the loads of step kt+2
-  // then refill stage kt & 1 while the last sub-step runs and the first
-  // fragments of step kt+1 are read, so a load has one whole step to land.
-  // Each sub-step is a scheduling region of its own (sched_barrier) in which
-  // groups pin the MFMA / read / load interleave.
+  // Step kt computes on A slot kt % 3 and B slot kt % 2.  Each of its KS MFMA
+  // sub-steps runs on fragments read during the previous one.  The A loads of
+  // step kt+2 go to the slot released at the previous barrier, spread over
+  // the first KS-1 sub-steps; before the last sub-step a wait + barrier makes
+  // step kt+1's slots visible and retires every read of step kt's, and the B
+  // loads of step kt+2 then refill B slot kt % 2 while the last sub-step runs
+  // and the first fragments of step kt+1 are read.  Loads thus flow through
+  // the whole step instead of in one burst per step, B loads have one step to
+  // land and A loads about one and a half; the wait leaves the A loads of
+  // this step in flight (vector-memory loads retire in order).  Each sub-step
+  // is a scheduling region of its own (sched_barrier) in which groups pin the
+  // MFMA / read / load interleave.
   constexpr int NREAD = WM + WN;
   constexpr int NMFMA = WM * WN;
+  constexpr int NA_W = A_TOT / kWaves;     // A loads every wave issues per step
   static_assert(NREAD < NMFMA, "need MFMAs to hide the fragment reads");
-  static_assert(KS % 2 == 0, "fragment double buffer parity");
+  static_assert(KS == 4, "A loads are spread over three sub-steps");
+  // A loads [0, A1), [A1, A2), [A2, A_INS) in sub-steps 0, 1, 2
+  constexpr int A1 = (A_INS + 2) / 3, A2 = A1 + (A_INS - A1 + 1) / 2;
+  using I0 = std::integral_constant<int, 0>;
+  using IA1 = std::integral_constant<int, A1>;
+  using IA2 = std::integral_constant<int, A2>;
+  using IAN = std::integral_constant<int, A_INS>;
+  using IBN = std::integral_constant<int, B_INS>;
   bf16x8 fa[2][WM], fb[2][WN];
-  issue_loads(0, 0);
-  wait_vm_lgkm0<0>();
+  issue_a(0, 0);
+  issue_b(0, 0);
+  issue_a(1, 1);
+  wait_vm_lgkm0<NA_W>();
   __builtin_amdgcn_s_barrier();
-  issue_loads(1, 1);
-  read_frags(0, 0, fa[0], fb[0]);
+  issue_b(1, 1);
+  read_frags(0, 0, 0, fa[0], fb[0]);
+  int sa = 0;                              // A slot of step kt (kt % 3)
   for (int kt = 0; kt < nk; ++kt) {
-    const int st = kt & 1;
-#pragma unroll
-    for (int ks = 0; ks < KS - 1; ++ks) {
-      __builtin_amdgcn_sched_barrier(0);
-      read_frags(st, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
-      mfmas(fa[ks & 1], fb[ks & 1]);
-      pin_groups<NMFMA, NREAD, 0, 0>();
-    }
-    wait_vm_lgkm0<0>();
+    const int sb = kt & 1;
+    const int sa_next = sa == NSLOT_A - 1 ? 0 : sa + 1;
+    const int sa_load = sa_next == NSLOT_A - 1 ? 0 : sa_next + 1;   // (kt + 2) % 3
+    __builtin_amdgcn_sched_barrier(0);
+    read_and_load(sa, sb, 1, fa[1], fb[1], kt + 2, sa_load, std::false_type{}, I0{}, IA1{});
+    mfmas(fa[0], fb[0]);
+    pin_groups<NMFMA, NREAD, A1, 0>();
+    __builtin_amdgcn_sched_barrier(0);
+    read_and_load(sa, sb, 2, fa[0], fb[0], kt + 2, sa_load, std::false_type{}, IA1{}, IA2{});
+    mfmas(fa[1], fb[1]);
+    pin_groups<NMFMA, NREAD, A2 - A1, 0>();
+    __builtin_amdgcn_sched_barrier(0);
+    read_and_load(sa, sb, 3, fa[1], fb[1], kt + 2, sa_load, std::false_type{}, IA2{}, IAN{});
+    mfmas(fa[0], fb[0]);
+    pin_groups<NMFMA, NREAD, A_INS - A2, 0>();
+    wait_vm_lgkm0<NA_W>();
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    read_and_load(st ^ 1, 0, fa[0], fb[0], kt + 2, st);
+    read_and_load(sa_next, sb ^ 1, 0, fa[0], fb[0], kt + 2, sb, std::true_type{}, I0{}, IBN{});
     mfmas(fa[1], fb[1]);
-    pin_groups<NMFMA, NREAD, NL, 0>();
+    pin_groups<NMFMA, NREAD, B_INS, 0>();
+    sa = sa_next;
   }
   // all LDS-DMA writes (including the out-of-range loads past the end) have
-  // landed and every wave is done with the ring before LDS is reused below
+  // landed and every wave is done with the rings before LDS is reused below
   wait_vm_lgkm0<0>();
   __builtin_amdgcn_s_barrier();
 
