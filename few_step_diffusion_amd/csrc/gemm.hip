@@ -8,27 +8,34 @@
 // up-projection costs no extra pass over Y.  The SwiGLU epilogue follows
 // Shazeer, "GLU Variants Improve Transformer" (2020).
 //
-// Kernel shape (one workgroup = 4 waves of 64 lanes, one output tile):
-//   * tile BM x BN = 256 x (64·WN); each wave owns a (32·WM) x (32·WN)
-//     sub-tile = WM x WN blocks of v_mfma_f32_32x32x16_bf16 (fp32
-//     accumulators, 256 of them per lane at WM = WN = 4).  The W fragment is
-//     the MFMA's first operand, so a lane ends up owning 4 consecutive output
-//     columns of one token.
+// Kernel shape (one workgroup = 8 waves of 64 lanes, two per SIMD, one
+// output tile):
+//   * tile BM x BN = 256 x (64·WN); the waves form a 4 x 2 grid, each owning
+//     a (32·WM) x (32·WN) sub-tile = WM x WN blocks of
+//     v_mfma_f32_32x32x16_bf16 with fp32 accumulators (128 per lane at
+//     WM = 2, WN = 4).  The W fragment is the MFMA's first operand, so a lane
+//     ends up owning 4 consecutive output columns of one token.
 //   * operands are K-contiguous rows (X row-major, W0 in out x in layout): a
 //     lane's MFMA fragment (8 consecutive k of one row) is one 16-byte chunk.
-//   * K is staged through a ring of NSTAGE LDS stages of BK = 32 columns.
-//     Global -> LDS uses 16-byte LDS-DMA buffer loads (buffer_load ... lds):
-//     no VGPR staging, and the buffer range check turns rows past M or N (and,
-//     by pushing the offset out of range, a K tail) into zeros.  Loads run
-//     NSTAGE-1 steps ahead, so about 96 KB per CU are in flight against the
-//     ~1 us latency of L2 misses.
-//   * each 64-byte tile row stores its four chunks XOR-swizzled by
-//     ((row>>1) ^ (row>>3)) & 3: fragment reads of 8 or 16 consecutive rows
-//     then hit distinct banks (no bank conflicts in either a 32- or 64-bank
-//     model).
-//   * one barrier per K step (a partial vmcnt wait keeps the younger stages in
-//     flight); the fragments of the next 16-k sub-step are read while the 16
-//     MFMAs of the current one run, pinned by scheduling groups.
+//   * K is staged in steps of BK = 64, so a tile row of one step is one
+//     128-byte L2 line and every L2 request is a whole line (at BK = 32 the
+//     64-byte half-line requests doubled the L2 request rate, which was the
+//     limit).  Global -> LDS uses 16-byte LDS-DMA buffer loads
+//     (buffer_load ... lds): no VGPR staging, and the buffer range check turns
+//     rows past M or N (and, by pushing the offset out of range, a K tail)
+//     into zeros.
+//   * A sits in a ring of three LDS slots and B in a ring of two (160 KB of
+//     LDS in all).  The A loads of step kt+2 are spread over the first three
+//     MFMA sub-steps of step kt and the B loads follow the step's barrier,
+//     so the loads of the whole workgroup (and, since all CUs run in step,
+//     of the chip) flow through each step instead of arriving as one burst
+//     per step, which left the load path busy but starved.
+//   * each 128-byte tile row stores its eight chunks XOR-swizzled by
+//     (row>>1) & 7: the fragment reads of 16 consecutive rows then cover all
+//     16 chunk slots of a 256-byte bank line (no bank conflicts).
+//   * one barrier per K step; the fragments of the next 16-k sub-step are
+//     read while the MFMAs of the current one run, pinned by scheduling
+//     groups together with the loads.
 //   * workgroup ids are remapped so that each XCD (ids round-robin over 8)
 //     gets a contiguous run of tiles, ordered in groups of 4 tile-rows: the
 //     32 tiles an XCD runs at once share 4 X tiles and 8 W tiles in its L2.
