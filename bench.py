@@ -12,8 +12,9 @@ Prints ONE JSON line on stdout (everything else goes to stderr):
              epilogue): its algorithmic flops per launch / its mean launch
              time from HIP events on its stream, against 2500 TFLOP/s bf16
   kernels    the same for every kernel of the step
-  elementwise  renoise / Euler GB/s at the 2K and 4K latents, cache-cold
-             (a 1 GiB write between repetitions), 12 bytes per element
+  elementwise  renoise / Euler GB/s at the 768P, 2K and 4K latents, 12 bytes
+             per element, cache-cold (a 1 GiB read between repetitions) and
+             warm; median / min / max of 20 after 5 warm-ups
   cpu_baseline the fp64 oracle on a bounded sample of tokens on host cores
 """
 from __future__ import annotations
@@ -32,6 +33,7 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 DOMINANT = "gate_up.up"
+SPIN_CYCLES = 200_000          # ~0.1 ms GPU spin queued ahead of a timed region
 
 
 def log(*a):
@@ -85,36 +87,51 @@ def kernel_times(events):
     return out
 
 
-def elementwise(torch, fsd, inputs):
-    """Cold renoise / Euler bandwidth at the 2K and 4K latents."""
+def elementwise(torch, fsd, inputs, warmup=5, reps=20):
+    """Renoise / Euler bandwidth at the 768P, 2K and 4K latents.
+
+    cold: before every repetition a 1 GiB buffer is read (not written), so
+    none of the operands is in L2 or the Infinity Cache and no dirty lines of
+    the flush are left for the timed kernel to write back; warm: the same
+    launch repeated with nothing in between.  Median, min and max of `reps`
+    repetitions after `warmup` untimed ones, HIP events on the current stream.
+    """
     dev = torch.device("cuda:0")
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
     res = {}
-    for wid, tag in ((2, "2k"), (3, "4k")):
+    for wid, tag in ((1, "768p"), (2, "2k"), (3, "4k")):
         n = inputs.WORKLOADS[wid].latent_elems
         u = torch.randn(n, device=dev)
         e = torch.randn(n, device=dev)
         z = torch.empty(n, device=dev)
         for name in ("renoise", "euler"):
-            ts = []
-            for rep in range(12):
-                flush.fill_(rep & 0xff)
-                a = torch.cuda.Event(enable_timing=True)
-                b = torch.cuda.Event(enable_timing=True)
-                a.record()
-                if name == "renoise":
-                    fsd.renoise(u, e, 0.909, out=z)
-                else:
-                    fsd.euler_step(z, e, 0.909, 0.857)
-                b.record()
-                torch.cuda.synchronize()
-                if rep >= 2:
-                    ts.append(a.elapsed_time(b))
-            med = statistics.median(ts)
-            gbs = 12.0 * n / (med * 1e-3) / 1e9
-            res[f"{name}_{tag}"] = {"us": round(med * 1e3, 2), "GB/s": round(gbs, 1),
-                                    "frac_hbm": round(gbs / PEAK_HBM_GBS, 3),
-                                    "bytes": 12 * n}
+            for mode in ("cold", "warm"):
+                ts = []
+                for rep in range(warmup + reps):
+                    # keep the GPU busy while the timed launch is enqueued, so the
+                    # interval holds the kernel and not the host's launch latency:
+                    # the 1 GiB read does it for the cold runs, a spin for the warm
+                    if mode == "cold":
+                        flush.sum()
+                    else:
+                        torch.cuda._sleep(SPIN_CYCLES)
+                    a = torch.cuda.Event(enable_timing=True)
+                    b = torch.cuda.Event(enable_timing=True)
+                    a.record()
+                    if name == "renoise":
+                        fsd.renoise(u, e, 0.909, out=z)
+                    else:
+                        fsd.euler_step(z, e, 0.909, 0.857)
+                    b.record()
+                    torch.cuda.synchronize()
+                    if rep >= warmup:
+                        ts.append(a.elapsed_time(b))
+                med = statistics.median(ts)
+                gbs = 12.0 * n / (med * 1e-3) / 1e9
+                key = f"{name}_{tag}" if mode == "cold" else f"{name}_{tag}_warm"
+                res[key] = {"us": round(med * 1e3, 2), "min_us": round(min(ts) * 1e3, 2),
+                            "max_us": round(max(ts) * 1e3, 2), "GB/s": round(gbs, 1),
+                            "frac_hbm": round(gbs / PEAK_HBM_GBS, 3), "bytes": 12 * n}
         del u, e, z
     del flush
     torch.cuda.empty_cache()
@@ -184,19 +201,24 @@ def main():
         log(f"warmup {w + 1}/{args.warmup} done")
     per_kernel = {}
     step_ms = []
+    step_events = []
     torch.cuda.synchronize()
     t_start = time.perf_counter()
+    # the K steps run back to back (events are read after the final sync), so
+    # every launch is queued behind running work and each interval between
+    # marks is kernel time, not host launch latency
+    torch.cuda._sleep(SPIN_CYCLES)
     for s in range(args.steps):
         model.events = []
         model.refine(u, eps)
-        torch.cuda.synchronize()
-        ev = model.events
+        step_events.append(model.events)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t_start) / args.steps * 1e3
+    for s, ev in enumerate(step_events):
         step_ms.append(ev[0][1].elapsed_time(ev[-1][1]))
         for k, v in kernel_times(ev).items():
             per_kernel.setdefault(k, []).extend(v)
         log(f"step {s + 1}/{args.steps}: {step_ms[-1]:.2f} ms")
-    torch.cuda.synchronize()
-    wall = (time.perf_counter() - t_start) / args.steps * 1e3
     model.events = None
 
     flops = model.flops_per_step()
@@ -207,7 +229,9 @@ def main():
     kernels = {}
     for name, ts in per_kernel.items():
         mean = statistics.mean(ts)
-        ent = {"launches_per_step": len(ts) // args.steps, "mean_us": round(mean * 1e3, 1)}
+        ent = {"launches_per_step": len(ts) // args.steps, "mean_us": round(mean * 1e3, 1),
+               "median_us": round(statistics.median(ts) * 1e3, 1),
+               "min_us": round(min(ts) * 1e3, 1), "max_us": round(max(ts) * 1e3, 1)}
         if name in flops:
             per_launch = flops[name] / steps_per_refine
             ent["tflops"] = round(per_launch / (mean * 1e-3) / 1e12, 1)

@@ -287,6 +287,7 @@ int fsd_token_embed(const float* z, const void* E, void* X, int64_t ldx, int64_t
   if (M == 0) return FSD_OK;
   if (!z || !E || !X || ldx < D || ldx % 8) return FSD_EINVAL;
   if (!aligned16(X) || ((uintptr_t)z & 3u) || ((uintptr_t)E & 1u)) return FSD_EALIGN;
+  if (C * D * 2 > kMaxOffsetBytes) return FSD_EUNSUPPORTED;
   const int64_t xb = span_bytes(M, D, ldx, 2);
   if (overlap(X, xb, z, M * C * 4) || overlap(X, xb, E, D * C * 2)) return FSD_EINVAL;
   return from_hip(fsd::launch_embed(z, (const bf16_t*)E, (bf16_t*)X, ldx, M, (int)C, D,

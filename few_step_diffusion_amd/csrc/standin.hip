@@ -5,10 +5,15 @@
 // High-Resolution Video Refinement with Few-Step Diffusion" (agientry.com),
 // section "Why upscaling happens in latent space", shape equation.
 //
-// embed: X[m, n] = bf16(sum_c z[m, c]·E[n, c]).  K = C is tiny (24), so this
-//   is a write-bound outer product: each lane keeps two columns of E in
-//   registers, a block stages 64 latent rows in LDS and streams out 64 rows of
-//   X (1 KiB contiguous per row per block).  fp32 FMAs, no MFMA: z stays fp32.
+// embed: X[m, n] = bf16(sum_c z[m, c]·E[n, c]).  K = C is tiny (<= 32), so
+//   the kernel is bound by writing X.  The sums run on MFMA with fp32
+//   accumulation: z (fp32) is split as z = zh + zl with zh = bf16(z) and
+//   zl = bf16(z - zh), which leaves a relative error below 2^-16 in z, far
+//   under the bf16 rounding of X itself, and X = zh·Eᵀ + zl·Eᵀ takes two
+//   32x32x16 bf16 MFMAs per 16 channels.  E is the MFMA's first operand, so a
+//   lane holds 4 consecutive columns of one token and writes them as one
+//   8-byte store.  One wave owns 128 tokens x 512 columns: its z fragments
+//   are loaded once, and each E fragment serves 4 blocks of 32 tokens.
 // head:  v[m, c] = sum_n H[m, n]·P[c, n].  A read-bound GEMM with N = C <= 32:
 //   each wave owns 128 rows and the 32 (zero-padded) columns, one
 //   32x32x16 bf16 MFMA per (32-row block, 16 k).  Within every 64-wide slice of
@@ -24,11 +29,13 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
 constexpr int kMaxC = 32;
-constexpr int kEmbedRows = 64;
-constexpr int kEmbedCols = 2 * kThreads;   // two output columns per lane
+constexpr int kEmbedTokens = 128;          // tokens per wave (4 MFMA blocks)
+constexpr int kEmbedCols = 512;            // output columns per wave
+constexpr uint32_t kOutOfRange = 0x80000000u;
 constexpr int kHeadRowsPerWave = 128;
 
 __device__ __forceinline__ float bf16_to_f32(bf16_t h) {
@@ -40,35 +47,107 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
                                            0x00020000);
 }
 
+// Physical 16-byte chunk of logical chunk c in staged row r: XOR with bits
+// 1..3 of the row spreads 16 consecutive rows over the 16 chunk slots of a
+// 256-byte bank line.
+__device__ __forceinline__ int embed_swz(int r, int c) { return c ^ ((r >> 1) & 7); }
+
 __global__ __launch_bounds__(kThreads) void embed_kernel(const float* z, const bf16_t* E,
                                                          bf16_t* X, int64_t ldx, int64_t M,
-                                                         int C, int64_t D) {
-  __shared__ float zs[kEmbedRows * kMaxC];
-  const int64_t m0 = (int64_t)blockIdx.y * kEmbedRows;
-  const int rows = (int)((M - m0) < kEmbedRows ? (M - m0) : kEmbedRows);
-  for (int i = threadIdx.x; i < rows * C; i += kThreads) zs[i] = z[m0 * C + i];
-  const int64_t n = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 2;
-  float e0[kMaxC], e1[kMaxC];
+                                                         int C, int64_t D, int vec_e) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave_id = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  const int64_t nchunk = (D + kEmbedCols - 1) / kEmbedCols;
+  const int64_t m0 = (wave_id / nchunk) * kEmbedTokens;
+  const int64_t c0 = (wave_id % nchunk) * kEmbedCols;
+  if (m0 >= M) return;
+  const int j = lane & 31;
+  const int h = lane >> 5;
+  // z fragments (operand B): token m0 + 32·bi + j, channels 16·kb + 8·h + e
+  bf16x8 zh[4][2], zl[4][2];
 #pragma unroll
-  for (int c = 0; c < kMaxC; ++c) {
-    e0[c] = (n < D && c < C) ? bf16_to_f32(E[n * C + c]) : 0.0f;
-    e1[c] = (n < D && c < C) ? bf16_to_f32(E[(n + 1) * C + c]) : 0.0f;
+  for (int bi = 0; bi < 4; ++bi) {
+    const int64_t t = m0 + 32 * bi + j;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int c = 16 * kb + 8 * h + e;
+        const float v = (t < M && c < C) ? z[t * C + c] : 0.0f;
+        const __bf16 hi = (__bf16)v;
+        zh[bi][kb][e] = hi;
+        zl[bi][kb][e] = (__bf16)(v - (float)hi);
+      }
   }
-  __syncthreads();
-  if (n >= D) return;
-  for (int r = 0; r < rows; ++r) {
-    const float* zr = zs + r * C;
-    float s0 = 0.0f, s1 = 0.0f;
+  // E fragments (operand A): column n0 + j, channels 16·kb + 8·h + e.  Rows
+  // past D fall outside the buffer and read as zeros; channels past C are
+  // masked (they would read the next row).
+  const __amdgpu_buffer_rsrc_t rE = make_rsrc(E, D * C * 2);
+  // per-wave staging: 128 tokens x 64 columns (128 B per token row)
+  __shared__ __attribute__((aligned(16))) char stage_all[(kThreads / 64) * kEmbedTokens * 128];
+  char* stage = stage_all + (threadIdx.x >> 6) * kEmbedTokens * 128;
+  const int64_t c_end = (c0 + kEmbedCols) < D ? (c0 + kEmbedCols) : D;
+  for (int64_t n0 = c0; n0 < c_end; n0 += 32) {
+    const int64_t n = n0 + j;
+    bf16x8 ef[2];
 #pragma unroll
-    for (int c = 0; c < kMaxC; ++c) {
-      if (c < C) {
-        s0 = fmaf(zr[c], e0[c], s0);
-        s1 = fmaf(zr[c], e1[c], s1);
+    for (int kb = 0; kb < 2; ++kb) {
+      const int k0 = 16 * kb + 8 * h;
+      if (vec_e) {
+        const uint32_t off = k0 < C ? (uint32_t)((n * C + k0) * 2) : kOutOfRange;
+        ef[kb] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rE, off, 0, 0));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t off = (k0 + e) < C ? (uint32_t)((n * C + k0 + e) * 2) : kOutOfRange;
+          const uint16_t bits = __builtin_amdgcn_raw_buffer_load_b16(rE, off, 0, 0);
+          ef[kb][e] = __builtin_bit_cast(__bf16, bits);
+        }
       }
     }
-    const uint32_t packed = (uint32_t)__builtin_bit_cast(bf16_t, (__bf16)s0) |
-                            ((uint32_t)__builtin_bit_cast(bf16_t, (__bf16)s1) << 16);
-    *(uint32_t*)(X + (m0 + r) * ldx + n) = packed;
+    f32x16 acc[4];
+#pragma unroll
+    for (int bi = 0; bi < 4; ++bi) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[bi][e] = 0.0f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        acc[bi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ef[kb], zh[bi][kb], acc[bi], 0, 0, 0);
+        acc[bi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ef[kb], zl[bi][kb], acc[bi], 0, 0, 0);
+      }
+    }
+    // Stage: lane holds token 32·bi + j, columns n0 + 8·g + 4·h + 0..3, i.e.
+    // 8 bytes of logical chunk (n0 % 64)/8 + g of its staged row.
+    const int half = (int)((n0 - c0) >> 5) & 1;
+#pragma unroll
+    for (int bi = 0; bi < 4; ++bi) {
+      const int r = 32 * bi + j;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        u32x2 pk;
+        pk.x = (uint32_t)__builtin_bit_cast(bf16_t, (__bf16)acc[bi][4 * g]) |
+               ((uint32_t)__builtin_bit_cast(bf16_t, (__bf16)acc[bi][4 * g + 1]) << 16);
+        pk.y = (uint32_t)__builtin_bit_cast(bf16_t, (__bf16)acc[bi][4 * g + 2]) |
+               ((uint32_t)__builtin_bit_cast(bf16_t, (__bf16)acc[bi][4 * g + 3]) << 16);
+        *(u32x2*)(stage + r * 128 + (embed_swz(r, 4 * half + g) << 4) + 8 * h) = pk;
+      }
+    }
+    // every 64 columns (or at the end of the wave's range) write whole rows
+    if (half == 1 || n0 + 32 >= c_end) {
+      const int64_t col = n0 - 32 * half;            // first column of the staged slab
+      __builtin_amdgcn_s_waitcnt(0xc07f);            // lgkmcnt(0): the wave's staging is done
+#pragma unroll 4
+      for (int it = 0; it < kEmbedTokens / 8; ++it) {
+        const int r = 8 * it + (lane >> 3);
+        const int pc = lane & 7;
+        const int lc = embed_swz(r, pc);             // the swizzle is an involution
+        const int64_t t = m0 + r;
+        const int64_t nn = col + 8 * lc;
+        const u32x4 v = *(const u32x4*)(stage + r * 128 + (pc << 4));
+        if (t < M && nn < D) __builtin_nontemporal_store(v, (u32x4*)(X + t * ldx + nn));
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);            // reads done before the next slab's writes
+    }
   }
 }
 
@@ -126,9 +205,13 @@ __global__ __launch_bounds__(kThreads) void head_kernel(const bf16_t* H, int64_t
 hipError_t launch_embed(const float* z, const bf16_t* E, bf16_t* X, int64_t ldx, int64_t M,
                         int C, int64_t D, hipStream_t s) {
   if (M == 0) return hipSuccess;
-  const dim3 grid((unsigned)((D + kEmbedCols - 1) / kEmbedCols),
-                  (unsigned)((M + kEmbedRows - 1) / kEmbedRows));
-  hipLaunchKernelGGL(embed_kernel, grid, dim3(kThreads), 0, s, z, E, X, ldx, M, C, D);
+  const int64_t waves = ((M + kEmbedTokens - 1) / kEmbedTokens) *
+                        ((D + kEmbedCols - 1) / kEmbedCols);
+  const int64_t blocks = (waves + kThreads / 64 - 1) / (kThreads / 64);
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  const int vec_e = (C % 8 == 0) && (((uintptr_t)E & 15u) == 0);
+  hipLaunchKernelGGL(embed_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, z, E, X, ldx,
+                     M, C, D, vec_e);
   return hipGetLastError();
 }
 

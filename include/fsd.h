@@ -184,9 +184,11 @@ int fsd_euler_step(float* z, const float* v, float sigma, float sigma_next,
  * [EN] section "Why upscaling happens in latent space", shape equation) and
  * the model width D.
  *
- * fsd_token_embed:  X[m, n] = bf16( sum_c z[m, c]·E[n, c] ),  fp32 sums.
+ * fsd_token_embed:  X[m, n] = bf16( sum_c z[m, c]·E[n, c] ),  fp32 sums
+ *   (z enters as the bf16 pair hi + lo, within 2^-16 relative of z).
  *   z fp32 [M, C] (row stride C), E bf16 [D, C] (row stride C),
- *   X bf16 [M, D] row stride ldx >= D.  1 <= C <= 32, D multiple of 8.
+ *   X bf16 [M, D] row stride ldx >= D.  1 <= C <= 32, D multiple of 8,
+ *   C·D·2 < 2^31 (else FSD_EUNSUPPORTED).
  * fsd_token_head:   v[m, c] = sum_n H[m, n]·P[c, n],  fp32 sums, fp32 out.
  *   H bf16 [M, D] row stride ldh >= D, P bf16 [C, D] (row stride D),
  *   v fp32 [M, C] (row stride C).  1 <= C <= 32, D multiple of 64.
