@@ -14,12 +14,14 @@
 //   lane holds 4 consecutive columns of one token and writes them as one
 //   8-byte store.  One wave owns 128 tokens x 512 columns: its z fragments
 //   are loaded once, and each E fragment serves 4 blocks of 32 tokens.
-// head:  v[m, c] = sum_n H[m, n]·P[c, n].  A read-bound GEMM with N = C <= 32:
-//   each wave owns 128 rows and the 32 (zero-padded) columns, one
-//   32x32x16 bf16 MFMA per (32-row block, 16 k).  Within every 64-wide slice of
-//   k a lane walks 32 contiguous k (64 bytes) of its row; the MFMA's sum over k
-//   does not depend on which k a lane supplies as long as H and P agree, so
-//   both operands use the same assignment.
+// head:  v[m, c] = sum_n H[m, n]·P[c, n].  A read-bound GEMM with N = C <= 32
+//   (zero-padded to 32).  One wave per block owns 64 rows (two 32-row MFMA
+//   blocks) and walks k in steps of 64 through a 4-stage LDS ring filled by
+//   LDS-DMA (buffer_load ... lds): every load moves whole 128-byte lines of H
+//   (8 rows x 128 B), which direct register loads in the MFMA's lane layout
+//   (one row per lane) cannot.  Each stage also holds the 32 x 64 slab of P;
+//   rows past M or C fall outside their buffers and read as zeros.  Rows are
+//   stored with their 16-byte chunks XOR-swizzled by (row >> 1) & 7.
 #include "fsd_internal.h"
 
 namespace fsd {
@@ -36,7 +38,11 @@ constexpr int kMaxC = 32;
 constexpr int kEmbedTokens = 128;          // tokens per wave (4 MFMA blocks)
 constexpr int kEmbedCols = 512;            // output columns per wave
 constexpr uint32_t kOutOfRange = 0x80000000u;
-constexpr int kHeadRowsPerWave = 128;
+constexpr int kHeadRows = 64;                // rows per (one-wave) block
+constexpr int kHeadStages = 4;
+constexpr int kHeadHBytes = kHeadRows * 128;  // 64 k of 64 rows
+constexpr int kHeadStage = kHeadHBytes + 32 * 128;   // + 64 k of 32 (padded) P rows
+constexpr int kHeadLoads = kHeadRows / 8 + 4;        // LDS-DMA loads per stage
 
 __device__ __forceinline__ float bf16_to_f32(bf16_t h) {
   return __uint_as_float((uint32_t)h << 16);
@@ -151,51 +157,86 @@ __global__ __launch_bounds__(kThreads) void embed_kernel(const float* z, const b
   }
 }
 
-__global__ __launch_bounds__(kThreads) void head_kernel(const bf16_t* H, int64_t ldh,
-                                                        const bf16_t* P, float* v, int64_t M,
-                                                        int64_t D, int C) {
-  const int lane = threadIdx.x & 63;
-  const int64_t wave_id = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-  const int64_t m0 = wave_id * kHeadRowsPerWave;
-  if (m0 >= M) return;
-  const int64_t rows_valid = (M - m0) < kHeadRowsPerWave ? (M - m0) : kHeadRowsPerWave;
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+template <int n>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(n >= 0 && n < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (0 << 8) | ((n >> 4) << 14));
+}
+
+__global__ __launch_bounds__(64) void head_kernel(const bf16_t* H, int64_t ldh, const bf16_t* P,
+                                                  float* v, int64_t M, int64_t D, int C) {
+  __shared__ __attribute__((aligned(1024))) char lds[kHeadStages * kHeadStage];
+  const int lane = threadIdx.x;
+  const int64_t m0 = (int64_t)blockIdx.x * kHeadRows;
+  const int64_t rows_valid = (M - m0) < kHeadRows ? (M - m0) : kHeadRows;
   const __amdgpu_buffer_rsrc_t rH = make_rsrc(H + m0 * ldh, rows_valid * ldh * 2);
   const __amdgpu_buffer_rsrc_t rP = make_rsrc(P, (int64_t)C * D * 2);   // rows >= C read 0
-  const int j = lane & 31;
-  const int h = lane >> 5;
-  f32x16 acc[4];
+  const int nk = (int)(D / 64);
+  // LDS-DMA: load i moves rows 8i .. 8i+7 of the stage's H slab (i < 8) or of
+  // its P slab (i >= 8); lane l fills row 8i + l/8, physical chunk l%8 with
+  // logical chunk swz(row, l%8).  The key ((8i + l/8) >> 1) & 7 only depends
+  // on the lane and on the parity of i.
+  const int lrow = lane >> 3;
+  const uint32_t cx_even = (uint32_t)(((lane & 7) ^ ((lrow >> 1) & 7)) * 16);
+  const uint32_t cx_odd = (uint32_t)(((lane & 7) ^ (((lrow >> 1) + 4) & 7)) * 16);
+  auto issue = [&](int kt, int st) {
+    const bool live = kt < nk;
+    const uint32_t kb = (uint32_t)kt * 128;
+    char* base = lds + st * kHeadStage;
 #pragma unroll
-  for (int bi = 0; bi < 4; ++bi)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) acc[bi][e] = 0.0f;
-  const uint32_t p_row = (uint32_t)(j * D * 2);
-  uint32_t h_row[4];
-#pragma unroll
-  for (int bi = 0; bi < 4; ++bi) h_row[bi] = (uint32_t)((bi * 32 + j) * ldh * 2);
-  for (int64_t k0 = 0; k0 < D; k0 += 64) {
-    u32x4 pf[4], hf[4][4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const uint32_t koff = (uint32_t)((k0 + 32 * h + 8 * s) * 2);
-      pf[s] = __builtin_amdgcn_raw_buffer_load_b128(rP, p_row + koff, 0, 0);
-#pragma unroll
-      for (int bi = 0; bi < 4; ++bi)
-        hf[bi][s] = __builtin_amdgcn_raw_buffer_load_b128(rH, h_row[bi] + koff, 0, 0);
+    for (int i = 0; i < kHeadRows / 8; ++i) {
+      const uint32_t cx = (i & 1) ? cx_odd : cx_even;
+      const uint32_t off = live ? (uint32_t)((8 * i + lrow) * ldh * 2) + kb + cx : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rH, (lds_ptr_t)(base + i * 1024), 16, off, 0, 0, 0);
     }
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t cx = (i & 1) ? cx_odd : cx_even;
+      const uint32_t off = live ? (uint32_t)((8 * i + lrow) * D * 2) + kb + cx : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rP, (lds_ptr_t)(base + kHeadHBytes + i * 1024), 16,
+                                               off, 0, 0, 0);
+    }
+  };
+  // fragments: lane l reads row 32·bi + l%32 (P: row l%32), logical chunk
+  // 2·ks + l/32; for such rows the key ((l%32) >> 1) & 7 is the lane's own
+  const int j = lane & 31;
+  const int h = lane >> 5;
+  const int key = (j >> 1) & 7;
+  f32x16 acc[2];
 #pragma unroll
-      for (int bi = 0; bi < 4; ++bi)
-        acc[bi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, hf[bi][s]),
-                                                          __builtin_bit_cast(bf16x8, pf[s]),
-                                                          acc[bi], 0, 0, 0);
+  for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[bi][e] = 0.0f;
+#pragma unroll
+  for (int st = 0; st < kHeadStages - 1; ++st) issue(st, st);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int st = kt % kHeadStages;
+    wait_vm_lgkm0<(kHeadStages - 2) * kHeadLoads>();   // step kt has landed
+    // stage (kt - 1) % stages was read in the previous iteration (those reads
+    // have retired: the wait above also drained lgkmcnt)
+    issue(kt + kHeadStages - 1, (kt + kHeadStages - 1) % kHeadStages);
+    const char* base = lds + st * kHeadStage;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int co = ((2 * ks + h) ^ key) * 16;
+      const bf16x8 pf = *(const bf16x8*)(base + kHeadHBytes + j * 128 + co);
+#pragma unroll
+      for (int bi = 0; bi < 2; ++bi) {
+        const bf16x8 hf = *(const bf16x8*)(base + (32 * bi + j) * 128 + co);
+        acc[bi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hf, pf, acc[bi], 0, 0, 0);
+      }
+    }
   }
+  wait_vm_lgkm0<0>();   // the out-of-range loads past the end have landed too
   if (j >= C) return;
+  // lane holds channel j of rows 32·bi + 8·(e/4) + 4·h + e%4
 #pragma unroll
-  for (int bi = 0; bi < 4; ++bi)
+  for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const int i = bi * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+      const int i = 32 * bi + 8 * (e >> 2) + 4 * h + (e & 3);
       if (i < rows_valid) v[(m0 + i) * C + j] = acc[bi][e];
     }
 }
@@ -218,10 +259,9 @@ hipError_t launch_embed(const float* z, const bf16_t* E, bf16_t* X, int64_t ldx,
 hipError_t launch_head(const bf16_t* H, int64_t ldh, const bf16_t* P, float* v, int64_t M,
                        int64_t D, int C, hipStream_t s) {
   if (M == 0) return hipSuccess;
-  const int64_t waves = (M + kHeadRowsPerWave - 1) / kHeadRowsPerWave;
-  const int64_t blocks = (waves + 3) / 4;
-  hipLaunchKernelGGL(head_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, H, ldh, P, v, M,
-                     D, C);
+  const int64_t blocks = (M + kHeadRows - 1) / kHeadRows;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(head_kernel, dim3((unsigned)blocks), dim3(64), 0, s, H, ldh, P, v, M, D, C);
   return hipGetLastError();
 }
 

@@ -277,6 +277,29 @@ def test_embed_and_head(gpu):
     assert_gemm(v.cpu().numpy(), oracle.head_rows(f32(H), f32(P)), "head")
 
 
+@pytest.mark.parametrize("M,C,D", [(1, 1, 64), (65, 7, 96), (129, 32, 192), (300, 24, 1000),
+                                   (64, 8, 576)])
+def test_embed_shapes(gpu, M, C, D):
+    """Tails in tokens (past 128 per wave), in columns (odd 32-column tile
+    counts, D not a multiple of 32 or of the 512-column wave range), and the
+    scalar E path (C not a multiple of 8)."""
+    say(f"embed M={M} C={C} D={D}")
+    z = inputs.normal((M, C), 1.0, 93)
+    E, _ = inputs.standin_projections(4, C, D)
+    X = fsd.token_embed(z.to(gpu), E.to(gpu))
+    assert_gemm(f32(X), oracle.embed_rows(z.numpy(), f32(E)), "embed")
+
+
+@pytest.mark.parametrize("M,C,D", [(1, 1, 64), (63, 7, 128), (65, 32, 192), (1000, 24, 640)])
+def test_head_shapes(gpu, M, C, D):
+    """Row tails around the 64-row block, every C up to 32, short K loops."""
+    say(f"head M={M} C={C} D={D}")
+    _, P = inputs.standin_projections(4, C, D)
+    H = inputs.normal((M, D), 1.0, 94, dtype=torch.bfloat16)
+    v = fsd.token_head(H.to(gpu), P.to(gpu))
+    assert_gemm(v.cpu().numpy(), oracle.head_rows(f32(H), f32(P)), "head")
+
+
 # ------------------------------------------------------- full-size shapes
 def _full_linear(gpu, wid, label, K, N, layer=0, M=None, rows=384):
     M = inputs.WORKLOADS[wid].tokens if M is None else M
