@@ -25,17 +25,18 @@
 //     rows past M or N (and, by pushing the offset out of range, a K tail)
 //     into zeros.
 //   * A sits in a ring of three LDS slots and B in a ring of two (160 KB of
-//     LDS in all).  The A loads of step kt+2 are spread over the first three
-//     MFMA sub-steps of step kt and the B loads follow the step's barrier,
-//     so the loads of the whole workgroup (and, since all CUs run in step,
-//     of the chip) flow through each step instead of arriving as one burst
-//     per step, which left the load path busy but starved.
+//     LDS in all).
+//   * ping-pong: the two waves on a SIMD (waves w and w + 4) belong to two
+//     groups that alternate, each K step, between a compute phase (all
+//     MFMAs of the step back to back from fragments already in registers)
+//     and a memory phase (every fragment of the next step from LDS, plus its
+//     share of the LDS-DMA loads: group 1 loads A, group 0 loads B).  Two
+//     barriers per step switch the phases, so a SIMD's MFMA pipe always has
+//     one wave streaming MFMAs while the other does its memory work, instead
+//     of both interleaving reads, loads and MFMAs.
 //   * each 128-byte tile row stores its eight chunks XOR-swizzled by
 //     (row>>1) & 7: the fragment reads of 16 consecutive rows then cover all
 //     16 chunk slots of a 256-byte bank line (no bank conflicts).
-//   * one barrier per K step; the fragments of the next 16-k sub-step are
-//     read while the MFMAs of the current one run, pinned by scheduling
-//     groups together with the loads.
 //   * workgroup ids are remapped so that each XCD (ids round-robin over 8)
 //     gets a contiguous run of tiles, ordered in groups of 4 tile-rows: the
 //     32 tiles an XCD runs at once share 4 X tiles and 8 W tiles in its L2.
@@ -95,21 +96,6 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
   __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (0 << 8) | ((n >> 4) << 14));
 }
 
-// Scheduling groups of one MFMA sub-step: an LDS read after each of the first
-// NREAD MFMAs and NLOAD global->LDS loads spread evenly over all of them.
-template <int NMFMA, int NREAD, int NLOAD, int J>
-__device__ __forceinline__ void pin_groups() {
-  if constexpr (J < NMFMA) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA
-    if constexpr (J < NREAD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
-    constexpr int nl = ((J + 1) * NLOAD) / NMFMA - (J * NLOAD) / NMFMA;
-    if constexpr (nl > 0) __builtin_amdgcn_sched_group_barrier(0x020, nl, 0);     // loads
-    pin_groups<NMFMA, NREAD, NLOAD, J + 1>();
-  } else {
-    __builtin_amdgcn_sched_barrier(0);
-  }
-}
-
 template <int WM, int WN, bool SWIGLU>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_kernel(GemmParams p) {
@@ -117,9 +103,6 @@ void gemm_kernel(GemmParams p) {
   constexpr int BN = kWaveCols * WN * 32;
   constexpr int A_TOT = BM / RPL;           // LDS-DMA loads per stage (A)
   constexpr int B_TOT = BN / RPL;           // ... (B)
-  constexpr int A_INS = (A_TOT + kWaves - 1) / kWaves;   // per wave (the last round may be partial)
-  constexpr int B_INS = (B_TOT + kWaves - 1) / kWaves;
-  constexpr int NL = A_INS + B_INS;
   constexpr int A_STAGE = BM * ROWB;        // bytes of one A stage
   constexpr int B_STAGE = BN * ROWB;
   constexpr int B_BASE = NSLOT_A * A_STAGE; // LDS: [A slots | B slots]
@@ -165,36 +148,38 @@ void gemm_kernel(GemmParams p) {
   const __amdgpu_buffer_rsrc_t rB1 = has1 ? make_rsrc(p.B1, N * p.ldb1 * 2) : rB0;
 
   // ---- global -> LDS assignment ------------------------------------------------
-  // The stage's 8-row loads are dealt round-robin to the waves: load i of this
-  // wave is q = i·kWaves + wave (skipped when q is past the tile).  Lane l
-  // writes LDS row q·8 + l/8, physical chunk l%8, fetching logical chunk
+  // The two waves on a SIMD are wave w and wave w + 4, so the waves form two
+  // groups of four, one wave per SIMD each (see the main loop).  Group 1
+  // (waves 4..7) loads A and group 0 (waves 0..3) loads B.  Loader wl =
+  // wave & 3 issues loads q = 4·i + wl of its operand: lane l writes LDS row
+  // 8q + l/8 = 32·i + my_row, physical chunk l%8, fetching logical chunk
   // swz(row, l%8), so the eight lanes of a row fetch one whole 128-byte line.
-  // Since q·8 ≡ wave·8 (mod 64), the swizzle depends on the lane and the wave
-  // only, and the A row offset is a per-lane base plus i times a scalar stride.
-  auto b_row = [&](int rt) -> int64_t {   // global row of B held by tile row rt
+  // Since 32·i leaves (row >> 1) & 7 unchanged, the swizzle depends on the
+  // lane and wl only, and every row offset is a per-lane base plus a scalar
+  // that only depends on i.
+  constexpr int A_PER = (A_TOT + 3) / 4;    // loads per loader wave per step
+  constexpr int B_PER = (B_TOT + 3) / 4;
+  const int wl = wave & 3;
+  const int wgrp = wave >> 2;
+  const int my_row = wl * RPL + lane / CPR;            // tile row of load i = 0
+  const uint32_t cx = (uint32_t)(swz(my_row, lane % CPR) * 16);
+  // A rows: m0 + 32·i + my_row
+  const uint32_t a_lane0 = (uint32_t)(my_row * p.lda0 * 2) + cx;
+  const uint32_t a_lane1 = (uint32_t)(my_row * p.lda1 * 2) + cx;
+  const uint32_t a_i0 = (uint32_t)(32 * p.lda0 * 2);
+  const uint32_t a_i1 = (uint32_t)(32 * p.lda1 * 2);
+  // B rows: tile row rt = 32·i + my_row holds global row tn·TN + my_row +
+  // piece(i), plus F for the up half of a SwiGLU tile (rows past N read 0)
+  const uint32_t b_lane0 = (uint32_t)(((int64_t)tn * TN + my_row) * p.ldb0 * 2) + cx;
+  const uint32_t b_lane1 = (uint32_t)(((int64_t)tn * TN + my_row) * p.ldb1 * 2) + cx;
+  auto b_piece = [&](int i, int64_t ldb) -> uint32_t {
     if constexpr (SWIGLU) {
-      constexpr int WNC = WN * 32, HALFC = WNC / 2;
-      const int wn_ = rt / WNC, within = rt % WNC;
-      const int half = within / HALFC;
-      const int64_t j = (int64_t)tn * TN + wn_ * HALFC + within % HALFC;
-      return half * F + j;          // up rows past N read as zeros
+      // wave column (i / 4) of 64 outputs; gate rows for i % 4 < 2, up rows after
+      return (uint32_t)((((i / 4) * 64 + (i % 2) * 32) + ((i % 4) / 2) * F) * ldb * 2);
     } else {
-      return (int64_t)tn * TN + rt; // rows past N read as zeros
+      return (uint32_t)(32 * i * ldb * 2);
     }
   };
-  const int my_row = wave * RPL + lane / CPR;          // tile row of load i = 0
-  const uint32_t cx = (uint32_t)(swz(my_row, lane % CPR) * 16);
-  const uint32_t a_base0 = (uint32_t)(my_row * p.lda0 * 2);
-  const uint32_t a_base1 = (uint32_t)(my_row * p.lda1 * 2);
-  const uint32_t a_step0 = (uint32_t)(kWaves * RPL * p.lda0 * 2);
-  const uint32_t a_step1 = (uint32_t)(kWaves * RPL * p.lda1 * 2);
-  uint32_t b_off0[B_INS], b_off1[B_INS];
-#pragma unroll
-  for (int i = 0; i < B_INS; ++i) {
-    const int64_t n = b_row(i * kWaves * RPL + my_row);
-    b_off0[i] = (uint32_t)(n * p.ldb0 * 2);
-    b_off1[i] = (uint32_t)(n * p.ldb1 * 2);
-  }
 
   // per-segment scalars, read once (selected by value inside the loop)
   const int K0 = __builtin_amdgcn_readfirstlane((int)p.K0);
@@ -203,53 +188,48 @@ void gemm_kernel(GemmParams p) {
   const int nk1 = (K1 + BK - 1) / BK;
   const int nk = nk0 + nk1;
 
-  // This wave's LDS-DMA loads of one operand for K-step kt.  Branch-free (but
-  // for the wave-uniform check of a partial last round) so the loads can be
-  // interleaved with MFMAs: chunks past the segment's K (a partial last step)
-  // and every chunk of a step past the end (kt >= nk) take an out-of-range
-  // offset and land as zeros without touching memory.
-  auto step_scalars = [&](int kt, bool& seg1, uint32_t& kb, bool& in_k) {
-    seg1 = kt >= nk0;
+  // This wave's LDS-DMA loads of its operand for K-step kt into slot `slot`.
+  // Branch-free but for the wave-uniform check of a partial last round:
+  // chunks past the segment's K (a partial last step) and every chunk of a
+  // step past the end (kt >= nk) take an out-of-range offset and land as
+  // zeros without touching memory.
+  auto issue_a = [&](int kt, int slot) {
+    const bool seg1 = kt >= nk0;
     const int kbase = (seg1 ? kt - nk0 : kt) * BK;
     const int kseg = seg1 ? K1 : K0;
     const int kleft = kt < nk ? kseg - kbase : 0;
-    const uint32_t climit = (uint32_t)(kleft >= BK ? BK * 2 : kleft * 2);  // valid bytes
-    kb = (uint32_t)(kbase * 2) + cx;
-    in_k = cx < climit;
-  };
-  auto load_a = [&](__amdgpu_buffer_rsrc_t r, uint32_t base, uint32_t stp, uint32_t kb,
-                    bool in_k, int i, int slot) {
-    const int q = i * kWaves + wave;
-    if (A_TOT % kWaves != 0 && q >= A_TOT) return;
-    const uint32_t off = in_k ? base + i * stp + kb : kOutOfRange;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        r, (lds_ptr_t)(lds + slot * A_STAGE + q * 1024), 16, off, 0, 0, 0);
-  };
-  auto load_b = [&](__amdgpu_buffer_rsrc_t r, bool seg1, uint32_t kb, bool in_k, int i,
-                    int slot) {
-    const int q = i * kWaves + wave;
-    if (B_TOT % kWaves != 0 && q >= B_TOT) return;
-    const uint32_t off = in_k ? (seg1 ? b_off1[i] : b_off0[i]) + kb : kOutOfRange;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        r, (lds_ptr_t)(lds + B_BASE + slot * B_STAGE + q * 1024), 16, off, 0, 0, 0);
-  };
-  auto issue_a = [&](int kt, int slot) {
-    bool seg1, in_k;
-    uint32_t kb;
-    step_scalars(kt, seg1, kb, in_k);
+    const uint32_t climit = (uint32_t)(kleft >= BK ? BK * 2 : kleft * 2);
+    const bool in_k = cx < climit;
     const __amdgpu_buffer_rsrc_t r = seg1 ? rA1 : rA0;
-    const uint32_t base = seg1 ? a_base1 : a_base0;
-    const uint32_t stp = seg1 ? a_step1 : a_step0;
+    const uint32_t base = (seg1 ? a_lane1 : a_lane0) + (uint32_t)(kbase * 2);
+    const uint32_t stp = seg1 ? a_i1 : a_i0;
 #pragma unroll
-    for (int i = 0; i < A_INS; ++i) load_a(r, base, stp, kb, in_k, i, slot);
+    for (int i = 0; i < A_PER; ++i) {
+      const int q = 4 * i + wl;
+      if (A_TOT % 4 != 0 && q >= A_TOT) continue;
+      const uint32_t off = in_k ? base + i * stp : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (lds_ptr_t)(lds + slot * A_STAGE + q * 1024), 16, off, 0, 0, 0);
+    }
   };
   auto issue_b = [&](int kt, int slot) {
-    bool seg1, in_k;
-    uint32_t kb;
-    step_scalars(kt, seg1, kb, in_k);
+    const bool seg1 = kt >= nk0;
+    const int kbase = (seg1 ? kt - nk0 : kt) * BK;
+    const int kseg = seg1 ? K1 : K0;
+    const int kleft = kt < nk ? kseg - kbase : 0;
+    const uint32_t climit = (uint32_t)(kleft >= BK ? BK * 2 : kleft * 2);
+    const bool in_k = cx < climit;
     const __amdgpu_buffer_rsrc_t r = seg1 ? rB1 : rB0;
+    const uint32_t base = (seg1 ? b_lane1 : b_lane0) + (uint32_t)(kbase * 2);
 #pragma unroll
-    for (int i = 0; i < B_INS; ++i) load_b(r, seg1, kb, in_k, i, slot);
+    for (int i = 0; i < B_PER; ++i) {
+      const int q = 4 * i + wl;
+      if (B_TOT % 4 != 0 && q >= B_TOT) continue;
+      const uint32_t piece = seg1 ? b_piece(i, p.ldb1) : b_piece(i, p.ldb0);
+      const uint32_t off = in_k ? base + piece : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (lds_ptr_t)(lds + B_BASE + slot * B_STAGE + q * 1024), 16, off, 0, 0, 0);
+    }
   };
 
   // ---- LDS -> MFMA fragments -----------------------------------------------------
@@ -264,42 +244,17 @@ void gemm_kernel(GemmParams p) {
     frag_lane[ks] = (uint32_t)((lane & 31) * ROWB + (((2 * ks + (lane >> 5)) ^ key_lane) * 16));
   const uint32_t a_wave = (uint32_t)(wm * WM * 32 * ROWB);
   const uint32_t b_wave = (uint32_t)(B_BASE + wn * WN * 32 * ROWB);
-  auto read_frags = [&](int sa, int sb, int ks, bf16x8 (&a)[WM], bf16x8 (&b)[WN]) {
-    const uint32_t ao = frag_lane[ks] + a_wave + sa * A_STAGE;
-    const uint32_t bo = frag_lane[ks] + b_wave + sb * B_STAGE;
+  // every fragment of one K step: KS x (WM + WN) x 16 bytes per lane
+  bf16x8 fa[KS][WM], fb[KS][WN];
+  auto read_step = [&](int sa, int sb) {
 #pragma unroll
-    for (int bi = 0; bi < WM; ++bi) a[bi] = *(const bf16x8*)(lds + ao + bi * 32 * ROWB);
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint32_t ao = frag_lane[ks] + a_wave + sa * A_STAGE;
+      const uint32_t bo = frag_lane[ks] + b_wave + sb * B_STAGE;
 #pragma unroll
-    for (int bj = 0; bj < WN; ++bj) b[bj] = *(const bf16x8*)(lds + bo + bj * 32 * ROWB);
-  };
-  // Fragment reads with loads interleaved in program order (read j, load j):
-  // the compiler cannot tell the DMA's LDS writes from the reads apart, so
-  // this order is what lets the scheduling groups pair each MFMA with one
-  // read and its share of the loads.  IS_B selects the B loads of step kt
-  // (all of them) or A loads [lo, hi) of step kt.
-  auto read_and_load = [&](int sa, int sb, int ks, bf16x8 (&a)[WM], bf16x8 (&b)[WN], int kt,
-                           int slot, auto is_b, auto lo, auto hi) {
-    constexpr bool IS_B = decltype(is_b)::value;
-    constexpr int LO = decltype(lo)::value, HI = decltype(hi)::value;
-    const uint32_t ao = frag_lane[ks] + a_wave + sa * A_STAGE;
-    const uint32_t bo = frag_lane[ks] + b_wave + sb * B_STAGE;
-    bool seg1, in_k;
-    uint32_t kb;
-    step_scalars(kt, seg1, kb, in_k);
-    const __amdgpu_buffer_rsrc_t rA = seg1 ? rA1 : rA0;
-    const __amdgpu_buffer_rsrc_t rB = seg1 ? rB1 : rB0;
-    const uint32_t a_base = seg1 ? a_base1 : a_base0;
-    const uint32_t a_step = seg1 ? a_step1 : a_step0;
-    constexpr int NLD = HI - LO;
-    constexpr int NJ = (WM + WN) > NLD ? (WM + WN) : NLD;
+      for (int bi = 0; bi < WM; ++bi) fa[ks][bi] = *(const bf16x8*)(lds + ao + bi * 32 * ROWB);
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      if (j < WM) a[j] = *(const bf16x8*)(lds + ao + j * 32 * ROWB);
-      else if (j < WM + WN) b[j - WM] = *(const bf16x8*)(lds + bo + (j - WM) * 32 * ROWB);
-      if (j < NLD) {
-        if constexpr (IS_B) load_b(rB, seg1, kb, in_k, LO + j, slot);
-        else load_a(rA, a_base, a_step, kb, in_k, LO + j, slot);
-      }
+      for (int bj = 0; bj < WN; ++bj) fb[ks][bj] = *(const bf16x8*)(lds + bo + bj * 32 * ROWB);
     }
   };
 
@@ -311,71 +266,85 @@ void gemm_kernel(GemmParams p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[bi][bj][v] = 0.0f;
 
-  auto mfmas = [&](const bf16x8 (&a)[WM], const bf16x8 (&b)[WN]) {
+  auto compute_step = [&]() {
 #pragma unroll
-    for (int bi = 0; bi < WM; ++bi)
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int bj = 0; bj < WN; ++bj)
-        acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[bj], a[bi], acc[bi][bj], 0, 0, 0);
+      for (int bi = 0; bi < WM; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < WN; ++bj)
+          acc[bi][bj] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks][bj], fa[ks][bi], acc[bi][bj], 0, 0, 0);
   };
 
-  // ---- main loop -----------------------------------------------------------------
-  // Step kt computes on A slot kt % 3 and B slot kt % 2.  Each of its KS MFMA
-  // sub-steps runs on fragments read during the previous one.  The A loads of
-  // step kt+2 go to the slot released at the previous barrier, spread over
-  // the first KS-1 sub-steps; before the last sub-step a wait + barrier makes
-  // step kt+1's slots visible and retires every read of step kt's, and the B
-  // loads of step kt+2 then refill B slot kt % 2 while the last sub-step runs
-  // and the first fragments of step kt+1 are read.  Loads thus flow through
-  // the whole step instead of in one burst per step, B loads have one step to
-  // land and A loads about one and a half; the wait leaves the A loads of
-  // this step in flight (vector-memory loads retire in order).  Each sub-step
-  // is a scheduling region of its own (sched_barrier) in which groups pin the
-  // MFMA / read / load interleave.
-  constexpr int NREAD = WM + WN;
-  constexpr int NMFMA = WM * WN;
-  constexpr int NA_W = A_TOT / kWaves;     // A loads every wave issues per step
-  static_assert(NREAD < NMFMA, "need MFMAs to hide the fragment reads");
-  static_assert(KS == 4, "A loads are spread over three sub-steps");
-  // A loads [0, A1), [A1, A2), [A2, A_INS) in sub-steps 0, 1, 2
-  constexpr int A1 = (A_INS + 2) / 3, A2 = A1 + (A_INS - A1 + 1) / 2;
-  using I0 = std::integral_constant<int, 0>;
-  using IA1 = std::integral_constant<int, A1>;
-  using IA2 = std::integral_constant<int, A2>;
-  using IAN = std::integral_constant<int, A_INS>;
-  using IBN = std::integral_constant<int, B_INS>;
-  bf16x8 fa[2][WM], fb[2][WN];
-  issue_a(0, 0);
-  issue_b(0, 0);
-  issue_a(1, 1);
-  wait_vm_lgkm0<NA_W>();
+  // ---- main loop: ping-pong ----------------------------------------------------------
+  // A K step is two phases separated by barriers.  In phase 0 of step kt,
+  // group 0 runs its WM·WN·KS MFMAs of step kt back to back from fragments
+  // already in registers, while group 1 reads every fragment of step kt from
+  // LDS and issues the A loads of step kt+2; in phase 1 the roles swap: group
+  // 1 computes step kt while group 0 issues the B loads of step kt+2 and reads
+  // the fragments of step kt+1.  Each SIMD holds one wave of each group, so
+  // its MFMA pipe always has one wave streaming MFMAs while the other does
+  // the memory work.
+  //   A of step kt sits in slot kt % 3 (read in phase 1 of kt-1 and phase 0
+  //   of kt); A(kt+2) refills slot (kt+2) % 3, free since phase 0 of kt-1,
+  //   and has until phase 1 of kt+1.  B of step kt sits in slot kt % 2; B(kt+2)
+  //   refills it in phase 1 of kt and has until phase 1 of kt+1.  Each loader
+  //   waits for its own loads before the barrier that precedes their first
+  //   reader (vector-memory loads retire in order).
+  constexpr int A_WAIT = A_TOT / 4;        // A loads a group-1 wave issues per step
+  static_assert(A_TOT % 4 == 0, "every loader issues the same number of A loads");
+  if (wgrp == 1) {
+    issue_a(0, 0);
+    issue_a(1, 1);
+    wait_vm_lgkm0<A_WAIT>();               // A(0) has landed
+  } else {
+    issue_b(0, 0);
+    issue_b(1, 1);
+    wait_vm_lgkm0<B_PER>();                // B(0) has landed (over-waits if partial)
+  }
   __builtin_amdgcn_s_barrier();
-  issue_b(1, 1);
-  read_frags(0, 0, 0, fa[0], fb[0]);
   int sa = 0;                              // A slot of step kt (kt % 3)
-  for (int kt = 0; kt < nk; ++kt) {
-    const int sb = kt & 1;
-    const int sa_next = sa == NSLOT_A - 1 ? 0 : sa + 1;
-    const int sa_load = sa_next == NSLOT_A - 1 ? 0 : sa_next + 1;   // (kt + 2) % 3
-    __builtin_amdgcn_sched_barrier(0);
-    read_and_load(sa, sb, 1, fa[1], fb[1], kt + 2, sa_load, std::false_type{}, I0{}, IA1{});
-    mfmas(fa[0], fb[0]);
-    pin_groups<NMFMA, NREAD, A1, 0>();
-    __builtin_amdgcn_sched_barrier(0);
-    read_and_load(sa, sb, 2, fa[0], fb[0], kt + 2, sa_load, std::false_type{}, IA1{}, IA2{});
-    mfmas(fa[1], fb[1]);
-    pin_groups<NMFMA, NREAD, A2 - A1, 0>();
-    __builtin_amdgcn_sched_barrier(0);
-    read_and_load(sa, sb, 3, fa[1], fb[1], kt + 2, sa_load, std::false_type{}, IA2{}, IAN{});
-    mfmas(fa[0], fb[0]);
-    pin_groups<NMFMA, NREAD, A_INS - A2, 0>();
-    wait_vm_lgkm0<NA_W>();
+  if (wgrp == 0) {
+    read_step(0, 0);
+    wait_vm_lgkm0<B_PER>();
     __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    read_and_load(sa_next, sb ^ 1, 0, fa[0], fb[0], kt + 2, sb, std::true_type{}, I0{}, IBN{});
-    mfmas(fa[1], fb[1]);
-    pin_groups<NMFMA, NREAD, B_INS, 0>();
-    sa = sa_next;
+    for (int kt = 0; kt < nk; ++kt) {
+      const int sb = kt & 1;
+      const int sa_next = sa == NSLOT_A - 1 ? 0 : sa + 1;
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(1);
+      compute_step();
+      __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vm_lgkm0<0>();                  // B(kt+1) has landed
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      issue_b(kt + 2, sb);
+      if (kt + 1 < nk) read_step(sa_next, sb ^ 1);
+      wait_vm_lgkm0<B_PER>();              // fragments in registers
+      __builtin_amdgcn_s_barrier();
+      sa = sa_next;
+    }
+  } else {
+    __builtin_amdgcn_s_barrier();
+    for (int kt = 0; kt < nk; ++kt) {
+      const int sb = kt & 1;
+      const int sa_next = sa == NSLOT_A - 1 ? 0 : sa + 1;
+      const int sa_load = sa_next == NSLOT_A - 1 ? 0 : sa_next + 1;   // (kt + 2) % 3
+      __builtin_amdgcn_sched_barrier(0);
+      read_step(sa, sb);
+      issue_a(kt + 2, sa_load);
+      wait_vm_lgkm0<A_WAIT>();             // A(kt+1) has landed; fragments in registers
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(1);
+      compute_step();
+      __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+      sa = sa_next;
+    }
   }
   // all LDS-DMA writes (including the out-of-range loads past the end) have
   // landed and every wave is done with the rings before LDS is reused below
