@@ -11,8 +11,8 @@
 // Kernel shape (one workgroup = 8 waves of 64 lanes, two per SIMD, one
 // output tile):
 //   * tile BM x BN = 256 x (64·WN); the waves form a 4 x 2 grid, each owning
-//     a (32·WM) x (32·WN) sub-tile = WM x WN blocks of
-//     v_mfma_f32_32x32x16_bf16 with fp32 accumulators (128 per lane at
+//     a (32·WM) x (32·WN) sub-tile = 2WM x 2WN blocks of
+//     v_mfma_f32_16x16x32_bf16 with fp32 accumulators (128 per lane at
 //     WM = 2, WN = 4).  The W fragment is the MFMA's first operand, so a lane
 //     ends up owning 4 consecutive output columns of one token.
 //   * operands are K-contiguous rows (X row-major, W0 in out x in layout): a
@@ -54,7 +54,6 @@ namespace fsd {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -68,7 +67,7 @@ constexpr int BK = 64;              // k per LDS stage
 constexpr int ROWB = BK * 2;        // bytes per tile row per stage: one 128-byte L2 line
 constexpr int CPR = ROWB / 16;      // 16-byte chunks per tile row (8)
 constexpr int RPL = 64 / CPR;       // tile rows per 64-lane LDS-DMA load (8)
-constexpr int KS = BK / 16;         // MFMA sub-steps per stage (4)
+constexpr int KS = BK / 32;         // MFMA k-blocks per stage (2 x 32 k)
 constexpr int NSLOT_A = 3;          // LDS slots of the A ring (loads spread over a step)
 constexpr int NSLOT_B = 2;          // LDS slots of the B ring
 constexpr int kGroupM = 4;
@@ -233,53 +232,59 @@ void gemm_kernel(GemmParams p) {
   };
 
   // ---- LDS -> MFMA fragments -----------------------------------------------------
-  // Fragment (32 rows x 16 k) of block row base rb (a multiple of 32) in
-  // sub-step ks: lane l reads row rb + l%32, logical chunk 2·ks + l/32.  For
-  // such rows the swizzle key (l>>1) & 7 does not depend on rb, so one lane
-  // offset per sub-step serves every block.
-  const int key_lane = (lane >> 1) & (CPR - 1);
+  // v_mfma_f32_16x16x32_bf16: a lane holds 8 consecutive k of one row of each
+  // operand, row l%16 and k-chunk l/16 of the 32-k block.  Fragment (16 rows x
+  // 32 k) of block row base rb (a multiple of 16) in k-block kk: lane l reads
+  // row rb + l%16, logical chunk 4·kk + l/16.  For such rows the swizzle key
+  // ((l%16) >> 1) & 7 does not depend on rb, so one lane offset per k-block
+  // serves every block.  (16x16x32 moves half the accumulator bytes per
+  // multiply-add of 32x32x16 through the register file; with random operands
+  // that lowers power enough to run the MFMAs at a measurably higher clock.)
+  constexpr int RB = WM * 2;               // 16-row blocks per wave (tokens)
+  constexpr int CB = WN * 2;               // 16-column blocks per wave (outputs)
+  const int key_lane = ((lane & 15) >> 1) & (CPR - 1);
   uint32_t frag_lane[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
-    frag_lane[ks] = (uint32_t)((lane & 31) * ROWB + (((2 * ks + (lane >> 5)) ^ key_lane) * 16));
+  for (int kk = 0; kk < KS; ++kk)
+    frag_lane[kk] = (uint32_t)((lane & 15) * ROWB + (((4 * kk + (lane >> 4)) ^ key_lane) * 16));
   const uint32_t a_wave = (uint32_t)(wm * WM * 32 * ROWB);
   const uint32_t b_wave = (uint32_t)(B_BASE + wn * WN * 32 * ROWB);
-  // every fragment of one K step: KS x (WM + WN) x 16 bytes per lane
-  bf16x8 fa[KS][WM], fb[KS][WN];
+  // every fragment of one K step: KS x (RB + CB) x 16 bytes per lane
+  bf16x8 fa[KS][RB], fb[KS][CB];
   auto read_step = [&](int sa, int sb) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const uint32_t ao = frag_lane[ks] + a_wave + sa * A_STAGE;
-      const uint32_t bo = frag_lane[ks] + b_wave + sb * B_STAGE;
+    for (int kk = 0; kk < KS; ++kk) {
+      const uint32_t ao = frag_lane[kk] + a_wave + sa * A_STAGE;
+      const uint32_t bo = frag_lane[kk] + b_wave + sb * B_STAGE;
 #pragma unroll
-      for (int bi = 0; bi < WM; ++bi) fa[ks][bi] = *(const bf16x8*)(lds + ao + bi * 32 * ROWB);
+      for (int i = 0; i < RB; ++i) fa[kk][i] = *(const bf16x8*)(lds + ao + i * 16 * ROWB);
 #pragma unroll
-      for (int bj = 0; bj < WN; ++bj) fb[ks][bj] = *(const bf16x8*)(lds + bo + bj * 32 * ROWB);
+      for (int j = 0; j < CB; ++j) fb[kk][j] = *(const bf16x8*)(lds + bo + j * 16 * ROWB);
     }
   };
 
-  f32x16 acc[WM][WN];
+  f32x4 acc[RB][CB];
 #pragma unroll
-  for (int bi = 0; bi < WM; ++bi)
+  for (int i = 0; i < RB; ++i)
 #pragma unroll
-    for (int bj = 0; bj < WN; ++bj)
+    for (int j = 0; j < CB; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[bi][bj][v] = 0.0f;
+      for (int v = 0; v < 4; ++v) acc[i][j][v] = 0.0f;
 
   auto compute_step = [&]() {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
+    for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
-      for (int bi = 0; bi < WM; ++bi)
+      for (int i = 0; i < RB; ++i)
 #pragma unroll
-        for (int bj = 0; bj < WN; ++bj)
-          acc[bi][bj] =
-              __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks][bj], fa[ks][bi], acc[bi][bj], 0, 0, 0);
+        for (int j = 0; j < CB; ++j)
+          acc[i][j] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[kk][j], fa[kk][i], acc[i][j], 0, 0, 0);
   };
 
   // ---- main loop: ping-pong ----------------------------------------------------------
   // A K step is two phases separated by barriers.  In phase 0 of step kt,
-  // group 0 runs its WM·WN·KS MFMAs of step kt back to back from fragments
+  // group 0 runs its RB·CB·KS MFMAs of step kt back to back from fragments
   // already in registers, while group 1 reads every fragment of step kt from
   // LDS and issues the A loads of step kt+2; in phase 1 the roles swap: group
   // 1 computes step kt while group 0 issues the B loads of step kt+2 and reads
@@ -352,9 +357,9 @@ void gemm_kernel(GemmParams p) {
   __builtin_amdgcn_s_barrier();
 
   // ---- epilogue ---------------------------------------------------------------
-  // Block (bi, bj) holds the transposed 32x32 output: lane l owns token
-  // bi·32 + l%32 of the wave and, in accumulator group g (elements 4g .. 4g+3),
-  // the four consecutive output columns bj·32 + 8g + 4·(l/32) + 0..3.  Each
+  // Block (i, j) holds the transposed 16x16 output: lane l owns token
+  // 16·i + l%16 of the wave and the four consecutive output columns
+  // 16·j + 4·(l/16) + 0..3 (accumulator elements 0..3).  Each
   // wave stages its (token x column) bf16 tile in its own LDS region, adding
   // the residual (loaded into the same place first) before the single
   // rounding, then writes whole row segments with 16-byte stores.  Staged rows
@@ -392,8 +397,8 @@ void gemm_kernel(GemmParams p) {
     __builtin_amdgcn_s_waitcnt(0);
   }
 
-  const int tok = lane & 31;
-  const int c4 = 4 * (lane >> 5);
+  const int tok = lane & 15;
+  const int c4 = 4 * (lane >> 4);
   auto slot = [&](int row, int oc) -> char* {
     return ow + row * PITCH + pchunk(row, oc >> 3) * 16 + (oc & 7) * 2;
   };
@@ -406,56 +411,54 @@ void gemm_kernel(GemmParams p) {
     return b;
   };
   if constexpr (SWIGLU) {
-    constexpr int HALF = WN / 2;
+    // gate columns are the wave's first CB/2 blocks, the matching up columns
+    // the last CB/2
+    constexpr int HALFB = CB / 2;
 #pragma unroll
-    for (int bj = 0; bj < HALF; ++bj)
+    for (int j = 0; j < HALFB; ++j) {
+      const int oc = j * 16 + c4;
+      const int64_t n = col0 + oc;
+      const f32x4 bg = bias4(n, n < F);
+      const f32x4 bu = bias4(F + n, n < F);
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int oc = bj * 32 + 8 * g + c4;
-        const int64_t j = col0 + oc;
-        const f32x4 bg = bias4(j, j < F);
-        const f32x4 bu = bias4(F + j, j < F);
+      for (int i = 0; i < RB; ++i) {
+        float h[4];
 #pragma unroll
-        for (int bi = 0; bi < WM; ++bi) {
-          float h[4];
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const float gt = acc[bi][bj][4 * g + k] * alpha + bg[k];
-            const float up = acc[bi][bj + HALF][4 * g + k] * alpha + bu[k];
-            h[k] = gt / (1.0f + __expf(-gt)) * up;
-          }
-          u32x2 pk;
-          pk.x = f32_to_bf16(h[0]) | (f32_to_bf16(h[1]) << 16);
-          pk.y = f32_to_bf16(h[2]) | (f32_to_bf16(h[3]) << 16);
-          *(u32x2*)slot(bi * 32 + tok, oc) = pk;
+        for (int k = 0; k < 4; ++k) {
+          const float gt = acc[i][j][k] * alpha + bg[k];
+          const float up = acc[i][j + HALFB][k] * alpha + bu[k];
+          h[k] = gt / (1.0f + __expf(-gt)) * up;
         }
+        u32x2 pk;
+        pk.x = f32_to_bf16(h[0]) | (f32_to_bf16(h[1]) << 16);
+        pk.y = f32_to_bf16(h[2]) | (f32_to_bf16(h[3]) << 16);
+        *(u32x2*)slot(i * 16 + tok, oc) = pk;
       }
+    }
   } else {
 #pragma unroll
-    for (int bj = 0; bj < WN; ++bj)
+    for (int j = 0; j < CB; ++j) {
+      const int oc = j * 16 + c4;
+      const f32x4 bn = bias4(col0 + oc, col0 + oc < Nout);
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int oc = bj * 32 + 8 * g + c4;
-        const f32x4 bn = bias4(col0 + oc, col0 + oc < Nout);
+      for (int i = 0; i < RB; ++i) {
+        char* s = slot(i * 16 + tok, oc);
+        float y[4];
 #pragma unroll
-        for (int bi = 0; bi < WM; ++bi) {
-          char* s = slot(bi * 32 + tok, oc);
-          float y[4];
-#pragma unroll
-          for (int k = 0; k < 4; ++k) y[k] = acc[bi][bj][4 * g + k] * alpha + bn[k];
-          if (p.res) {
-            const u32x2 rv = *(const u32x2*)s;
-            y[0] += __uint_as_float(rv.x << 16);
-            y[1] += __uint_as_float(rv.x & 0xffff0000u);
-            y[2] += __uint_as_float(rv.y << 16);
-            y[3] += __uint_as_float(rv.y & 0xffff0000u);
-          }
-          u32x2 pk;
-          pk.x = f32_to_bf16(y[0]) | (f32_to_bf16(y[1]) << 16);
-          pk.y = f32_to_bf16(y[2]) | (f32_to_bf16(y[3]) << 16);
-          *(u32x2*)s = pk;
+        for (int k = 0; k < 4; ++k) y[k] = acc[i][j][k] * alpha + bn[k];
+        if (p.res) {
+          const u32x2 rv = *(const u32x2*)s;
+          y[0] += __uint_as_float(rv.x << 16);
+          y[1] += __uint_as_float(rv.x & 0xffff0000u);
+          y[2] += __uint_as_float(rv.y << 16);
+          y[3] += __uint_as_float(rv.y & 0xffff0000u);
         }
+        u32x2 pk;
+        pk.x = f32_to_bf16(y[0]) | (f32_to_bf16(y[1]) << 16);
+        pk.y = f32_to_bf16(y[2]) | (f32_to_bf16(y[3]) << 16);
+        *(u32x2*)s = pk;
       }
+    }
   }
   __builtin_amdgcn_s_waitcnt(0);   // the wave's staged tile is complete (its own region)
   for (int idx = lane; idx < OROWS * OCH; idx += 64) {
