@@ -269,7 +269,27 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
     }
-    del model
+    # the same step as one HIP graph per sampler step with the Euler update fused
+    # into the head (fewer launches, v never written)
+    graphs = model.capture_steps(fused=True)
+    for _ in range(max(1, args.warmup)):
+        model.refine_graphs(graphs, u, eps)
+    torch.cuda.synchronize()
+    ga = torch.cuda.Event(enable_timing=True)
+    gb = torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(SPIN_CYCLES)
+    ga.record()
+    for _ in range(args.steps):
+        model.refine_graphs(graphs, u, eps)
+    gb.record()
+    torch.cuda.synchronize()
+    g_ms = ga.elapsed_time(gb) / args.steps
+    out["graph_fused"] = {"ms_per_step": round(g_ms, 3),
+                          "tflops": round(total_flops / (g_ms * 1e-3) / 1e12, 1),
+                          "note": "renoise + one replayed HIP graph per sampler step, "
+                                  "head and Euler fused"}
+    log(f"graph + fused head/Euler: {g_ms:.2f} ms per step")
+    del graphs, model
     torch.cuda.empty_cache()
     if not args.no_elementwise:
         log("elementwise cold-cache timing ...")

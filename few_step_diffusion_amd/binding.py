@@ -15,7 +15,7 @@ import torch
 __all__ = [
     "FsdError", "library_path", "lib", "abi_version", "lora_merge", "workspace_bytes",
     "lora_down", "lora_up", "lora_linear", "renoise", "euler_step", "token_embed",
-    "token_head", "EPI_NONE", "EPI_SWIGLU",
+    "token_head", "token_head_euler", "EPI_NONE", "EPI_SWIGLU",
 ]
 
 EPI_NONE = 0
@@ -65,6 +65,8 @@ _SIGS = {
                         _int),
     "fsd_token_head": ([_c_void_p, _i64, _c_void_p, _c_void_p, _i64, _i64, _i64, _c_void_p],
                        _int),
+    "fsd_token_head_euler": ([_c_void_p, _i64, _c_void_p, _c_void_p, _i64, _i64, _i64, _f32,
+                              _f32, _c_void_p], _int),
 }
 
 
@@ -303,3 +305,17 @@ def token_head(H, P, out=None):
     st = lib().fsd_token_head(_ptr(H), _ld(H), _ptr(P), _ptr(out), M, D, C, _stream(H))
     _check("fsd_token_head", st)
     return out
+
+
+def token_head_euler(H, P, z, sigma, sigma_next):
+    """z += (sigma_next - sigma)·(H·Pᵀ) in place: H bf16 [M, D], P bf16 [C, D], z fp32 [M, C]."""
+    _need(H, "H", torch.bfloat16)
+    _need(P, "P", torch.bfloat16)
+    M, D = H.shape
+    C = P.shape[0]
+    if z.dtype != torch.float32 or not z.is_contiguous() or tuple(z.shape[-2:]) != (M, C):
+        raise ValueError("z must be a contiguous fp32 [M, C] tensor")
+    st = lib().fsd_token_head_euler(_ptr(H), _ld(H), _ptr(P), _ptr(z), M, D, C, float(sigma),
+                                    float(sigma_next), _stream(H))
+    _check("fsd_token_head_euler", st)
+    return z

@@ -308,4 +308,20 @@ int fsd_token_head(const void* H, int64_t ldh, const void* P, float* v, int64_t 
                                    as_stream(stream)));
 }
 
+int fsd_token_head_euler(const void* H, int64_t ldh, const void* P, float* z, int64_t M,
+                         int64_t D, int64_t C, float sigma, float sigma_next, void* stream) {
+  if (M < 0 || C < 1 || C > 32 || D < 64 || D % 64) return FSD_EINVAL;
+  if (!isfinite(sigma) || !isfinite(sigma_next)) return FSD_EINVAL;
+  if (M == 0) return FSD_OK;
+  if (!H || !P || !z || ldh < D || ldh % 8) return FSD_EINVAL;
+  if (!aligned16(H) || !aligned16(P) || ((uintptr_t)z & 3u)) return FSD_EALIGN;
+  if (C * D * 2 > kMaxOffsetBytes || 128 * ldh * 2 > kMaxOffsetBytes) return FSD_EUNSUPPORTED;
+  const int64_t zb = M * C * 4;
+  if (overlap(z, zb, H, span_bytes(M, D, ldh, 2)) || overlap(z, zb, P, C * D * 2))
+    return FSD_EINVAL;
+  const float d = sigma_next - sigma;
+  return from_hip(fsd::launch_head_euler((const bf16_t*)H, ldh, (const bf16_t*)P, z, d, M, D,
+                                         (int)C, as_stream(stream)));
+}
+
 }  // extern "C"

@@ -45,5 +45,7 @@ hipError_t launch_embed(const float* z, const bf16_t* E, bf16_t* X, int64_t ldx,
                         int C, int64_t D, hipStream_t s);
 hipError_t launch_head(const bf16_t* H, int64_t ldh, const bf16_t* P, float* v, int64_t M,
                        int64_t D, int C, hipStream_t s);
+hipError_t launch_head_euler(const bf16_t* H, int64_t ldh, const bf16_t* P, float* z,
+                             float dsigma, int64_t M, int64_t D, int C, hipStream_t s);
 
 }  // namespace fsd

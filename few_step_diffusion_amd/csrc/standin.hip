@@ -22,6 +22,11 @@
 //   (one row per lane) cannot.  Each stage also holds the 32 x 64 slab of P;
 //   rows past M or C fall outside their buffers and read as zeros.  Rows are
 //   stored with their 16-byte chunks XOR-swizzled by (row >> 1) & 7.
+// head + Euler: the same kernel applies the sampler's Euler update
+//   z <- z + (sigma_next - sigma)·v ("Open-H3-Regenerate-2K: High-Resolution
+//   Video Refinement with Few-Step Diffusion" (agientry.com), section "Three
+//   steps instead of dozens", Euler update equation) to the latent in place
+//   as it produces v, so v never goes through HBM.
 #include "fsd_internal.h"
 
 namespace fsd {
@@ -165,8 +170,12 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
   __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (0 << 8) | ((n >> 4) << 14));
 }
 
+// EULER: instead of writing v, apply the Euler update z += dsigma·v in place
+// (v never leaves registers; same fp32 fma as the separate Euler kernel).
+template <bool EULER>
 __global__ __launch_bounds__(64) void head_kernel(const bf16_t* H, int64_t ldh, const bf16_t* P,
-                                                  float* v, int64_t M, int64_t D, int C) {
+                                                  float* v, int64_t M, int64_t D, int C,
+                                                  float dsigma) {
   __shared__ __attribute__((aligned(1024))) char lds[kHeadStages * kHeadStage];
   const int lane = threadIdx.x;
   const int64_t m0 = (int64_t)blockIdx.x * kHeadRows;
@@ -237,7 +246,11 @@ __global__ __launch_bounds__(64) void head_kernel(const bf16_t* H, int64_t ldh, 
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int i = 32 * bi + 8 * (e >> 2) + 4 * h + (e & 3);
-      if (i < rows_valid) v[(m0 + i) * C + j] = acc[bi][e];
+      if (i < rows_valid) {
+        float* out = v + (m0 + i) * C + j;
+        if constexpr (EULER) *out = fmaf(dsigma, acc[bi][e], *out);
+        else *out = acc[bi][e];
+      }
     }
 }
 
@@ -261,7 +274,18 @@ hipError_t launch_head(const bf16_t* H, int64_t ldh, const bf16_t* P, float* v, 
   if (M == 0) return hipSuccess;
   const int64_t blocks = (M + kHeadRows - 1) / kHeadRows;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(head_kernel, dim3((unsigned)blocks), dim3(64), 0, s, H, ldh, P, v, M, D, C);
+  hipLaunchKernelGGL(head_kernel<false>, dim3((unsigned)blocks), dim3(64), 0, s, H, ldh, P, v, M,
+                     D, C, 0.0f);
+  return hipGetLastError();
+}
+
+hipError_t launch_head_euler(const bf16_t* H, int64_t ldh, const bf16_t* P, float* z,
+                             float dsigma, int64_t M, int64_t D, int C, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  const int64_t blocks = (M + kHeadRows - 1) / kHeadRows;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(head_kernel<true>, dim3((unsigned)blocks), dim3(64), 0, s, H, ldh, P, z, M,
+                     D, C, dsigma);
   return hipGetLastError();
 }
 

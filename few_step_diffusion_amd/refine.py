@@ -82,15 +82,59 @@ class StandinRefiner:
         fsd.token_head(self.h, self.P, out=self.v)
         return self.v
 
-    def refine(self, u, eps, sigmas=SIGMAS):
+    def velocity_euler(self, sigma, sigma_next):
+        """The velocity with the Euler update fused into the head: z += (sigma_next - sigma)·v
+        without v going through HBM (bitwise equal to velocity() then euler_step)."""
+        D = self.D
+        self._mark("embed")
+        fsd.token_embed(self.z, self.E, out=self.h)
+        self._linear(0, self.h, self.qkv)
+        self._linear(1, self.qkv[:, 2 * D:3 * D], self.h, residual=self.h)
+        self._linear(2, self.h, self.g, epilogue=fsd.EPI_SWIGLU)
+        self._linear(3, self.g, self.h, residual=self.h)
+        self._mark("head_euler")
+        fsd.token_head_euler(self.h, self.P, self.z, sigma, sigma_next)
+        return self.z
+
+    def step(self, k, sigmas=SIGMAS, fused=False):
+        """Sampler step k: one velocity evaluation and one Euler update, sigmas[k] -> sigmas[k+1]."""
+        if fused:
+            self.velocity_euler(sigmas[k], sigmas[k + 1])
+        else:
+            self.velocity()
+            self._mark("euler")
+            fsd.euler_step(self.z, self.v, sigmas[k], sigmas[k + 1])
+
+    def refine(self, u, eps, sigmas=SIGMAS, fused=False):
         """Renoise u with eps at sigmas[0], then one Euler step per sigma pair."""
         self._mark("renoise")
         fsd.renoise(u, eps, sigmas[0], out=self.z)
         for k in range(len(sigmas) - 1):
-            self.velocity()
-            self._mark("euler")
-            fsd.euler_step(self.z, self.v, sigmas[k], sigmas[k + 1])
+            self.step(k, sigmas, fused)
         self._mark("end")
+        return self.z
+
+    def capture_steps(self, sigmas=SIGMAS, fused=True):
+        """One HIP graph per sampler step (the launches of step k over this refiner's fixed
+        buffers, sigmas baked in).  Replaying graph k performs step k on self.z; the renoise
+        stays an ordinary launch.  Nothing is allocated inside the captured region."""
+        self.events = None
+        graphs = []
+        side = torch.cuda.Stream(device=self.dev)
+        for k in range(len(sigmas) - 1):
+            g = torch.cuda.CUDAGraph()
+            side.wait_stream(torch.cuda.current_stream(self.dev))
+            with torch.cuda.graph(g, stream=side):
+                self.step(k, sigmas, fused)
+            torch.cuda.current_stream(self.dev).wait_stream(side)
+            graphs.append(g)
+        return graphs
+
+    def refine_graphs(self, graphs, u, eps, sigmas=SIGMAS):
+        """refine() through graphs from capture_steps()."""
+        fsd.renoise(u, eps, sigmas[0], out=self.z)
+        for g in graphs:
+            g.replay()
         return self.z
 
     def flops_per_step(self) -> dict:

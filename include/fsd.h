@@ -198,6 +198,19 @@ int fsd_token_embed(const float* z, const void* E, void* X, int64_t ldx,
 int fsd_token_head(const void* H, int64_t ldh, const void* P, float* v,
                    int64_t M, int64_t D, int64_t C, void* stream);
 
+/* fsd_token_head_euler: the head with the sampler's Euler update fused in,
+ *   z[m, c] <- z[m, c] + (sigma_next - sigma)·sum_n H[m, n]·P[c, n]
+ * ([EN] section "Three steps instead of dozens", Euler update equation,
+ * with v the head's output).  v is never written: the sums stay in
+ * registers and each z element is updated with the same fp32 fma as
+ * fsd_euler_step applies to a stored v, so the two routes agree bit for bit.
+ * H, P, C, D as for fsd_token_head; z fp32 [M, C] (row stride C), updated in
+ * place, 4-byte aligned, must not overlap H or P; sigma, sigma_next finite
+ * (else FSD_EINVAL); (sigma_next - sigma) is formed in fp32. */
+int fsd_token_head_euler(const void* H, int64_t ldh, const void* P, float* z,
+                         int64_t M, int64_t D, int64_t C, float sigma,
+                         float sigma_next, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

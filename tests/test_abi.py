@@ -135,6 +135,17 @@ def test_standin_and_merge_validation(L):
     assert L.fsd_token_head(a(1), 3072, a(2), a(3), 10, 3000, 24, None) == EINVAL
     assert L.fsd_token_head(a(1), 3072, a(2), P(BASE + 3 * 0x10000000 + 2), 10, 3072, 24,
                             None) == EALIGN
+    f = ctypes.c_float
+    assert L.fsd_token_head_euler(a(1), 3072, a(2), a(3), 10, 3072, 24, f(math.nan), f(0.8),
+                                  None) == EINVAL
+    assert L.fsd_token_head_euler(a(1), 3072, a(2), a(3), 10, 3072, 33, f(0.9), f(0.8),
+                                  None) == EINVAL
+    assert L.fsd_token_head_euler(a(1), 3072, a(2), P(BASE + 3 * 0x10000000 + 2), 10, 3072, 24,
+                                  f(0.9), f(0.8), None) == EALIGN
+    assert L.fsd_token_head_euler(a(1), 3072, a(2), P(BASE + 0x10000000 + 64), 10, 3072, 24,
+                                  f(0.9), f(0.8), None) == EINVAL        # z overlaps H
+    assert L.fsd_token_head_euler(a(1), 3072, a(2), a(3), 0, 3072, 24, f(0.9), f(0.8),
+                                  None) == OK
     arr = (P * 1)(a(1))
     rk = (ctypes.c_int64 * 1)(8)
     assert L.fsd_lora_merge(0, arr, arr, rk, None, 16, 16, a(2), a(3), None) == EINVAL

@@ -300,6 +300,51 @@ def test_head_shapes(gpu, M, C, D):
     assert_gemm(v.cpu().numpy(), oracle.head_rows(f32(H), f32(P)), "head")
 
 
+def test_head_euler_fused(gpu):
+    """z += (σ'−σ)·H·Pᵀ in one kernel: against the oracle's head then Euler step,
+    and bit for bit against the unfused route (same fp32 sums, same fma)."""
+    M, C, D = 1000, 24, 3072
+    say(f"head+Euler M={M} C={C} D={D}")
+    H = inputs.normal((M, D), 1.0, 95, dtype=torch.bfloat16)
+    _, P = inputs.standin_projections(4, C, D)
+    z0 = inputs.normal((M, C), 1.0, 96)
+    Hd, Pd = H.to(gpu), P.to(gpu)
+    z = z0.to(gpu).clone()
+    fsd.token_head_euler(Hd, Pd, z, 0.857, 0.667)
+    z_ref = oracle.euler_step(z0.numpy(), oracle.head_rows(f32(H), f32(P)), 0.857, 0.667)
+    e = metrics.token_error(z.cpu().numpy(), z_ref)
+    say(f"  token err {e:.3e}")
+    assert e <= metrics.SAMPLER_TOL
+    z2 = z0.to(gpu).clone()
+    fsd.euler_step(z2, fsd.token_head(Hd, Pd), 0.857, 0.667)
+    assert torch.equal(z, z2)
+
+
+def test_refine_fused_and_step_graphs(gpu):
+    """The refine with the head+Euler kernel equals the unfused refine bit for bit;
+    one HIP graph per sampler step, replayed with eager work and synchronisations
+    between replays, reproduces it on every replay."""
+    M = 4096 + 37
+    say(f"stand-in refine M={M}: fused and graph replays")
+    model = StandinRefiner(M, device=gpu)
+    u, eps = inputs.latent(4, tokens=M)
+    u, eps = u.to(gpu), eps.to(gpu)
+    z_ref = model.refine(u, eps).clone()
+    z_fused = model.refine(u, eps, fused=True).clone()
+    assert torch.equal(z_ref, z_fused)
+    graphs = model.capture_steps(fused=True)
+    for rep in range(3):
+        noise = torch.randn(1 << 20, device=gpu)
+        _ = (noise * 2.0).sum().item()                 # eager work + a synchronisation
+        model.z.fill_(float("nan"))
+        z_g = model.refine_graphs(graphs, u, eps).clone()
+        torch.cuda.synchronize()
+        say(f"  replay {rep}: equal {torch.equal(z_g, z_ref)}")
+        assert torch.equal(z_g, z_ref), rep
+    del model, graphs
+    torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------- full-size shapes
 def _full_linear(gpu, wid, label, K, N, layer=0, M=None, rows=384):
     M = inputs.WORKLOADS[wid].tokens if M is None else M
