@@ -21,8 +21,7 @@ import torch
 
 from . import binding as fsd
 from . import inputs
-
-SIGMAS = (0.909, 0.857, 0.667, 0.0)
+from .schedules import REFINE as SIGMAS
 
 
 class StandinRefiner:

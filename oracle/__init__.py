@@ -245,6 +245,35 @@ def head_rows(H, P):
 SIGMAS = (0.909, 0.857, 0.667, 0.0)   # [EN] "Three steps instead of dozens", schedule
 
 
+# ---- in-context (IC) sampler routes ([CW] section "三步接着放大的草稿画，八步从噪声重画")
+# The pages name an 8-step noise table with video shift 12 but print no formula.
+# Reading: the usual time-shifted flow-matching table sigma = s·t / (1 + (s-1)·t)
+# on t = 1, 7/8, ..., 0, which reproduces the pages' up4 start 0.923 at t = 1/2.
+# up3's printed start 0.835 is not a point of that table (its last-three start is
+# 0.878): the route mixes to the printed 0.835 and then takes the table's last
+# three targets.  Parity unpinned beyond the 0.923 point and the end points.
+IC_TABLE_STEPS = 8
+IC_VIDEO_SHIFT = 12.0
+IC_ROUTE_START = {"up3": (0.835, 3), "up4": (0.923, 4), "hf8": (1.0, 8)}
+REFERENCE_ROW_SIGMA = 0.001
+
+
+def shifted_table(steps=IC_TABLE_STEPS, shift=IC_VIDEO_SHIFT):
+    """sigma_k = shift·t_k / (1 + (shift - 1)·t_k), t_k = 1 - k/steps, k = 0..steps (fp64)."""
+    out = []
+    for k in range(steps + 1):
+        t = 1.0 - k / steps
+        out.append(shift * t / (1.0 + (shift - 1.0) * t))
+    return out
+
+
+def ic_route(route):
+    """sigma sequence of an IC route: the printed start, then the last n table targets."""
+    start, n = IC_ROUTE_START[route]
+    table = shifted_table()
+    return [start] + table[len(table) - n:]
+
+
 def renoise(u, eps, sigma):
     u = _f32(u)
     eps = _f32(eps)

@@ -16,7 +16,7 @@ import torch
 import few_step_diffusion_amd as fsd
 import oracle
 from oracle import metrics
-from few_step_diffusion_amd import inputs
+from few_step_diffusion_amd import inputs, schedules
 from few_step_diffusion_amd.refine import StandinRefiner
 
 pytestmark = pytest.mark.gpu
@@ -241,6 +241,36 @@ def test_sampler_full_latent(gpu, wid):
         assert e <= metrics.SAMPLER_TOL, (k, e)
     # closed form: the last step lands on x0
     assert float((hist[-1] - x0).abs().max()) <= 1e-5
+
+
+@pytest.mark.parametrize("route", ["up3", "up4", "hf8"])
+def test_ic_sampler_routes(gpu, route):
+    """The in-context routes on the 768P latent: renoise at the route's start, then
+    one Euler step per table target, every step against the oracle; the last step
+    lands on x0 (closed form, exact velocity)."""
+    sig = schedules.route(route)
+    x0, eps = inputs.latent(1)
+    say(f"IC route {route}: sigmas {[round(x, 4) for x in sig]}, {x0.numel()} elements")
+    xd, ed = x0.to(gpu), eps.to(gpu)
+    z = fsd.renoise(xd, ed, sig[0])
+    hist = [z.cpu().clone()]
+    v = ed - xd
+    for k in range(len(sig) - 1):
+        fsd.euler_step(z, v, sig[k], sig[k + 1])
+        hist.append(z.cpu().clone())
+    ref = oracle.sampler_exact_velocity(x0.numpy(), eps.numpy(), oracle.ic_route(route))
+    for k in range(len(sig)):
+        e = metrics.token_error(hist[k].numpy(), ref[k])
+        assert e <= metrics.SAMPLER_TOL, (route, k, e)
+    assert float((hist[-1] - x0).abs().max()) <= 1e-5
+
+
+def test_reference_row_renoise(gpu):
+    """The reference row of the IC routes: 99.9% draft + 0.1% noise."""
+    x0, eps = inputs.latent(1)
+    z = fsd.renoise(x0.to(gpu), eps.to(gpu), schedules.REFERENCE_ROW_SIGMA)
+    ref = oracle.renoise(x0.numpy(), eps.numpy(), oracle.REFERENCE_ROW_SIGMA)
+    assert metrics.token_error(z.cpu().numpy(), ref) <= metrics.SAMPLER_TOL
 
 
 @pytest.mark.parametrize("n", [0, 1, 3, 4, 5, 7, 1023, 4099])
