@@ -1,0 +1,112 @@
+"""fp64 reference of MXFP8 (E4M3 elements, E8M0 block scales) — TEST INFRASTRUCTURE ONLY.
+
+The pages replace the refiner's bf16 linears by "MXFP8 linear layers: FP8 GEMMs,
+re-quantized per stage" and fuse SwiGLU with a one-pass activation quantizer
+([EN] "Open-H3-Regenerate-2K: High-Resolution Video Refinement with Few-Step
+Diffusion", section "Where the 3.9x speedup comes from", inference-configuration
+table).  They give no block size, scale rule or rounding; the reading taken is the
+OCP "Microscaling Formats (MX) Specification" v1.0, MXFP8 E4M3:
+  * blocks of 32 consecutive elements along the reduction (K) dimension;
+  * shared scale X = 2^(floor(log2(amax)) - 8), 8 being E4M3's largest exponent,
+    stored as E8M0 (exponent + 127; an all-zero block gets the smallest, 2^-127);
+  * elements x/X rounded to nearest-even in E4M3 (bias 7, 3 mantissa bits,
+    subnormals down to 2^-9), magnitudes past the largest finite value 448
+    saturated to 448.
+Everything here is plain numpy float64, element by element where it matters.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+E4M3_MAX = 448.0
+E4M3_EMAX = 8          # exponent of the largest power of two below E4M3_MAX
+E4M3_EMIN = -6         # smallest normal exponent; the quantum below it is 2^-9
+MX_BLOCK = 32
+
+
+def e4m3_round(y: float) -> float:
+    """Nearest-even E4M3 value of y, saturated to +-448 (y finite)."""
+    a = abs(y)
+    if a == 0.0:
+        return 0.0 * y
+    m, ex = math.frexp(a)              # a = m·2^ex, 0.5 <= m < 1 (exact floor(log2))
+    e = max(ex - 1, E4M3_EMIN)
+    q = math.ldexp(1.0, e - 3)         # spacing of E4M3 values in [2^e, 2^(e+1))
+    k = a / q                          # exact: q is a power of two
+    r = math.floor(k)
+    frac = k - r
+    if frac > 0.5 or (frac == 0.5 and r % 2 == 1):
+        r += 1
+    v = min(r * q, E4M3_MAX)
+    return math.copysign(v, y)
+
+
+def e4m3_bits(v: float) -> int:
+    """Byte of an E4M3-representable value v (sign, 4-bit exponent with bias 7, 3-bit mantissa)."""
+    s = 0x80 if math.copysign(1.0, v) < 0 else 0
+    a = abs(v)
+    if a == 0.0:
+        return s
+    m, ex = math.frexp(a)
+    e = ex - 1
+    if e < E4M3_EMIN:                  # subnormal: a = mant·2^-9
+        mant = a / math.ldexp(1.0, E4M3_EMIN - 3)
+        assert mant == int(mant) and 0 < mant < 8
+        return s | int(mant)
+    mant = (a / math.ldexp(1.0, e) - 1.0) * 8.0
+    assert mant == int(mant) and 0 <= mant < 8 and e <= E4M3_EMAX
+    return s | ((e + 7) << 3) | int(mant)
+
+
+def e4m3_value(b: int) -> float:
+    """Value of an E4M3 byte (0x7f / 0xff are NaN and never produced here)."""
+    s = -1.0 if b & 0x80 else 1.0
+    e = (b >> 3) & 0xF
+    m = b & 7
+    if e == 0:
+        return s * math.ldexp(m / 8.0, E4M3_EMIN)
+    return s * math.ldexp(1.0 + m / 8.0, e - 7)
+
+
+def block_exponent(block) -> int:
+    """Shared exponent of one block: floor(log2(amax)) - 8, clamped to E8M0's [-127, 127]."""
+    amax = max(abs(float(x)) for x in block)
+    if amax == 0.0:
+        return -127
+    m, ex = math.frexp(amax)
+    return max(-127, min(127, (ex - 1) - E4M3_EMAX))
+
+
+def quantize_rows(X, K=None):
+    """MXFP8 of the rows of X (float values) along their length.
+
+    Returns (q, s): q uint8 [rows, Kp] E4M3 bytes, Kp = K rounded up to a
+    multiple of 128 (the padding holds zeros), and s uint8 [rows, Kp/32] E8M0
+    bytes (padded blocks get 127, i.e. a scale of 1).
+    """
+    X = np.asarray(X, dtype=np.float64)
+    rows, K0 = X.shape
+    K = K0 if K is None else K
+    Kp = (K + 127) // 128 * 128
+    q = np.zeros((rows, Kp), np.uint8)
+    s = np.full((rows, Kp // MX_BLOCK), 127, np.uint8)
+    for i in range(rows):
+        for b in range(0, K, MX_BLOCK):
+            blk = X[i, b:b + MX_BLOCK]
+            se = block_exponent(blk)
+            s[i, b // MX_BLOCK] = se + 127
+            for j, x in enumerate(blk):
+                q[i, b + j] = e4m3_bits(e4m3_round(math.ldexp(float(x), -se)))
+    return q, s
+
+
+def dequantize_rows(q, s, K):
+    """Float64 values [rows, K] of MXFP8 rows (element value times its block's scale)."""
+    rows = q.shape[0]
+    out = np.empty((rows, K), np.float64)
+    for i in range(rows):
+        for k in range(K):
+            out[i, k] = math.ldexp(e4m3_value(int(q[i, k])), int(s[i, k // MX_BLOCK]) - 127)
+    return out

@@ -1,0 +1,79 @@
+"""Pins of the MXFP8 oracle (oracle/mx.py) against the OCP MX v1.0 format facts,
+an independent library conversion (torch's float8_e4m3fn cast) and closed forms."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import mx
+
+
+def test_e4m3_code_table():
+    finite = [b for b in range(256) if (b & 0x7F) != 0x7F]
+    vals = [mx.e4m3_value(b) for b in finite]
+    assert max(vals) == 448.0 and mx.e4m3_bits(448.0) == 0x7E       # largest finite E4M3
+    assert mx.e4m3_value(0x01) == 2.0 ** -9                          # smallest subnormal
+    assert mx.e4m3_value(0x08) == 2.0 ** -6                          # smallest normal
+    assert mx.e4m3_value(0x38) == 1.0
+    for b in finite:                                                 # every code round-trips
+        v = mx.e4m3_value(b)
+        assert mx.e4m3_round(v) == v
+        if v != 0.0:
+            assert mx.e4m3_bits(v) == b
+
+
+def test_e4m3_ties_go_to_even():
+    assert mx.e4m3_round(1.0 + 1 / 16) == 1.0          # halfway between 1 and 1.125
+    assert mx.e4m3_round(1.0 + 3 / 16) == 1.25         # halfway between 1.125 and 1.25
+    assert mx.e4m3_round(-(1.0 + 3 / 16)) == -1.25
+    assert mx.e4m3_round(2.0 ** -10) == 0.0            # half the smallest subnormal -> 0 (even)
+    assert mx.e4m3_round(3 * 2.0 ** -10) == 2.0 ** -8  # 1.5 quanta -> 2 quanta
+
+
+def test_e4m3_saturates():
+    assert mx.e4m3_round(460.0) == 448.0
+    assert mx.e4m3_round(1e6) == 448.0
+    assert mx.e4m3_round(-500.0) == -448.0
+
+
+def test_e4m3_matches_torch_cast_in_range():
+    """torch's float8_e4m3fn cast (an independent implementation, nearest-even) agrees on
+    every value inside the finite range, including subnormals and ties."""
+    rng = np.random.default_rng(7)
+    ys = np.concatenate([rng.standard_normal(4000) * 40.0,
+                         rng.standard_normal(2000) * 2.0 ** -7,
+                         np.array([mx.e4m3_value(b) for b in range(0, 0x7E)]) * (1 + 1 / 16)])
+    ys = ys[np.abs(ys) < 448.0]
+    t = torch.from_numpy(ys).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    o = np.array([mx.e4m3_round(float(y)) for y in ys])
+    assert np.array_equal(t, o)
+
+
+def test_block_exponent_and_scaling():
+    assert mx.block_exponent([1.0] + [0.0] * 31) == -8          # amax 1 -> X = 2^-8, 1/X = 256
+    assert mx.block_exponent([0.0] * 32) == -127
+    assert mx.block_exponent([3.0, -300.0]) == math.floor(math.log2(300.0)) - 8
+    q, s = mx.quantize_rows(np.array([[1.0] + [0.5] * 31]))
+    assert q.shape == (1, 128) and s.shape == (1, 4)
+    assert s[0, 0] == 127 - 8 and s[0, 1] == 127                 # padded blocks: scale 1
+    assert mx.e4m3_value(int(q[0, 0])) == 256.0 and mx.e4m3_value(int(q[0, 1])) == 128.0
+    assert np.all(q[0, 32:] == 0)
+
+
+def test_quantization_error_bound():
+    """Per element: half a unit in the last place of E4M3 (2^-4 relative) for normal
+    results, the subnormal quantum below them, and the 448..512 clip of the top binade."""
+    rng = np.random.default_rng(11)
+    X = rng.standard_normal((6, 96)) * np.exp(rng.standard_normal((6, 1)) * 3)
+    q, s = mx.quantize_rows(X)
+    D = mx.dequantize_rows(q, s, 96)
+    for i in range(6):
+        for k in range(96):
+            X_scale = 2.0 ** (int(s[i, k // 32]) - 127)
+            y = X[i, k] / X_scale
+            if abs(y) > 448.0:
+                bound = (abs(y) - 448.0) * X_scale
+            else:
+                bound = max(abs(X[i, k]) * 2.0 ** -4, 2.0 ** -10 * X_scale)
+            assert abs(D[i, k] - X[i, k]) <= bound * (1 + 1e-12), (i, k)
