@@ -15,7 +15,7 @@ import torch
 __all__ = [
     "FsdError", "library_path", "lib", "abi_version", "lora_merge", "workspace_bytes",
     "lora_down", "lora_up", "lora_linear", "renoise", "euler_step", "token_embed",
-    "token_head", "token_head_euler", "EPI_NONE", "EPI_SWIGLU",
+    "token_head", "token_head_euler", "mx_quantize", "mx_padded_k", "EPI_NONE", "EPI_SWIGLU",
 ]
 
 EPI_NONE = 0
@@ -67,6 +67,9 @@ _SIGS = {
                        _int),
     "fsd_token_head_euler": ([_c_void_p, _i64, _c_void_p, _c_void_p, _i64, _i64, _i64, _f32,
                               _f32, _c_void_p], _int),
+    "fsd_mx_scale_bytes": ([_i64, _i64], ctypes.c_size_t),
+    "fsd_mx_quantize": ([_c_void_p, _i64, _i64, _i64, _c_void_p, _i64, _c_void_p, _c_void_p],
+                        _int),
 }
 
 
@@ -319,3 +322,22 @@ def token_head_euler(H, P, z, sigma, sigma_next):
                                     float(sigma_next), _stream(H))
     _check("fsd_token_head_euler", st)
     return z
+
+
+def mx_padded_k(K: int) -> int:
+    """Row length of MXFP8 elements: K rounded up to one GEMM K step (128)."""
+    return (K + 127) // 128 * 128
+
+
+def mx_quantize(X, Q=None, S=None):
+    """MXFP8 of X bf16 [M, K] (K % 32 == 0): returns (Q uint8 [M, Kp], S uint8 scales)."""
+    _need(X, "X", torch.bfloat16)
+    M, K = X.shape
+    Kp = mx_padded_k(K)
+    if Q is None:
+        Q = torch.empty((M, Kp), dtype=torch.uint8, device=X.device)
+    if S is None:
+        S = torch.empty(int(lib().fsd_mx_scale_bytes(M, K)), dtype=torch.uint8, device=X.device)
+    st = lib().fsd_mx_quantize(_ptr(X), _ld(X), M, K, _ptr(Q), Q.stride(0), _ptr(S), _stream(X))
+    _check("fsd_mx_quantize", st)
+    return Q, S

@@ -324,4 +324,24 @@ int fsd_token_head_euler(const void* H, int64_t ldh, const void* P, float* z, in
                                          (int)C, as_stream(stream)));
 }
 
+size_t fsd_mx_scale_bytes(int64_t M, int64_t K) {
+  if (M < 0 || K < 0) return 0;
+  return (size_t)(((K + 127) / 128) * ((M + 255) / 256 * 256) * 4);
+}
+
+int fsd_mx_quantize(const void* X, int64_t ldx, int64_t M, int64_t K, void* Q, int64_t ldq,
+                    void* S, void* stream) {
+  if (M < 0 || K < 32 || K % 32) return FSD_EINVAL;
+  if (M == 0) return FSD_OK;
+  const int64_t Kp = (K + 127) / 128 * 128;
+  if (!X || !Q || !S || ldx < K || ldx % 8 || ldq < Kp || ldq % 16) return FSD_EINVAL;
+  if (!aligned16(X) || !aligned16(Q)) return FSD_EALIGN;
+  const int64_t qb = span_bytes(M, Kp, ldq, 1);
+  const int64_t sb = (int64_t)fsd_mx_scale_bytes(M, K);
+  const int64_t xb = span_bytes(M, K, ldx, 2);
+  if (overlap(Q, qb, X, xb) || overlap(S, sb, X, xb) || overlap(S, sb, Q, qb)) return FSD_EINVAL;
+  return from_hip(fsd::launch_mx_quantize((const bf16_t*)X, ldx, M, K, (uint8_t*)Q, ldq,
+                                          (uint8_t*)S, as_stream(stream)));
+}
+
 }  // extern "C"

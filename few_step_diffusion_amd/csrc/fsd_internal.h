@@ -47,5 +47,7 @@ hipError_t launch_head(const bf16_t* H, int64_t ldh, const bf16_t* P, float* v, 
                        int64_t D, int C, hipStream_t s);
 hipError_t launch_head_euler(const bf16_t* H, int64_t ldh, const bf16_t* P, float* z,
                              float dsigma, int64_t M, int64_t D, int C, hipStream_t s);
+hipError_t launch_mx_quantize(const bf16_t* X, int64_t ldx, int64_t M, int64_t K, uint8_t* Q,
+                              int64_t ldq, uint8_t* S, hipStream_t s);
 
 }  // namespace fsd

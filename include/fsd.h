@@ -211,6 +211,29 @@ int fsd_token_head_euler(const void* H, int64_t ldh, const void* P, float* z,
                          int64_t M, int64_t D, int64_t C, float sigma,
                          float sigma_next, void* stream);
 
+/* ------------------------------------------------------------------------ *
+ * MXFP8 linears (NEXT step of the pages' own optimisation)                   *
+ * ------------------------------------------------------------------------ *
+ * The pages run the linears as MXFP8 FP8 GEMMs re-quantized per stage, with
+ * SwiGLU fused into a one-pass activation quantizer ([EN] section "Where the
+ * 3.9x speedup comes from", inference-configuration table).  Format (OCP MX
+ * v1.0, the pages fix none of it): blocks of 32 elements along K, shared
+ * E8M0 scale 2^(floor(log2 amax) - 8), E4M3 elements rounded to nearest-even
+ * and saturated at 448.
+ *
+ * Layout: elements Q as bytes [M, Kp], Kp = K rounded up to 128, row stride
+ * ldq >= Kp (multiple of 16), columns K..Kp-1 zero; scales S as
+ * [Kp/128][Mp][4] bytes with Mp = M rounded up to 256 (entry (t, m, b) is the
+ * scale of row m, elements 128t + 32b .. +31; padding entries are 127).
+ *
+ * fsd_mx_scale_bytes: size of S for M rows of K elements.
+ * fsd_mx_quantize: X bf16 [M, K] (row stride ldx >= K, multiple of 8, 16-byte
+ *   aligned), K a multiple of 32 -> Q, S as above.  Q 16-byte aligned; Q and S
+ *   must not overlap X or each other.  Errors: FSD_EINVAL, FSD_EALIGN. */
+size_t fsd_mx_scale_bytes(int64_t M, int64_t K);
+int fsd_mx_quantize(const void* X, int64_t ldx, int64_t M, int64_t K, void* Q,
+                    int64_t ldq, void* S, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
