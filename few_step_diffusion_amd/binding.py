@@ -10,12 +10,15 @@ from __future__ import annotations
 import ctypes
 import os
 
+import numpy as np
 import torch
 
 __all__ = [
     "FsdError", "library_path", "lib", "abi_version", "lora_merge", "workspace_bytes",
     "lora_down", "lora_up", "lora_linear", "renoise", "euler_step", "token_embed",
-    "token_head", "token_head_euler", "mx_quantize", "mx_padded_k", "EPI_NONE", "EPI_SWIGLU",
+    "token_head", "token_head_euler", "mx_quantize", "mx_padded_k", "mx_scale_bytes",
+    "mx_scale_offsets", "mx_pack_scales", "mx_unpack_scales", "mx_lora_down", "mx_lora_up",
+    "EPI_NONE", "EPI_SWIGLU",
 ]
 
 EPI_NONE = 0
@@ -70,6 +73,11 @@ _SIGS = {
     "fsd_mx_scale_bytes": ([_i64, _i64], ctypes.c_size_t),
     "fsd_mx_quantize": ([_c_void_p, _i64, _i64, _i64, _c_void_p, _i64, _c_void_p, _c_void_p],
                         _int),
+    "fsd_mx_lora_down": ([_c_void_p, _i64, _c_void_p, _c_void_p, _c_void_p, _f32, _c_void_p,
+                          _i64, _i64, _i64, _i64, _c_void_p], _int),
+    "fsd_mx_lora_up": ([_c_void_p, _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64,
+                        _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _c_void_p,
+                        _i64, _i64, _i64, _i64, _i64, _int, _c_void_p], _int),
 }
 
 
@@ -341,3 +349,108 @@ def mx_quantize(X, Q=None, S=None):
     st = lib().fsd_mx_quantize(_ptr(X), _ld(X), M, K, _ptr(Q), Q.stride(0), _ptr(S), _stream(X))
     _check("fsd_mx_quantize", st)
     return Q, S
+
+
+def mx_scale_bytes(M: int, K: int) -> int:
+    """Bytes of the scale array of M rows of K elements."""
+    return int(lib().fsd_mx_scale_bytes(M, K))
+
+
+def mx_scale_offsets(M: int, K: int) -> np.ndarray:
+    """Byte offset in the scale array of the scale of (row m, 32-element block b).
+
+    int64 [M, Kp/32].  Scales are grouped by 128-element step t and 64-row group
+    g; within a group, byte i of 32-bit word 16·b + r is row 64g + 16i + r.
+    """
+    Kp = mx_padded_k(K)
+    Mp = (M + 255) // 256 * 256
+    m = np.arange(M, dtype=np.int64)[:, None]
+    b = np.arange(Kp // 32, dtype=np.int64)[None, :]
+    return (((b >> 2) * (Mp >> 6) + (m >> 6)) * 64 + (b & 3) * 16 + (m & 15)) * 4 + ((m >> 4) & 3)
+
+
+def mx_pack_scales(s_rows, K: int) -> torch.Tensor:
+    """Host uint8 scales [M, Kp/32] (row-major, one byte per block) -> the scale
+    array layout (CPU uint8 tensor; padding rows hold 127)."""
+    s_rows = np.asarray(s_rows, dtype=np.uint8)
+    M = s_rows.shape[0]
+    out = np.full(max(mx_scale_bytes(M, K), 0), 127, np.uint8)
+    out[mx_scale_offsets(M, K)] = s_rows
+    return torch.from_numpy(out)
+
+
+def mx_unpack_scales(S, M: int, K: int) -> np.ndarray:
+    """Scale array (any device) -> host uint8 [M, Kp/32], one byte per (row, block)."""
+    flat = S.detach().cpu().numpy() if isinstance(S, torch.Tensor) else np.asarray(S)
+    return flat[mx_scale_offsets(M, K)]
+
+
+def _need_scales(S, name, rows, Kp):
+    if not isinstance(S, torch.Tensor) or S.device.type != "cuda" or S.dtype != torch.uint8:
+        raise TypeError(f"{name} must be a uint8 GPU tensor")
+    if not S.is_contiguous() or S.numel() < mx_scale_bytes(rows, Kp):
+        raise ValueError(f"{name} must hold the scales of {rows} rows of {Kp} elements")
+
+
+def mx_lora_down(Xq, Xs, Aq, As, scale=1.0, T=None):
+    """Phase A on MXFP8 operands: T = bf16(scale · deq(Xq)·deq(Aq)ᵀ).
+
+    Xq uint8 [M, Kp] with scales Xs; Aq uint8 [r, Kp] (contiguous) with scales As.
+    """
+    _need(Xq, "Xq", torch.uint8)
+    _need(Aq, "Aq", torch.uint8)
+    M, Kp = Xq.shape
+    r = Aq.shape[0]
+    if Aq.shape[1] != Kp or not Aq.is_contiguous():
+        raise ValueError("Aq must be a contiguous [r, Kp] tensor with Xq's Kp")
+    _need_scales(Xs, "Xs", M, Kp)
+    _need_scales(As, "As", r, Kp)
+    if T is None:
+        T = torch.empty((M, r), dtype=torch.bfloat16, device=Xq.device)
+    _need(T, "T", torch.bfloat16)
+    st = lib().fsd_mx_lora_down(_ptr(Xq), _ld(Xq), _ptr(Xs), _ptr(Aq), _ptr(As), float(scale),
+                                _ptr(T), _ld(T), M, Kp, r, _stream(Xq))
+    _check("fsd_mx_lora_down", st)
+    return T
+
+
+def mx_lora_up(Xq, Xs, W0q, W0s, Tq=None, Ts=None, Bq=None, Bs=None, bias=None,
+               residual=None, epilogue=EPI_NONE, out=None):
+    """Phase B on MXFP8 operands: Y = epi([Xq | Tq]·[W0q | Bq]ᵀ (dequantized) + bias) (+ residual).
+
+    Xq uint8 [M, Kp]; W0q uint8 [N, Kp] (contiguous); Tq uint8 [M, rp] and Bq uint8
+    [N, rp] (contiguous), rp a multiple of 128, or None for no LoRA term; Xs, W0s,
+    Ts, Bs their scale arrays.
+    """
+    epilogue = _epi(epilogue)
+    _need(Xq, "Xq", torch.uint8)
+    _need(W0q, "W0q", torch.uint8)
+    M, Kp = Xq.shape
+    N = W0q.shape[0]
+    if W0q.shape[1] != Kp or not W0q.is_contiguous():
+        raise ValueError("W0q must be a contiguous [N, Kp] tensor with Xq's Kp")
+    _need_scales(Xs, "Xs", M, Kp)
+    _need_scales(W0s, "W0s", N, Kp)
+    rp = 0 if Bq is None else Bq.shape[1]
+    if rp:
+        _need(Tq, "Tq", torch.uint8)
+        _need(Bq, "Bq", torch.uint8)
+        if Tq.shape != (M, rp) or Bq.shape[0] != N or not Bq.is_contiguous():
+            raise ValueError("Tq must be [M, rp] and Bq a contiguous [N, rp]")
+        _need_scales(Ts, "Ts", M, rp)
+        _need_scales(Bs, "Bs", N, rp)
+    if bias is not None:
+        _need(bias, "bias", torch.float32, dims=1)
+    if residual is not None:
+        _need(residual, "residual", torch.bfloat16)
+    if out is None:
+        out = torch.empty((M, _out_cols(N, epilogue)), dtype=torch.bfloat16, device=Xq.device)
+    _need(out, "out", torch.bfloat16)
+    st = lib().fsd_mx_lora_up(_ptr(Xq), _ld(Xq), _ptr(Xs), _ptr(W0q), _ptr(W0s),
+                              _ptr(Tq) if rp else None, _ld(Tq) if rp else 0,
+                              _ptr(Ts) if rp else None, _ptr(Bq) if rp else None,
+                              _ptr(Bs) if rp else None, _ptr(bias), _ptr(residual),
+                              _ld(residual) if residual is not None else 0, _ptr(out), _ld(out),
+                              M, N, Kp, rp, epilogue, _stream(Xq))
+    _check("fsd_mx_lora_up", st)
+    return out

@@ -128,6 +128,34 @@ int validate_down(const void* X, int64_t ldx, const void* A, float scale, const 
   return FSD_OK;
 }
 
+// ---- MXFP8 operands --------------------------------------------------------
+inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+// Scale bytes of `rows` rows over Kp (a multiple of 128) elements.
+inline int64_t mx_scale_span(int64_t rows, int64_t Kp) {
+  return (Kp / 128) * round_up(rows, kTileM) * 4;
+}
+
+// One MX operand: codes [rows, Kp] with row stride ld bytes plus its scales.
+// A weight operand (whole_matrix) is addressed from its base; an activation
+// operand from each 256-row tile.
+int validate_mx_operand(const void* q, int64_t ld, const void* s, int64_t rows, int64_t Kp,
+                        bool whole_matrix) {
+  if (!q || !s || ld < Kp || ld % 16) return FSD_EINVAL;
+  if (!aligned16(q) || ((uintptr_t)s & 3u)) return FSD_EALIGN;
+  const int64_t span = whole_matrix ? (rows + kTileM) * ld : kTileM * ld;
+  if (span > kMaxOffsetBytes || mx_scale_span(rows, Kp) > kMaxOffsetBytes)
+    return FSD_EUNSUPPORTED;
+  return FSD_OK;
+}
+
+// Output Y (bytes yb) must not overlap an operand's codes or scales.
+inline bool mx_overlaps(const void* Y, int64_t yb, const void* q, int64_t ld, const void* s,
+                        int64_t rows, int64_t Kp) {
+  return overlap(Y, yb, q, span_bytes(rows, Kp, ld, 1)) ||
+         overlap(Y, yb, s, mx_scale_span(rows, Kp));
+}
+
 }  // namespace
 
 extern "C" {
@@ -335,13 +363,88 @@ int fsd_mx_quantize(const void* X, int64_t ldx, int64_t M, int64_t K, void* Q, i
   if (M == 0) return FSD_OK;
   const int64_t Kp = (K + 127) / 128 * 128;
   if (!X || !Q || !S || ldx < K || ldx % 8 || ldq < Kp || ldq % 16) return FSD_EINVAL;
-  if (!aligned16(X) || !aligned16(Q)) return FSD_EALIGN;
+  if (!aligned16(X) || !aligned16(Q) || ((uintptr_t)S & 3u)) return FSD_EALIGN;
   const int64_t qb = span_bytes(M, Kp, ldq, 1);
   const int64_t sb = (int64_t)fsd_mx_scale_bytes(M, K);
   const int64_t xb = span_bytes(M, K, ldx, 2);
   if (overlap(Q, qb, X, xb) || overlap(S, sb, X, xb) || overlap(S, sb, Q, qb)) return FSD_EINVAL;
   return from_hip(fsd::launch_mx_quantize((const bf16_t*)X, ldx, M, K, (uint8_t*)Q, ldq,
                                           (uint8_t*)S, as_stream(stream)));
+}
+
+int fsd_mx_lora_down(const void* Xq, int64_t ldxq, const void* Xs, const void* Aq,
+                     const void* As, float scale, void* T, int64_t ldt, int64_t M, int64_t K,
+                     int64_t r, void* stream) {
+  if (M < 0 || K < 32 || K % 32 || r < 8 || r % 8 || !isfinite(scale)) return FSD_EINVAL;
+  if (!T || ldt < r || ldt % 8) return FSD_EINVAL;
+  if (!aligned16(T)) return FSD_EALIGN;
+  const int64_t Kp = round_up(K, 128);
+  int st = validate_mx_operand(Xq, ldxq, Xs, M, Kp, false);
+  if (st == FSD_OK) st = validate_mx_operand(Aq, Kp, As, r, Kp, true);
+  if (st != FSD_OK) return st;
+  const int64_t tb = span_bytes(M, r, ldt, 2);
+  if (mx_overlaps(T, tb, Xq, ldxq, Xs, M, Kp) || mx_overlaps(T, tb, Aq, Kp, As, r, Kp))
+    return FSD_EINVAL;
+  if (M == 0) return FSD_OK;
+  fsd::GemmParams p;
+  memset(&p, 0, sizeof(p));
+  p.A0 = Xq; p.lda0 = ldxq; p.sA0 = (const uint8_t*)Xs;
+  p.B0 = Aq; p.ldb0 = Kp;   p.sB0 = (const uint8_t*)As;
+  p.M = M; p.N = r; p.K0 = Kp; p.K1 = 0;
+  p.sMp = round_up(M, kTileM); p.sNp = round_up(r, kTileM);
+  p.alpha = scale;
+  p.Y = (bf16_t*)T; p.ldy = ldt;
+  return from_hip(fsd::launch_gemm(fsd::GEMM_MX_DOWN, p, as_stream(stream)));
+}
+
+int fsd_mx_lora_up(const void* Xq, int64_t ldxq, const void* Xs, const void* W0q,
+                   const void* W0s, const void* Tq, int64_t ldtq, const void* Ts,
+                   const void* Bq, const void* Bs, const float* bias, const void* residual,
+                   int64_t ldr, void* Y, int64_t ldy, int64_t M, int64_t N, int64_t K,
+                   int64_t r, int epilogue, void* stream) {
+  if (M < 0 || K < 32 || K % 32 || N < 8 || N % 8 || r < 0 || r % 32) return FSD_EINVAL;
+  if (epilogue != FSD_EPI_NONE && epilogue != FSD_EPI_SWIGLU) return FSD_EINVAL;
+  const bool swiglu = epilogue == FSD_EPI_SWIGLU;
+  if (swiglu && N % 16) return FSD_EINVAL;
+  if (swiglu && (N % 128 || residual)) return FSD_EUNSUPPORTED;
+  const int64_t nout = swiglu ? N / 2 : N;
+  if (!Y || ldy < nout || ldy % 8) return FSD_EINVAL;
+  if (residual && (ldr < nout || ldr % 8)) return FSD_EINVAL;
+  if (!aligned16(Y) || (residual && !aligned16(residual))) return FSD_EALIGN;
+  if (bias && ((uintptr_t)bias & 3u)) return FSD_EALIGN;
+  const int64_t Kp = round_up(K, 128), rp = round_up(r, 128);
+  int st = validate_mx_operand(Xq, ldxq, Xs, M, Kp, false);
+  if (st == FSD_OK) st = validate_mx_operand(W0q, Kp, W0s, N, Kp, true);
+  if (st == FSD_OK && r > 0) st = validate_mx_operand(Tq, ldtq, Ts, M, rp, false);
+  if (st == FSD_OK && r > 0) st = validate_mx_operand(Bq, rp, Bs, N, rp, true);
+  if (st != FSD_OK) return st;
+  const int64_t yb = span_bytes(M, nout, ldy, 2);
+  if (mx_overlaps(Y, yb, Xq, ldxq, Xs, M, Kp) || mx_overlaps(Y, yb, W0q, Kp, W0s, N, Kp) ||
+      overlap(Y, yb, bias, bias ? N * 4 : 0))
+    return FSD_EINVAL;
+  if (r > 0 && (mx_overlaps(Y, yb, Tq, ldtq, Ts, M, rp) || mx_overlaps(Y, yb, Bq, rp, Bs, N, rp)))
+    return FSD_EINVAL;
+  if (residual) {
+    const bool same = residual == Y && ldr == ldy;
+    if (!same && overlap(Y, yb, residual, span_bytes(M, nout, ldr, 2))) return FSD_EINVAL;
+  }
+  if (M == 0) return FSD_OK;
+  fsd::GemmParams p;
+  memset(&p, 0, sizeof(p));
+  p.A0 = Xq; p.lda0 = ldxq; p.sA0 = (const uint8_t*)Xs;
+  p.B0 = W0q; p.ldb0 = Kp;  p.sB0 = (const uint8_t*)W0s;
+  if (r > 0) {
+    p.A1 = Tq; p.lda1 = ldtq; p.sA1 = (const uint8_t*)Ts;
+    p.B1 = Bq; p.ldb1 = rp;   p.sB1 = (const uint8_t*)Bs;
+  }
+  p.M = M; p.N = N; p.K0 = Kp; p.K1 = rp;
+  p.sMp = round_up(M, kTileM); p.sNp = round_up(N, kTileM);
+  p.alpha = 1.0f;
+  p.bias = bias;
+  p.res = (const bf16_t*)residual; p.ldr = ldr;
+  p.Y = (bf16_t*)Y; p.ldy = ldy;
+  const fsd::GemmKind kind = swiglu ? fsd::GEMM_MX_UP_SWIGLU : fsd::GEMM_MX_UP;
+  return from_hip(fsd::launch_gemm(kind, p, as_stream(stream)));
 }
 
 }  // extern "C"

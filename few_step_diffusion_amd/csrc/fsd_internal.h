@@ -14,22 +14,32 @@ typedef uint16_t bf16_t;   // bfloat16 storage word
 // (A1, B1); K1 == 0 disables segment 1.  A* are [M, K*] with row stride lda*,
 // B* are [N, K*] with row stride ldb*.  With SwiGLU the N accumulator columns
 // are [gate | up] halves and Y has N/2 columns.
+// For the MXFP8 kinds the operands are E4M3 bytes (lengths K0, K1 and strides
+// in elements = bytes, K a multiple of 128) and sA*, sB* their E8M0 scales in
+// the layout mx.hip writes (per 128-k step and 64-row group, 64 dwords), for
+// sMp (A) and sNp (B) rows: the operand's row count rounded up to 256.
 struct GemmParams {
-  const bf16_t* A0; int64_t lda0;
-  const bf16_t* B0; int64_t ldb0;
-  const bf16_t* A1; int64_t lda1;
-  const bf16_t* B1; int64_t ldb1;
+  const void* A0; int64_t lda0;
+  const void* B0; int64_t ldb0;
+  const void* A1; int64_t lda1;
+  const void* B1; int64_t ldb1;
   int64_t M, N, K0, K1;
   float alpha;
   const float* bias;
   const bf16_t* res; int64_t ldr;
   bf16_t* Y; int64_t ldy;
+  const uint8_t* sA0; const uint8_t* sB0;
+  const uint8_t* sA1; const uint8_t* sB1;
+  int64_t sMp, sNp;
 };
 
 enum GemmKind {
-  GEMM_DOWN = 0,     // phase A: T = bf16(alpha · X·Aᵀ), N = rank (tile 256 x 192)
-  GEMM_UP = 1,       // phase B, plain / bias / residual epilogue (tile 256 x 256)
-  GEMM_UP_SWIGLU = 2 // phase B with the SwiGLU epilogue
+  GEMM_DOWN = 0,        // phase A: T = bf16(alpha · X·Aᵀ), N = rank (tile 256 x 192)
+  GEMM_UP = 1,          // phase B, plain / bias / residual epilogue (tile 256 x 256)
+  GEMM_UP_SWIGLU = 2,   // phase B with the SwiGLU epilogue
+  GEMM_MX_DOWN = 3,     // the same three with MXFP8 operands
+  GEMM_MX_UP = 4,
+  GEMM_MX_UP_SWIGLU = 5
 };
 
 hipError_t launch_gemm(GemmKind kind, const GemmParams& p, hipStream_t s);

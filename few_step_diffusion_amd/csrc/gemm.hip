@@ -46,6 +46,7 @@
 //     evict the X and W lines that other tiles are re-reading from L2 and the
 //     Infinity Cache.
 #include <type_traits>
+#include <utility>
 
 #include "fsd_internal.h"
 
@@ -57,6 +58,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 constexpr int kWaveRows = 4;        // waves along M
@@ -95,9 +97,23 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
   __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (0 << 8) | ((n >> 4) << 14));
 }
 
-template <int WM, int WN, bool SWIGLU>
+template <typename Fn, int... Is>
+__device__ __forceinline__ void static_for_seq(Fn&& fn, std::integer_sequence<int, Is...>) {
+  (fn(std::integral_constant<int, Is>{}), ...);
+}
+// fn(std::integral_constant<int, 0>) ... fn(std::integral_constant<int, N - 1>)
+template <int N, typename Fn>
+__device__ __forceinline__ void static_for(Fn&& fn) {
+  static_for_seq(fn, std::make_integer_sequence<int, N>{});
+}
+
+// MX: E4M3 operands with E8M0 block scales (v_mfma_scale_f32_16x16x128_f8f6f4):
+// a K step is 128 elements, still one 128-byte line per tile row.
+template <int WM, int WN, bool SWIGLU, bool MX>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_kernel(GemmParams p) {
+  constexpr int ESZ = MX ? 1 : 2;           // bytes per element
+  constexpr int KSTEP = ROWB / ESZ;         // elements per K step
   constexpr int BM = kWaveRows * WM * 32;
   constexpr int BN = kWaveCols * WN * 32;
   constexpr int A_TOT = BM / RPL;           // LDS-DMA loads per stage (A)
@@ -139,12 +155,14 @@ void gemm_kernel(GemmParams p) {
   const int wm = wave / kWaveCols, wn = wave % kWaveCols;
 
   // ---- buffer resources ------------------------------------------------------
-  const __amdgpu_buffer_rsrc_t rA0 = make_rsrc(p.A0 + m0 * p.lda0, rows_valid * p.lda0 * 2);
-  const __amdgpu_buffer_rsrc_t rB0 = make_rsrc(p.B0, N * p.ldb0 * 2);
+  const char* A0 = (const char*)p.A0;
+  const char* A1 = (const char*)p.A1;
+  const __amdgpu_buffer_rsrc_t rA0 = make_rsrc(A0 + m0 * p.lda0 * ESZ, rows_valid * p.lda0 * ESZ);
+  const __amdgpu_buffer_rsrc_t rB0 = make_rsrc(p.B0, N * p.ldb0 * ESZ);
   const bool has1 = p.K1 > 0;
   const __amdgpu_buffer_rsrc_t rA1 =
-      has1 ? make_rsrc(p.A1 + m0 * p.lda1, rows_valid * p.lda1 * 2) : rA0;
-  const __amdgpu_buffer_rsrc_t rB1 = has1 ? make_rsrc(p.B1, N * p.ldb1 * 2) : rB0;
+      has1 ? make_rsrc(A1 + m0 * p.lda1 * ESZ, rows_valid * p.lda1 * ESZ) : rA0;
+  const __amdgpu_buffer_rsrc_t rB1 = has1 ? make_rsrc(p.B1, N * p.ldb1 * ESZ) : rB0;
 
   // ---- global -> LDS assignment ------------------------------------------------
   // The two waves on a SIMD are wave w and wave w + 4, so the waves form two
@@ -163,28 +181,28 @@ void gemm_kernel(GemmParams p) {
   const int my_row = wl * RPL + lane / CPR;            // tile row of load i = 0
   const uint32_t cx = (uint32_t)(swz(my_row, lane % CPR) * 16);
   // A rows: m0 + 32·i + my_row
-  const uint32_t a_lane0 = (uint32_t)(my_row * p.lda0 * 2) + cx;
-  const uint32_t a_lane1 = (uint32_t)(my_row * p.lda1 * 2) + cx;
-  const uint32_t a_i0 = (uint32_t)(32 * p.lda0 * 2);
-  const uint32_t a_i1 = (uint32_t)(32 * p.lda1 * 2);
+  const uint32_t a_lane0 = (uint32_t)(my_row * p.lda0 * ESZ) + cx;
+  const uint32_t a_lane1 = (uint32_t)(my_row * p.lda1 * ESZ) + cx;
+  const uint32_t a_i0 = (uint32_t)(32 * p.lda0 * ESZ);
+  const uint32_t a_i1 = (uint32_t)(32 * p.lda1 * ESZ);
   // B rows: tile row rt = 32·i + my_row holds global row tn·TN + my_row +
   // piece(i), plus F for the up half of a SwiGLU tile (rows past N read 0)
-  const uint32_t b_lane0 = (uint32_t)(((int64_t)tn * TN + my_row) * p.ldb0 * 2) + cx;
-  const uint32_t b_lane1 = (uint32_t)(((int64_t)tn * TN + my_row) * p.ldb1 * 2) + cx;
+  const uint32_t b_lane0 = (uint32_t)(((int64_t)tn * TN + my_row) * p.ldb0 * ESZ) + cx;
+  const uint32_t b_lane1 = (uint32_t)(((int64_t)tn * TN + my_row) * p.ldb1 * ESZ) + cx;
   auto b_piece = [&](int i, int64_t ldb) -> uint32_t {
     if constexpr (SWIGLU) {
       // wave column (i / 4) of 64 outputs; gate rows for i % 4 < 2, up rows after
-      return (uint32_t)((((i / 4) * 64 + (i % 2) * 32) + ((i % 4) / 2) * F) * ldb * 2);
+      return (uint32_t)((((i / 4) * 64 + (i % 2) * 32) + ((i % 4) / 2) * F) * ldb * ESZ);
     } else {
-      return (uint32_t)(32 * i * ldb * 2);
+      return (uint32_t)(32 * i * ldb * ESZ);
     }
   };
 
   // per-segment scalars, read once (selected by value inside the loop)
   const int K0 = __builtin_amdgcn_readfirstlane((int)p.K0);
   const int K1 = __builtin_amdgcn_readfirstlane((int)p.K1);
-  const int nk0 = (K0 + BK - 1) / BK;
-  const int nk1 = (K1 + BK - 1) / BK;
+  const int nk0 = (K0 + KSTEP - 1) / KSTEP;
+  const int nk1 = (K1 + KSTEP - 1) / KSTEP;
   const int nk = nk0 + nk1;
 
   // This wave's LDS-DMA loads of its operand for K-step kt into slot `slot`.
@@ -194,13 +212,13 @@ void gemm_kernel(GemmParams p) {
   // zeros without touching memory.
   auto issue_a = [&](int kt, int slot) {
     const bool seg1 = kt >= nk0;
-    const int kbase = (seg1 ? kt - nk0 : kt) * BK;
+    const int kbase = (seg1 ? kt - nk0 : kt) * KSTEP;
     const int kseg = seg1 ? K1 : K0;
     const int kleft = kt < nk ? kseg - kbase : 0;
-    const uint32_t climit = (uint32_t)(kleft >= BK ? BK * 2 : kleft * 2);
+    const uint32_t climit = (uint32_t)(kleft >= KSTEP ? ROWB : kleft * ESZ);
     const bool in_k = cx < climit;
     const __amdgpu_buffer_rsrc_t r = seg1 ? rA1 : rA0;
-    const uint32_t base = (seg1 ? a_lane1 : a_lane0) + (uint32_t)(kbase * 2);
+    const uint32_t base = (seg1 ? a_lane1 : a_lane0) + (uint32_t)(kbase * ESZ);
     const uint32_t stp = seg1 ? a_i1 : a_i0;
 #pragma unroll
     for (int i = 0; i < A_PER; ++i) {
@@ -213,13 +231,13 @@ void gemm_kernel(GemmParams p) {
   };
   auto issue_b = [&](int kt, int slot) {
     const bool seg1 = kt >= nk0;
-    const int kbase = (seg1 ? kt - nk0 : kt) * BK;
+    const int kbase = (seg1 ? kt - nk0 : kt) * KSTEP;
     const int kseg = seg1 ? K1 : K0;
     const int kleft = kt < nk ? kseg - kbase : 0;
-    const uint32_t climit = (uint32_t)(kleft >= BK ? BK * 2 : kleft * 2);
+    const uint32_t climit = (uint32_t)(kleft >= KSTEP ? ROWB : kleft * ESZ);
     const bool in_k = cx < climit;
     const __amdgpu_buffer_rsrc_t r = seg1 ? rB1 : rB0;
-    const uint32_t base = (seg1 ? b_lane1 : b_lane0) + (uint32_t)(kbase * 2);
+    const uint32_t base = (seg1 ? b_lane1 : b_lane0) + (uint32_t)(kbase * ESZ);
 #pragma unroll
     for (int i = 0; i < B_PER; ++i) {
       const int q = 4 * i + wl;
@@ -243,23 +261,101 @@ void gemm_kernel(GemmParams p) {
   constexpr int RB = WM * 2;               // 16-row blocks per wave (tokens)
   constexpr int CB = WN * 2;               // 16-column blocks per wave (outputs)
   const int key_lane = ((lane & 15) >> 1) & (CPR - 1);
-  uint32_t frag_lane[KS];
+  // bf16: 8 consecutive k per lane; MX (probed on gfx950): 32 k per lane, bytes
+  // 0..15 = k 16·(l/16) + 0..15 and bytes 16..31 = k 64 + 16·(l/16) + 0..15 of
+  // the 128-k block, i.e. logical chunks l/16 and 4 + l/16 of the row.
+  constexpr int NFL = MX ? 2 : KS;
+  uint32_t frag_lane[NFL];
 #pragma unroll
-  for (int kk = 0; kk < KS; ++kk)
-    frag_lane[kk] = (uint32_t)((lane & 15) * ROWB + (((4 * kk + (lane >> 4)) ^ key_lane) * 16));
+  for (int f = 0; f < NFL; ++f) {
+    const int chunk = MX ? 4 * f + (lane >> 4) : 4 * f + (lane >> 4);
+    frag_lane[f] = (uint32_t)((lane & 15) * ROWB + ((chunk ^ key_lane) * 16));
+  }
   const uint32_t a_wave = (uint32_t)(wm * WM * 32 * ROWB);
   const uint32_t b_wave = (uint32_t)(B_BASE + wn * WN * 32 * ROWB);
-  // every fragment of one K step: KS x (RB + CB) x 16 bytes per lane
-  bf16x8 fa[KS][RB], fb[KS][CB];
+  // every fragment of one K step (bf16: KS x (RB + CB) x 16 bytes per lane;
+  // MX: (RB + CB) x 32 bytes per lane)
+  bf16x8 fa[MX ? 1 : KS][MX ? 1 : RB], fb[MX ? 1 : KS][MX ? 1 : CB];
+  i32x8 xa[MX ? RB : 1], xb[MX ? CB : 1];
+  // MX block scales.  The scale array holds, for each 128-k step t and 64-row
+  // group g, one dword per lane l = 16·b + r whose byte i is the E8M0 scale of
+  // row 64g + 16i + r over 32-k block b of the step: the MFMA's byte select
+  // then picks the scale of 16-row block i, so a wave keeps one dword per
+  // four 16-row blocks.  A wave's A rows start on a 64-row boundary; its B
+  // rows may start 16, 32 or 48 rows into a group (96-row waves), in which
+  // case one dword more is loaded and consecutive dwords are re-aligned with
+  // a funnel shift before the MFMAs.
+  constexpr int NGA = (RB + 3) / 4;
+  constexpr int NGB = (CB + 3) / 4;
+  constexpr bool B_ALIGNED = SWIGLU || (TN % 64 == 0 && (WN * 32) % 64 == 0);
+  constexpr int NLB = B_ALIGNED ? NGB : NGB + 1;
+  static_assert(!MX || (WM * 32) % 64 == 0, "MX: a wave's A rows span whole 64-row groups");
+  static_assert(!MX || !SWIGLU || (WN * 16) % 64 == 0, "MX: SwiGLU halves span whole groups");
+  uint32_t sca[MX ? NGA : 1], scb[MX ? NLB : 1];
   auto read_step = [&](int sa, int sb) {
+    if constexpr (MX) {
+      const uint32_t ao = a_wave + sa * A_STAGE;
+      const uint32_t bo = b_wave + sb * B_STAGE;
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      const uint32_t ao = frag_lane[kk] + a_wave + sa * A_STAGE;
-      const uint32_t bo = frag_lane[kk] + b_wave + sb * B_STAGE;
+      for (int i = 0; i < RB; ++i) {
+        const u32x4 lo = *(const u32x4*)(lds + ao + frag_lane[0] + i * 16 * ROWB);
+        const u32x4 hi = *(const u32x4*)(lds + ao + frag_lane[1] + i * 16 * ROWB);
+        xa[i] = (i32x8){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                        (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
 #pragma unroll
-      for (int i = 0; i < RB; ++i) fa[kk][i] = *(const bf16x8*)(lds + ao + i * 16 * ROWB);
+      for (int j = 0; j < CB; ++j) {
+        const u32x4 lo = *(const u32x4*)(lds + bo + frag_lane[0] + j * 16 * ROWB);
+        const u32x4 hi = *(const u32x4*)(lds + bo + frag_lane[1] + j * 16 * ROWB);
+        xb[j] = (i32x8){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                        (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
+    } else {
 #pragma unroll
-      for (int j = 0; j < CB; ++j) fb[kk][j] = *(const bf16x8*)(lds + bo + j * 16 * ROWB);
+      for (int kk = 0; kk < KS; ++kk) {
+        const uint32_t ao = frag_lane[kk] + a_wave + sa * A_STAGE;
+        const uint32_t bo = frag_lane[kk] + b_wave + sb * B_STAGE;
+#pragma unroll
+        for (int i = 0; i < RB; ++i) fa[kk][i] = *(const bf16x8*)(lds + ao + i * 16 * ROWB);
+#pragma unroll
+        for (int j = 0; j < CB; ++j) fb[kk][j] = *(const bf16x8*)(lds + bo + j * 16 * ROWB);
+      }
+    }
+  };
+  // MX scales of step kt (buffer loads: groups past the padded scale arrays
+  // read as zeros)
+  const __amdgpu_buffer_rsrc_t rsA0 =
+      MX ? make_rsrc(p.sA0, (K0 / 128) * p.sMp * 4) : rA0;
+  const __amdgpu_buffer_rsrc_t rsB0 =
+      MX ? make_rsrc(p.sB0, (K0 / 128) * p.sNp * 4) : rB0;
+  const __amdgpu_buffer_rsrc_t rsA1 =
+      (MX && has1) ? make_rsrc(p.sA1, (K1 / 128) * p.sMp * 4) : rsA0;
+  const __amdgpu_buffer_rsrc_t rsB1 =
+      (MX && has1) ? make_rsrc(p.sB1, (K1 / 128) * p.sNp * 4) : rsB0;
+  const int64_t ga = (m0 + wm * WM * 32) >> 6;          // A: first 64-row group
+  // B: first group of each dword (SwiGLU: gate half, then up half) and the
+  // funnel shift in bits for waves that start inside a group
+  const int64_t nb0 = SWIGLU ? (int64_t)tn * TN + wn * (WN * 16)
+                             : (int64_t)tn * TN + wn * WN * 32;
+  const int64_t gb = nb0 >> 6;
+  const int bsh = (int)(nb0 & 63) >> 1;
+  auto load_scales = [&](int kt) {
+    if constexpr (MX) {
+      const bool seg1 = kt >= nk0;
+      const int64_t t = seg1 ? kt - nk0 : kt;
+      const __amdgpu_buffer_rsrc_t ra = seg1 ? rsA1 : rsA0;
+      const __amdgpu_buffer_rsrc_t rb = seg1 ? rsB1 : rsB0;
+      const int64_t ta = t * (p.sMp >> 6), tb = t * (p.sNp >> 6);
+#pragma unroll
+      for (int q = 0; q < NGA; ++q)
+        sca[q] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
+            ra, (uint32_t)(((ta + ga + q) * 64 + lane) * 4), 0, 0);
+#pragma unroll
+      for (int q = 0; q < NLB; ++q) {
+        const int64_t g = SWIGLU ? q * (F >> 6) + gb : gb + q;
+        scb[q] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
+            rb, (uint32_t)(((tb + g) * 64 + lane) * 4), 0, 0);
+      }
     }
   };
 
@@ -272,14 +368,29 @@ void gemm_kernel(GemmParams p) {
       for (int v = 0; v < 4; ++v) acc[i][j][v] = 0.0f;
 
   auto compute_step = [&]() {
+    if constexpr (MX) {
+      uint32_t sbv[NGB];
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk)
+      for (int q = 0; q < NGB; ++q)
+        sbv[q] = B_ALIGNED ? scb[q] : __builtin_amdgcn_alignbit(scb[q + 1], scb[q], bsh);
+      // the byte selects are immediates: unroll over compile-time indexes
+      static_for<RB>([&](auto I) {
+        static_for<CB>([&](auto J) {
+          constexpr int i = decltype(I)::value, j = decltype(J)::value;
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              xb[j], xa[i], acc[i][j], 0, 0, j & 3, (int)sbv[j >> 2], i & 3, (int)sca[i >> 2]);
+        });
+      });
+    } else {
 #pragma unroll
-      for (int i = 0; i < RB; ++i)
+      for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
-        for (int j = 0; j < CB; ++j)
-          acc[i][j] =
-              __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[kk][j], fa[kk][i], acc[i][j], 0, 0, 0);
+        for (int i = 0; i < RB; ++i)
+#pragma unroll
+          for (int j = 0; j < CB; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[kk][j], fa[kk][i], acc[i][j],
+                                                                0, 0, 0);
+    }
   };
 
   // ---- main loop: ping-pong ----------------------------------------------------------
@@ -311,8 +422,10 @@ void gemm_kernel(GemmParams p) {
   __builtin_amdgcn_s_barrier();
   int sa = 0;                              // A slot of step kt (kt % 3)
   if (wgrp == 0) {
+    load_scales(0);
     read_step(0, 0);
-    wait_vm_lgkm0<B_PER>();
+    if constexpr (MX) wait_vm_lgkm0<0>();    // the scales were issued after B(1)
+    else wait_vm_lgkm0<B_PER>();
     __builtin_amdgcn_s_barrier();
     for (int kt = 0; kt < nk; ++kt) {
       const int sb = kt & 1;
@@ -325,9 +438,12 @@ void gemm_kernel(GemmParams p) {
       wait_vm_lgkm0<0>();                  // B(kt+1) has landed
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
+      // MX reads unconditionally (after the last step: stale LDS and scales that
+      // are never used), which keeps the 8-register fragments out of phis
+      if (MX || kt + 1 < nk) load_scales(kt + 1);   // before the B loads: retire first
       issue_b(kt + 2, sb);
-      if (kt + 1 < nk) read_step(sa_next, sb ^ 1);
-      wait_vm_lgkm0<B_PER>();              // fragments in registers
+      if (MX || kt + 1 < nk) read_step(sa_next, sb ^ 1);
+      wait_vm_lgkm0<B_PER>();              // fragments (and scales) in registers
       __builtin_amdgcn_s_barrier();
       sa = sa_next;
     }
@@ -338,6 +454,7 @@ void gemm_kernel(GemmParams p) {
       const int sa_next = sa == NSLOT_A - 1 ? 0 : sa + 1;
       const int sa_load = sa_next == NSLOT_A - 1 ? 0 : sa_next + 1;   // (kt + 2) % 3
       __builtin_amdgcn_sched_barrier(0);
+      load_scales(kt);                     // (MX) before the A loads: retire first
       read_step(sa, sb);
       issue_a(kt + 2, sa_load);
       wait_vm_lgkm0<A_WAIT>();             // A(kt+1) has landed; fragments in registers
@@ -471,7 +588,7 @@ void gemm_kernel(GemmParams p) {
   }
 }
 
-template <int WM, int WN, bool SWIGLU>
+template <int WM, int WN, bool SWIGLU, bool MX>
 hipError_t launch(const GemmParams& p, hipStream_t s) {
   constexpr int BM = kWaveRows * WM * 32;
   constexpr int TN = (SWIGLU ? 16 : 32) * kWaveCols * WN;
@@ -479,8 +596,8 @@ hipError_t launch(const GemmParams& p, hipStream_t s) {
   const int64_t tiles = ((p.M + BM - 1) / BM) * ((nout + TN - 1) / TN);
   if (tiles <= 0) return hipSuccess;
   if (tiles > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_kernel<WM, WN, SWIGLU>), dim3((unsigned)tiles), dim3(kThreads), 0, s,
-                     p);
+  hipLaunchKernelGGL((gemm_kernel<WM, WN, SWIGLU, MX>), dim3((unsigned)tiles), dim3(kThreads), 0,
+                     s, p);
   return hipGetLastError();
 }
 
@@ -488,9 +605,12 @@ hipError_t launch(const GemmParams& p, hipStream_t s) {
 
 hipError_t launch_gemm(GemmKind kind, const GemmParams& p, hipStream_t s) {
   switch (kind) {
-    case GEMM_DOWN: return launch<2, 3, false>(p, s);
-    case GEMM_UP: return launch<2, 4, false>(p, s);
-    case GEMM_UP_SWIGLU: return launch<2, 4, true>(p, s);
+    case GEMM_DOWN: return launch<2, 3, false, false>(p, s);
+    case GEMM_UP: return launch<2, 4, false, false>(p, s);
+    case GEMM_UP_SWIGLU: return launch<2, 4, true, false>(p, s);
+    case GEMM_MX_DOWN: return launch<2, 3, false, true>(p, s);
+    case GEMM_MX_UP: return launch<2, 4, false, true>(p, s);
+    case GEMM_MX_UP_SWIGLU: return launch<2, 4, true, true>(p, s);
   }
   return hipErrorInvalidValue;
 }

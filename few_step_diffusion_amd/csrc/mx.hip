@@ -15,10 +15,12 @@
 //
 // Layout written here (and read by the MXFP8 GEMM): elements as bytes [M, Kp]
 // with Kp = K rounded up to a multiple of 128 (one GEMM K step), the padding
-// zero; scales step-major, S[t][m][b] = scale of row m, block 4t + b, for
-// t < Kp/128, m < Mp = M rounded up to 256, b < 4 (padded rows and blocks hold
-// 127, a scale of 1), so the scales of one 256-row tile for one K step are one
-// contiguous 1 KB.
+// zero.  Scales are grouped by K step t (128 elements) and 64-row group g:
+// dword (t·Mp/64 + g)·64 + 16·b + r holds in its byte i the scale of row
+// 64g + 16i + r over block 4t + b, for t < Kp/128, g < Mp/64 with Mp = M
+// rounded up to 256, and b, i < 4, r < 16 (padded rows and blocks hold 127, a
+// scale of 1).  That is the order in which the GEMM's 64 lanes take a row
+// block's scales, with one dword serving four 16-row blocks.
 #include "fsd_internal.h"
 
 namespace fsd {
@@ -56,7 +58,8 @@ __global__ __launch_bounds__(kThreads) void mx_quantize_kernel(const bf16_t* X, 
   if (id >= Mp * nb) return;
   const int64_t m = id / nb;
   const int64_t b = id - m * nb;
-  uint8_t* s_out = S + ((b >> 2) * Mp + m) * 4 + (b & 3);
+  uint8_t* s_out =
+      S + (((b >> 2) * (Mp >> 6) + (m >> 6)) * 64 + (b & 3) * 16 + (m & 15)) * 4 + ((m >> 4) & 3);
   if (m >= M) {                                        // padded row: scale only
     *s_out = 127;
     return;

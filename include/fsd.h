@@ -222,17 +222,48 @@ int fsd_token_head_euler(const void* H, int64_t ldh, const void* P, float* z,
  * and saturated at 448.
  *
  * Layout: elements Q as bytes [M, Kp], Kp = K rounded up to 128, row stride
- * ldq >= Kp (multiple of 16), columns K..Kp-1 zero; scales S as
- * [Kp/128][Mp][4] bytes with Mp = M rounded up to 256 (entry (t, m, b) is the
- * scale of row m, elements 128t + 32b .. +31; padding entries are 127).
+ * ldq >= Kp (multiple of 16), columns K..Kp-1 zero.  Scales S, Mp = M rounded
+ * up to 256: for each 128-element step t < Kp/128 and 64-row group g < Mp/64,
+ * 64 consecutive 32-bit words; byte i (0..3, little-endian) of word 16·b + r
+ * (b < 4, r < 16) is the E8M0 scale of row 64g + 16i + r over elements
+ * 128t + 32b .. +31.  That is the order in which the MXFP8 GEMM's lanes take
+ * the scales of a 16-row block, one word serving four blocks.  Padding rows
+ * and blocks hold 127 (a scale of 1) and zero elements.  S is 4-byte aligned.
  *
  * fsd_mx_scale_bytes: size of S for M rows of K elements.
  * fsd_mx_quantize: X bf16 [M, K] (row stride ldx >= K, multiple of 8, 16-byte
  *   aligned), K a multiple of 32 -> Q, S as above.  Q 16-byte aligned; Q and S
- *   must not overlap X or each other.  Errors: FSD_EINVAL, FSD_EALIGN. */
+ *   must not overlap X or each other.  Errors: FSD_EINVAL, FSD_EALIGN.
+ *
+ * fsd_mx_lora_down: phase A on MXFP8 operands,
+ *   T = bf16(scale · deq(Xq, Xs) · deq(Aq, As)ᵀ), fp32 accumulation.
+ *   Xq [M, Kp] (row stride ldxq) with scales Xs for M rows; Aq [r, Kp] (row
+ *   stride Kp) with scales As for r rows; K a multiple of 32, r a multiple of
+ *   8; T bf16 [M, r] (row stride ldt >= r, multiple of 8, 16-byte aligned),
+ *   not overlapping any input.
+ * fsd_mx_lora_up: phase B on MXFP8 operands,
+ *   Y = epi(deq(Xq)·deq(W0q)ᵀ + deq(Tq)·deq(Bq)ᵀ + bias) (+ residual), with
+ *   W0q [N, Kp] (row stride Kp, scales W0s for N rows), Tq [M, rp] (row stride
+ *   ldtq, scales Ts for M rows) and Bq [N, rp] (row stride rp, scales Bs for
+ *   N rows), rp = r rounded up to 128.  r a multiple of 32 (0: no LoRA term;
+ *   Tq, Ts, Bq, Bs unused).  bias, residual, Y, ldy, epilogue as for
+ *   fsd_lora_up; SwiGLU needs N a multiple of 128 (else FSD_EUNSUPPORTED).
+ * In both, code arrays are 16-byte aligned with row strides multiples of 16,
+ * scale arrays 4-byte aligned; a weight operand must span less than 2 GiB with
+ * 256 extra rows, an activation operand's 256-row tile likewise, and every
+ * scale array less than 2 GiB (else FSD_EUNSUPPORTED). */
 size_t fsd_mx_scale_bytes(int64_t M, int64_t K);
 int fsd_mx_quantize(const void* X, int64_t ldx, int64_t M, int64_t K, void* Q,
                     int64_t ldq, void* S, void* stream);
+int fsd_mx_lora_down(const void* Xq, int64_t ldxq, const void* Xs, const void* Aq,
+                     const void* As, float scale, void* T, int64_t ldt, int64_t M,
+                     int64_t K, int64_t r, void* stream);
+int fsd_mx_lora_up(const void* Xq, int64_t ldxq, const void* Xs, const void* W0q,
+                   const void* W0s, const void* Tq, int64_t ldtq, const void* Ts,
+                   const void* Bq, const void* Bs, const float* bias,
+                   const void* residual, int64_t ldr, void* Y, int64_t ldy,
+                   int64_t M, int64_t N, int64_t K, int64_t r, int epilogue,
+                   void* stream);
 
 #ifdef __cplusplus
 }

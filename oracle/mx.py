@@ -110,3 +110,52 @@ def dequantize_rows(q, s, K):
         for k in range(K):
             out[i, k] = math.ldexp(e4m3_value(int(q[i, k])), int(s[i, k // MX_BLOCK]) - 127)
     return out
+
+
+# ------------------------------------------------------------------ array form
+# The same quantizer over whole arrays, for matrices too large for the element
+# loops above: every step is the scalar one (np.frexp gives the exact binade,
+# np.rint rounds half to even, np.ldexp scales exactly).  Pinned to
+# quantize_rows / dequantize_rows element for element by the CPU tests.
+_E4M3_TABLE = np.array([e4m3_value(b) if (b & 0x7F) != 0x7F else 0.0 for b in range(256)])
+
+
+def quantize_rows_np(X):
+    """quantize_rows for K a multiple of 32, as array operations."""
+    X = np.asarray(X, dtype=np.float64)
+    rows, K = X.shape
+    if K % MX_BLOCK:
+        raise ValueError("K must be a multiple of 32")
+    Kp = (K + 127) // 128 * 128
+    blk = X.reshape(rows, K // MX_BLOCK, MX_BLOCK)
+    amax = np.abs(blk).max(axis=2)
+    _, ex = np.frexp(amax)                          # amax = m·2^ex, 0.5 <= m < 1
+    e = np.clip(ex.astype(np.int64) - 1 - E4M3_EMAX, -127, 127)
+    e = np.where(amax == 0.0, -127, e)
+    y = np.ldexp(blk, -e[..., None])                # exact: a power-of-two scaling
+    a = np.abs(y)
+    _, ey = np.frexp(a)
+    binade = np.maximum(ey.astype(np.int64) - 1, E4M3_EMIN)
+    quantum = np.ldexp(1.0, binade - 3)
+    v = np.minimum(np.rint(a / quantum) * quantum, E4M3_MAX)   # nearest-even, saturated
+    # bytes of the rounded magnitudes
+    _, ev = np.frexp(v)
+    ev = ev.astype(np.int64) - 1
+    normal = v >= math.ldexp(1.0, E4M3_EMIN)
+    ev_n = np.where(normal, ev, 0)
+    mant_n = (np.ldexp(v, -ev_n) - 1.0) * 8.0
+    code_n = ((ev_n + 7) << 3) | mant_n.astype(np.int64)
+    code_s = (v / math.ldexp(1.0, E4M3_EMIN - 3)).astype(np.int64)
+    code = np.where(normal, code_n, code_s) | np.where(np.signbit(y), 0x80, 0)
+    q = np.zeros((rows, Kp), np.uint8)
+    q[:, :K] = code.reshape(rows, K).astype(np.uint8)
+    s = np.full((rows, Kp // MX_BLOCK), 127, np.uint8)
+    s[:, :K // MX_BLOCK] = (e + 127).astype(np.uint8)
+    return q, s
+
+
+def dequantize_rows_np(q, s, K):
+    """dequantize_rows as array operations."""
+    q = np.asarray(q)[:, :K]
+    sc = np.asarray(s, dtype=np.int64)[:, np.arange(K) // MX_BLOCK] - 127
+    return np.ldexp(_E4M3_TABLE[q], sc)

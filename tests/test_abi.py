@@ -154,6 +154,80 @@ def test_standin_and_merge_validation(L):
     assert L.fsd_lora_merge(1, arr, arr, rk, None, 16, 16, a(2), a(2), None) == EINVAL
 
 
+def test_mx_validation(L):
+    f = ctypes.c_float
+    assert L.fsd_mx_scale_bytes(300, 576) == 5 * 512 * 4
+    assert L.fsd_mx_scale_bytes(0, 576) == 0
+    # quantize
+    assert L.fsd_mx_quantize(a(1), 576, 0, 576, a(2), 640, a(3), None) == OK
+    assert L.fsd_mx_quantize(a(1), 576, 300, 560, a(2), 640, a(3), None) == EINVAL  # K % 32
+    assert L.fsd_mx_quantize(a(1), 576, 300, 576, a(2), 576, a(3), None) == EINVAL  # ldq < Kp
+    assert L.fsd_mx_quantize(a(1), 576, 300, 576, a(2), 640, P(BASE + 3 * 0x10000000 + 2),
+                             None) == EALIGN                                      # S word-aligned
+    assert L.fsd_mx_quantize(a(1), 576, 300, 576, a(2), 640, P(BASE + 0x10000000 + 64),
+                             None) == EINVAL                                      # S overlaps X
+
+    def down(**kw):
+        args = dict(Xq=a(1), ldxq=1024, Xs=a(2), Aq=a(3), As=a(4), s=1.0, T=a(5), ldt=576,
+                    M=100, K=1024, r=576)
+        args.update(kw)
+        return L.fsd_mx_lora_down(args["Xq"], args["ldxq"], args["Xs"], args["Aq"], args["As"],
+                                  f(args["s"]), args["T"], args["ldt"], args["M"], args["K"],
+                                  args["r"], None)
+    assert down(M=0) == OK
+    assert down(K=1000) == EINVAL                        # K % 32
+    assert down(ldxq=1000, K=992) == EINVAL              # ldxq < Kp (1024)
+    assert down(ldxq=1032) == EINVAL                     # ldxq % 16
+    assert down(Xs=None) == EINVAL
+    assert down(As=P(BASE + 4 * 0x10000000 + 2)) == EALIGN
+    assert down(Aq=P(BASE + 3 * 0x10000000 + 8)) == EALIGN
+    assert down(s=math.nan) == EINVAL
+    assert down(T=P(BASE + 2 * 0x10000000 + 64)) == EINVAL   # T overlaps Xs
+    assert down(r=576, K=4 * 1024 * 1024, ldxq=4 * 1024 * 1024) == EUNSUP
+
+    def upm(**kw):
+        args = dict(Xq=a(1), ldxq=1024, Xs=a(2), Wq=a(3), Ws=a(4), Tq=a(5), ldtq=640, Ts=a(6),
+                    Bq=a(7), Bs=a(8), bias=None, res=None, ldr=0, Y=a(9), ldy=1024, M=300,
+                    N=1024, K=1024, r=576, epi=0)
+        args.update(kw)
+        return L.fsd_mx_lora_up(args["Xq"], args["ldxq"], args["Xs"], args["Wq"], args["Ws"],
+                                args["Tq"], args["ldtq"], args["Ts"], args["Bq"], args["Bs"],
+                                args["bias"], args["res"], args["ldr"], args["Y"], args["ldy"],
+                                args["M"], args["N"], args["K"], args["r"], args["epi"], None)
+    assert upm(M=0) == OK
+    assert upm(r=0, Tq=None, Ts=None, Bq=None, Bs=None, M=0) == OK
+    assert upm(r=40) == EINVAL                           # r % 32
+    assert upm(ldtq=576) == EINVAL                       # ldtq < rp (640)
+    assert upm(Ts=None) == EINVAL
+    assert upm(Bs=P(BASE + 8 * 0x10000000 + 1)) == EALIGN
+    assert upm(epi=1, N=1040) == EUNSUP                  # MX SwiGLU needs N % 128 == 0
+    assert upm(epi=1, N=1032) == EINVAL                  # ... and N % 16 as always
+    assert upm(epi=1, res=a(10), ldr=512) == EUNSUP
+    assert upm(epi=3) == EINVAL
+    assert upm(Y=P(BASE + 7 * 0x10000000 + 4096)) == EINVAL   # Y overlaps Bq
+    assert upm(M=0, res=a(9), ldr=1024) == OK            # in-place residual is legal
+
+
+def test_mx_scale_layout_helpers():
+    """The host pack / unpack helpers follow the documented layout: byte i of word
+    16·b + r of (step t, group g) is row 64g + 16i + r, block 4t + b."""
+    import numpy as np
+    M, K = 300, 576
+    off = fsd.mx_scale_offsets(M, K)
+    Mp = 512
+    assert off.shape == (M, 20)
+    for m, blk in [(0, 0), (17, 1), (63, 3), (64, 4), (299, 19), (130, 9)]:
+        t, b = blk // 4, blk % 4
+        g, i, r = m // 64, (m % 64) // 16, m % 16
+        assert off[m, blk] == ((t * (Mp // 64) + g) * 64 + 16 * b + r) * 4 + i
+    assert len(set(off.ravel().tolist())) == off.size   # one byte per scale
+    s = np.random.default_rng(0).integers(0, 255, size=(M, 20), dtype=np.uint8)
+    S = fsd.mx_pack_scales(s, K)
+    assert S.numel() == fsd.mx_scale_bytes(M, K)
+    assert np.array_equal(fsd.mx_unpack_scales(S, M, K), s)
+    assert int((S.numpy() == 127).sum()) >= (Mp - M) * 20   # padding rows
+
+
 def test_python_binding_rejects_cpu_tensors():
     import torch
     with pytest.raises(ValueError):

@@ -1,13 +1,17 @@
 """GPU parity of the MXFP8 path against the fp64 MX oracle (oracle/mx.py).
 
 Quantization is byte work: elements and scales must match the oracle bit for bit.
+The MXFP8 GEMMs take operands quantized by the oracle on the host and are
+compared with the fp64 product of the dequantized values (bf16 output: per-row
+rel-L2 and rel-max <= 2e-2, the bf16 linears' gate).
 """
 import numpy as np
 import pytest
 import torch
 
 import few_step_diffusion_amd as fsd
-from oracle import mx
+import oracle
+from oracle import metrics, mx
 
 pytestmark = pytest.mark.gpu
 
@@ -36,11 +40,9 @@ def mx_rows(M, K, seed):
 
 
 def scales_by_row(S, M, K):
-    """Rows x blocks view of the step-major scale array [Kp/128][Mp][4]."""
-    Kp = fsd.mx_padded_k(K)
+    """Rows x blocks view of the scale array (padding rows included)."""
     Mp = (M + 255) // 256 * 256
-    t = S.cpu().numpy().reshape(Kp // 128, Mp, 4)
-    return t.transpose(1, 0, 2).reshape(Mp, Kp // 32)
+    return fsd.mx_unpack_scales(S, Mp, K)
 
 
 @pytest.mark.parametrize("M,K", [(1, 32), (5, 96), (300, 576), (8, 3072)])
@@ -57,3 +59,91 @@ def test_mx_quantize_bit_exact(gpu, M, K):
     s_rows = scales_by_row(S, M, K)
     assert np.array_equal(s_rows[:M], s_ref)
     assert np.all(s_rows[M:] == 127)
+
+
+# ------------------------------------------------------------------ MXFP8 GEMMs
+def mx_operand(a, dev):
+    """Oracle MXFP8 of host rows a [rows, K]: device codes and scales, and the
+    fp64 dequantized values [rows, Kp] (zero past K)."""
+    a = np.asarray(a, dtype=np.float64)
+    q, s = mx.quantize_rows_np(a)
+    Q = torch.from_numpy(q).to(dev)
+    S = fsd.mx_pack_scales(s, a.shape[1]).to(dev)
+    return Q, S, mx.dequantize_rows_np(q, s, q.shape[1])
+
+
+def assert_gemm(Y, ref, what):
+    ok, err = metrics.gemm_ok(Y.float().cpu().numpy(), ref)
+    say(f"{what}: rel_l2 {err[0]:.3e} rel_max {err[1]:.3e}")
+    assert ok, (what, err)
+
+
+@pytest.mark.parametrize("M,K,r", [(1, 32, 576), (300, 1024, 576), (257, 608, 64)])
+def test_mx_lora_down(gpu, M, K, r):
+    say(f"mx lora_down M={M} K={K} r={r}")
+    rng = np.random.default_rng(M + 7 * K + r)
+    Qx, Sx, Xd = mx_operand(rng.standard_normal((M, K)), gpu)
+    Qa, Sa, Ad = mx_operand(rng.standard_normal((r, K)) * 0.02, gpu)
+    T = fsd.mx_lora_down(Qx, Sx, Qa, Sa, scale=0.5)
+    assert T.shape == (M, r)
+    ref = 0.5 * oracle.lora_linear_rows(Xd, Ad, None, None)
+    assert_gemm(T, ref, f"mx down M={M} K={K} r={r}")
+
+
+@pytest.mark.parametrize("M,N,K,r,epi,extras", [
+    (300, 512, 1024, 576, "none", False),
+    (300, 200, 256, 0, "none", True),
+    (1, 384, 128, 64, "none", True),
+    (130, 256, 512, 576, "swiglu", True),
+    (513, 384, 384, 576, "swiglu", False),
+])
+def test_mx_lora_up(gpu, M, N, K, r, epi, extras):
+    say(f"mx lora_up M={M} N={N} K={K} r={r} {epi} extras={extras}")
+    rng = np.random.default_rng(M + 3 * N + 5 * K + r)
+    Qx, Sx, Xd = mx_operand(rng.standard_normal((M, K)), gpu)
+    Qw, Sw, Wd = mx_operand(rng.standard_normal((N, K)) * 0.03, gpu)
+    if r:
+        Qt, St, Td = mx_operand(rng.standard_normal((M, r)) * 0.3, gpu)
+        Qb, Sb, Bd = mx_operand(rng.standard_normal((N, r)) * 0.02, gpu)
+        Xcat, Wcat = np.hstack([Xd, Td]), np.hstack([Wd, Bd])
+    else:
+        Qt = St = Qb = Sb = None
+        Xcat, Wcat = Xd, Wd
+    nout = N // 2 if epi == "swiglu" else N
+    bias = rng.standard_normal(N).astype(np.float32) * 0.1 if extras else None
+    res = None
+    if extras and epi == "none":
+        res = torch.from_numpy(rng.standard_normal((M, nout))).to(torch.bfloat16)
+    Y = fsd.mx_lora_up(Qx, Sx, Qw, Sw, Qt, St, Qb, Sb,
+                       bias=None if bias is None else torch.from_numpy(bias).to(gpu),
+                       residual=None if res is None else res.to(gpu), epilogue=epi)
+    assert Y.shape == (M, nout)
+    ref = oracle.lora_linear_rows(Xcat, Wcat, None, None, bias=bias,
+                                  residual=None if res is None else res.float().numpy(),
+                                  swiglu=epi == "swiglu")
+    assert_gemm(Y, ref, f"mx up M={M} N={N} K={K} r={r} {epi}")
+
+
+def test_mx_chain_through_quantizer(gpu):
+    """bf16 X -> MXFP8 -> phase A -> bf16 T -> MXFP8 -> phase B, all on the GPU,
+    against the oracle running the same chain (its T rounded to bf16 as the GPU's is)."""
+    M, N, K, r = 300, 384, 640, 576
+    say(f"mx chain M={M} N={N} K={K} r={r}")
+    rng = np.random.default_rng(42)
+    Xb = torch.from_numpy(rng.standard_normal((M, K))).to(torch.bfloat16)
+    Qw, Sw, Wd = mx_operand(rng.standard_normal((N, K)) * 0.03, gpu)
+    Qa, Sa, Ad = mx_operand(rng.standard_normal((r, K)) * 0.05, gpu)
+    Qb, Sb, Bd = mx_operand(rng.standard_normal((N, r)) * 0.02, gpu)
+    Qx, Sx = fsd.mx_quantize(Xb.to(gpu))
+    T = fsd.mx_lora_down(Qx, Sx, Qa, Sa, scale=0.75)
+    Qt, St = fsd.mx_quantize(T)
+    Y = fsd.mx_lora_up(Qx, Sx, Qw, Sw, Qt, St, Qb, Sb)
+    qx, sx = mx.quantize_rows_np(Xb.float().numpy())
+    Xd = mx.dequantize_rows_np(qx, sx, qx.shape[1])
+    T_ref = 0.75 * oracle.lora_linear_rows(Xd, Ad, None, None)
+    assert_gemm(T, T_ref, "chain T")
+    T_b = oracle.bf16_value(oracle.bf16_bits(T_ref.astype(np.float32))).reshape(T_ref.shape)
+    qt, st = mx.quantize_rows_np(T_b)
+    Td = mx.dequantize_rows_np(qt, st, qt.shape[1])
+    ref = oracle.lora_linear_rows(np.hstack([Xd, Td]), np.hstack([Wd, Bd]), None, None)
+    assert_gemm(Y, ref, "chain Y")

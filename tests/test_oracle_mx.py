@@ -77,3 +77,38 @@ def test_quantization_error_bound():
             else:
                 bound = max(abs(X[i, k]) * 2.0 ** -4, 2.0 ** -10 * X_scale)
             assert abs(D[i, k] - X[i, k]) <= bound * (1 + 1e-12), (i, k)
+
+
+def _awkward_rows():
+    """Rows over many binades with zeros, huge and tiny rows, E4M3 ties, saturating
+    values, subnormal results and signed zeros."""
+    rng = np.random.default_rng(5)
+    X = rng.standard_normal((9, 160)) * np.exp(rng.standard_normal((9, 1)) * 4.0)
+    X[0] = 0.0
+    X[1] *= 1e36
+    X[2] *= 1e-36
+    ties = [1.0625, 1.1875, 1.3125, 1.4375, 1.5625, 1.6875, 1.8125, 1.875, 1.9375]
+    X[3, :32] = 0.0
+    X[3, :9] = ties
+    X[3, 9:18] = [-t for t in ties]
+    X[4, :32] = -0.0
+    X[4, 0] = 1.0
+    X[4, 1:8] = [-2.0 ** -20, 2.0 ** -17, -2.0 ** -16.5, 2.0 ** -14.9, 3.0 * 2.0 ** -18,
+                 -5.0 * 2.0 ** -18, 2.0 ** -18]                  # subnormal and flushed results
+    X[5, :32] = np.linspace(-1.0, 1.0, 32)
+    X[5, 32:64] = 0.0
+    X[5, 32] = -2.0 ** -140                                      # a tiny-amax block
+    return X
+
+
+def test_array_form_matches_element_loops():
+    X = _awkward_rows()
+    q, s = mx.quantize_rows(X)
+    qn, sn = mx.quantize_rows_np(X)
+    assert np.array_equal(q, qn) and np.array_equal(s, sn)
+    assert np.array_equal(mx.dequantize_rows(q, s, 160), mx.dequantize_rows_np(q, s, 160))
+    # every byte pattern but the NaNs decodes the same way
+    codes = np.array([[b for b in range(256) if (b & 0x7F) != 0x7F][:224]], np.uint8)
+    sc = np.array([[120, 127, 134, 2, 250, 127, 64]], np.uint8)
+    assert np.array_equal(mx.dequantize_rows(codes, sc, 224),
+                          mx.dequantize_rows_np(codes, sc, 224))
