@@ -18,6 +18,7 @@ __all__ = [
     "lora_down", "lora_up", "lora_linear", "renoise", "euler_step", "token_embed",
     "token_head", "token_head_euler", "mx_quantize", "mx_padded_k", "mx_scale_bytes",
     "mx_scale_offsets", "mx_pack_scales", "mx_unpack_scales", "mx_lora_down", "mx_lora_up",
+    "mx_lora_up_swiglu_mx",
     "EPI_NONE", "EPI_SWIGLU",
 ]
 
@@ -78,6 +79,9 @@ _SIGS = {
     "fsd_mx_lora_up": ([_c_void_p, _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64,
                         _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _c_void_p,
                         _i64, _i64, _i64, _i64, _i64, _int, _c_void_p], _int),
+    "fsd_mx_lora_up_swiglu_mx": ([_c_void_p, _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                  _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                  _i64, _c_void_p, _i64, _i64, _i64, _i64, _c_void_p], _int),
 }
 
 
@@ -414,15 +418,7 @@ def mx_lora_down(Xq, Xs, Aq, As, scale=1.0, T=None):
     return T
 
 
-def mx_lora_up(Xq, Xs, W0q, W0s, Tq=None, Ts=None, Bq=None, Bs=None, bias=None,
-               residual=None, epilogue=EPI_NONE, out=None):
-    """Phase B on MXFP8 operands: Y = epi([Xq | Tq]·[W0q | Bq]ᵀ (dequantized) + bias) (+ residual).
-
-    Xq uint8 [M, Kp]; W0q uint8 [N, Kp] (contiguous); Tq uint8 [M, rp] and Bq uint8
-    [N, rp] (contiguous), rp a multiple of 128, or None for no LoRA term; Xs, W0s,
-    Ts, Bs their scale arrays.
-    """
-    epilogue = _epi(epilogue)
+def _mx_up_operands(Xq, Xs, W0q, W0s, Tq, Ts, Bq, Bs, bias):
     _need(Xq, "Xq", torch.uint8)
     _need(W0q, "W0q", torch.uint8)
     M, Kp = Xq.shape
@@ -441,16 +437,50 @@ def mx_lora_up(Xq, Xs, W0q, W0s, Tq=None, Ts=None, Bq=None, Bs=None, bias=None,
         _need_scales(Bs, "Bs", N, rp)
     if bias is not None:
         _need(bias, "bias", torch.float32, dims=1)
+    ops = (_ptr(Xq), _ld(Xq), _ptr(Xs), _ptr(W0q), _ptr(W0s), _ptr(Tq) if rp else None,
+           _ld(Tq) if rp else 0, _ptr(Ts) if rp else None, _ptr(Bq) if rp else None,
+           _ptr(Bs) if rp else None, _ptr(bias))
+    return M, N, Kp, rp, ops
+
+
+def mx_lora_up(Xq, Xs, W0q, W0s, Tq=None, Ts=None, Bq=None, Bs=None, bias=None,
+               residual=None, epilogue=EPI_NONE, out=None):
+    """Phase B on MXFP8 operands: Y = epi([Xq | Tq]·[W0q | Bq]ᵀ (dequantized) + bias) (+ residual).
+
+    Xq uint8 [M, Kp]; W0q uint8 [N, Kp] (contiguous); Tq uint8 [M, rp] and Bq uint8
+    [N, rp] (contiguous), rp a multiple of 128, or None for no LoRA term; Xs, W0s,
+    Ts, Bs their scale arrays.
+    """
+    epilogue = _epi(epilogue)
+    M, N, Kp, rp, ops = _mx_up_operands(Xq, Xs, W0q, W0s, Tq, Ts, Bq, Bs, bias)
     if residual is not None:
         _need(residual, "residual", torch.bfloat16)
     if out is None:
         out = torch.empty((M, _out_cols(N, epilogue)), dtype=torch.bfloat16, device=Xq.device)
     _need(out, "out", torch.bfloat16)
-    st = lib().fsd_mx_lora_up(_ptr(Xq), _ld(Xq), _ptr(Xs), _ptr(W0q), _ptr(W0s),
-                              _ptr(Tq) if rp else None, _ld(Tq) if rp else 0,
-                              _ptr(Ts) if rp else None, _ptr(Bq) if rp else None,
-                              _ptr(Bs) if rp else None, _ptr(bias), _ptr(residual),
+    st = lib().fsd_mx_lora_up(*ops, _ptr(residual),
                               _ld(residual) if residual is not None else 0, _ptr(out), _ld(out),
                               M, N, Kp, rp, epilogue, _stream(Xq))
     _check("fsd_mx_lora_up", st)
     return out
+
+
+def mx_lora_up_swiglu_mx(Xq, Xs, W0q, W0s, Tq=None, Ts=None, Bq=None, Bs=None, bias=None,
+                         Hq=None, Hs=None):
+    """Phase B with SwiGLU, its output H quantized to MXFP8 in the same pass.
+
+    Returns (Hq uint8 [M, N/2], Hs scales), the bytes mx_quantize would make of the
+    bf16 output of mx_lora_up(..., epilogue="swiglu").  N % 256 == 0.
+    """
+    M, N, Kp, rp, ops = _mx_up_operands(Xq, Xs, W0q, W0s, Tq, Ts, Bq, Bs, bias)
+    F = N // 2
+    if Hq is None:
+        Hq = torch.empty((M, F), dtype=torch.uint8, device=Xq.device)
+    if Hs is None:
+        Hs = torch.empty(max(mx_scale_bytes(M, F), 4), dtype=torch.uint8, device=Xq.device)
+    _need(Hq, "Hq", torch.uint8)
+    _need_scales(Hs, "Hs", M, F)
+    st = lib().fsd_mx_lora_up_swiglu_mx(*ops, _ptr(Hq), _ld(Hq), _ptr(Hs), M, N, Kp, rp,
+                                        _stream(Xq))
+    _check("fsd_mx_lora_up_swiglu_mx", st)
+    return Hq, Hs

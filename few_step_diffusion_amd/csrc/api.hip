@@ -156,6 +156,49 @@ inline bool mx_overlaps(const void* Y, int64_t yb, const void* q, int64_t ld, co
          overlap(Y, yb, s, mx_scale_span(rows, Kp));
 }
 
+// Shared checks of the MXFP8 phase-B inputs; `out` / `ob` is the first output
+// (Y, or the E4M3 bytes of H), checked against every input for overlap.
+int validate_mx_up_inputs(const void* Xq, int64_t ldxq, const void* Xs, const void* W0q,
+                          const void* W0s, const void* Tq, int64_t ldtq, const void* Ts,
+                          const void* Bq, const void* Bs, const float* bias, int64_t M,
+                          int64_t N, int64_t K, int64_t r, const void* out, int64_t ob) {
+  if (M < 0 || K < 32 || K % 32 || N < 8 || N % 8 || r < 0 || r % 32) return FSD_EINVAL;
+  if (bias && ((uintptr_t)bias & 3u)) return FSD_EALIGN;
+  const int64_t Kp = round_up(K, 128), rp = round_up(r, 128);
+  int st = validate_mx_operand(Xq, ldxq, Xs, M, Kp, false);
+  if (st == FSD_OK) st = validate_mx_operand(W0q, Kp, W0s, N, Kp, true);
+  if (st == FSD_OK && r > 0) st = validate_mx_operand(Tq, ldtq, Ts, M, rp, false);
+  if (st == FSD_OK && r > 0) st = validate_mx_operand(Bq, rp, Bs, N, rp, true);
+  if (st != FSD_OK) return st;
+  if (mx_overlaps(out, ob, Xq, ldxq, Xs, M, Kp) || mx_overlaps(out, ob, W0q, Kp, W0s, N, Kp) ||
+      overlap(out, ob, bias, bias ? N * 4 : 0))
+    return FSD_EINVAL;
+  if (r > 0 && (mx_overlaps(out, ob, Tq, ldtq, Ts, M, rp) ||
+                mx_overlaps(out, ob, Bq, rp, Bs, N, rp)))
+    return FSD_EINVAL;
+  return FSD_OK;
+}
+
+fsd::GemmParams mx_up_params(const void* Xq, int64_t ldxq, const void* Xs, const void* W0q,
+                             const void* W0s, const void* Tq, int64_t ldtq, const void* Ts,
+                             const void* Bq, const void* Bs, const float* bias, int64_t M,
+                             int64_t N, int64_t K, int64_t r) {
+  const int64_t Kp = round_up(K, 128), rp = round_up(r, 128);
+  fsd::GemmParams p;
+  memset(&p, 0, sizeof(p));
+  p.A0 = Xq; p.lda0 = ldxq; p.sA0 = (const uint8_t*)Xs;
+  p.B0 = W0q; p.ldb0 = Kp;  p.sB0 = (const uint8_t*)W0s;
+  if (r > 0) {
+    p.A1 = Tq; p.lda1 = ldtq; p.sA1 = (const uint8_t*)Ts;
+    p.B1 = Bq; p.ldb1 = rp;   p.sB1 = (const uint8_t*)Bs;
+  }
+  p.M = M; p.N = N; p.K0 = Kp; p.K1 = rp;
+  p.sMp = round_up(M, kTileM); p.sNp = round_up(N, kTileM);
+  p.alpha = 1.0f;
+  p.bias = bias;
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -402,49 +445,55 @@ int fsd_mx_lora_up(const void* Xq, int64_t ldxq, const void* Xs, const void* W0q
                    const void* Bq, const void* Bs, const float* bias, const void* residual,
                    int64_t ldr, void* Y, int64_t ldy, int64_t M, int64_t N, int64_t K,
                    int64_t r, int epilogue, void* stream) {
-  if (M < 0 || K < 32 || K % 32 || N < 8 || N % 8 || r < 0 || r % 32) return FSD_EINVAL;
   if (epilogue != FSD_EPI_NONE && epilogue != FSD_EPI_SWIGLU) return FSD_EINVAL;
   const bool swiglu = epilogue == FSD_EPI_SWIGLU;
-  if (swiglu && N % 16) return FSD_EINVAL;
+  if (N < 8 || (swiglu && N % 16)) return FSD_EINVAL;
   if (swiglu && (N % 128 || residual)) return FSD_EUNSUPPORTED;
   const int64_t nout = swiglu ? N / 2 : N;
   if (!Y || ldy < nout || ldy % 8) return FSD_EINVAL;
   if (residual && (ldr < nout || ldr % 8)) return FSD_EINVAL;
   if (!aligned16(Y) || (residual && !aligned16(residual))) return FSD_EALIGN;
-  if (bias && ((uintptr_t)bias & 3u)) return FSD_EALIGN;
-  const int64_t Kp = round_up(K, 128), rp = round_up(r, 128);
-  int st = validate_mx_operand(Xq, ldxq, Xs, M, Kp, false);
-  if (st == FSD_OK) st = validate_mx_operand(W0q, Kp, W0s, N, Kp, true);
-  if (st == FSD_OK && r > 0) st = validate_mx_operand(Tq, ldtq, Ts, M, rp, false);
-  if (st == FSD_OK && r > 0) st = validate_mx_operand(Bq, rp, Bs, N, rp, true);
-  if (st != FSD_OK) return st;
   const int64_t yb = span_bytes(M, nout, ldy, 2);
-  if (mx_overlaps(Y, yb, Xq, ldxq, Xs, M, Kp) || mx_overlaps(Y, yb, W0q, Kp, W0s, N, Kp) ||
-      overlap(Y, yb, bias, bias ? N * 4 : 0))
-    return FSD_EINVAL;
-  if (r > 0 && (mx_overlaps(Y, yb, Tq, ldtq, Ts, M, rp) || mx_overlaps(Y, yb, Bq, rp, Bs, N, rp)))
-    return FSD_EINVAL;
+  const int st = validate_mx_up_inputs(Xq, ldxq, Xs, W0q, W0s, Tq, ldtq, Ts, Bq, Bs, bias, M, N,
+                                       K, r, Y, yb);
+  if (st != FSD_OK) return st;
   if (residual) {
     const bool same = residual == Y && ldr == ldy;
     if (!same && overlap(Y, yb, residual, span_bytes(M, nout, ldr, 2))) return FSD_EINVAL;
   }
   if (M == 0) return FSD_OK;
-  fsd::GemmParams p;
-  memset(&p, 0, sizeof(p));
-  p.A0 = Xq; p.lda0 = ldxq; p.sA0 = (const uint8_t*)Xs;
-  p.B0 = W0q; p.ldb0 = Kp;  p.sB0 = (const uint8_t*)W0s;
-  if (r > 0) {
-    p.A1 = Tq; p.lda1 = ldtq; p.sA1 = (const uint8_t*)Ts;
-    p.B1 = Bq; p.ldb1 = rp;   p.sB1 = (const uint8_t*)Bs;
-  }
-  p.M = M; p.N = N; p.K0 = Kp; p.K1 = rp;
-  p.sMp = round_up(M, kTileM); p.sNp = round_up(N, kTileM);
-  p.alpha = 1.0f;
-  p.bias = bias;
+  fsd::GemmParams p = mx_up_params(Xq, ldxq, Xs, W0q, W0s, Tq, ldtq, Ts, Bq, Bs, bias, M, N, K, r);
   p.res = (const bf16_t*)residual; p.ldr = ldr;
   p.Y = (bf16_t*)Y; p.ldy = ldy;
   const fsd::GemmKind kind = swiglu ? fsd::GEMM_MX_UP_SWIGLU : fsd::GEMM_MX_UP;
   return from_hip(fsd::launch_gemm(kind, p, as_stream(stream)));
+}
+
+int fsd_mx_lora_up_swiglu_mx(const void* Xq, int64_t ldxq, const void* Xs, const void* W0q,
+                             const void* W0s, const void* Tq, int64_t ldtq, const void* Ts,
+                             const void* Bq, const void* Bs, const float* bias, void* Hq,
+                             int64_t ldhq, void* Hs, int64_t M, int64_t N, int64_t K, int64_t r,
+                             void* stream) {
+  if (N < 16 || N % 16) return FSD_EINVAL;
+  if (N % 256) return FSD_EUNSUPPORTED;
+  const int64_t F = N / 2;
+  if (!Hq || !Hs || ldhq < F || ldhq % 16) return FSD_EINVAL;
+  if (!aligned16(Hq) || ((uintptr_t)Hs & 3u)) return FSD_EALIGN;
+  if (kTileM * ldhq > kMaxOffsetBytes || mx_scale_span(M, F) > kMaxOffsetBytes)
+    return FSD_EUNSUPPORTED;
+  const int64_t hb = span_bytes(M, F, ldhq, 1), hsb = mx_scale_span(M, F);
+  int st = validate_mx_up_inputs(Xq, ldxq, Xs, W0q, W0s, Tq, ldtq, Ts, Bq, Bs, bias, M, N, K, r,
+                                 Hq, hb);
+  if (st == FSD_OK)
+    st = validate_mx_up_inputs(Xq, ldxq, Xs, W0q, W0s, Tq, ldtq, Ts, Bq, Bs, bias, M, N, K, r,
+                               Hs, hsb);
+  if (st != FSD_OK) return st;
+  if (overlap(Hq, hb, Hs, hsb)) return FSD_EINVAL;
+  if (M == 0) return FSD_OK;
+  fsd::GemmParams p = mx_up_params(Xq, ldxq, Xs, W0q, W0s, Tq, ldtq, Ts, Bq, Bs, bias, M, N, K, r);
+  p.Yq = (uint8_t*)Hq; p.ldyq = ldhq;
+  p.Ys = (uint8_t*)Hs; p.sYp = round_up(M, kTileM);
+  return from_hip(fsd::launch_gemm(fsd::GEMM_MX_UP_SWIGLU_MX, p, as_stream(stream)));
 }
 
 }  // extern "C"

@@ -31,6 +31,10 @@ struct GemmParams {
   const uint8_t* sA0; const uint8_t* sB0;
   const uint8_t* sA1; const uint8_t* sB1;
   int64_t sMp, sNp;
+  // SwiGLU -> MXFP8 output (GEMM_MX_UP_SWIGLU_MX): E4M3 bytes [M, N/2] with row
+  // stride ldyq and their scales for sYp (M rounded up to 256) rows
+  uint8_t* Yq; int64_t ldyq;
+  uint8_t* Ys; int64_t sYp;
 };
 
 enum GemmKind {
@@ -39,7 +43,8 @@ enum GemmKind {
   GEMM_UP_SWIGLU = 2,   // phase B with the SwiGLU epilogue
   GEMM_MX_DOWN = 3,     // the same three with MXFP8 operands
   GEMM_MX_UP = 4,
-  GEMM_MX_UP_SWIGLU = 5
+  GEMM_MX_UP_SWIGLU = 5,
+  GEMM_MX_UP_SWIGLU_MX = 6  // ... whose H leaves quantized to MXFP8 (N/2 % 128 == 0)
 };
 
 hipError_t launch_gemm(GemmKind kind, const GemmParams& p, hipStream_t s);

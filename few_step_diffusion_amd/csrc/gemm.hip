@@ -49,6 +49,7 @@
 #include <utility>
 
 #include "fsd_internal.h"
+#include "mx_codec.h"
 
 namespace fsd {
 
@@ -109,7 +110,8 @@ __device__ __forceinline__ void static_for(Fn&& fn) {
 
 // MX: E4M3 operands with E8M0 block scales (v_mfma_scale_f32_16x16x128_f8f6f4):
 // a K step is 128 elements, still one 128-byte line per tile row.
-template <int WM, int WN, bool SWIGLU, bool MX>
+// QOUT (with SWIGLU): H leaves as MXFP8 (E4M3 bytes and scales) instead of bf16.
+template <int WM, int WN, bool SWIGLU, bool MX, bool QOUT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_kernel(GemmParams p) {
   constexpr int ESZ = MX ? 1 : 2;           // bytes per element
@@ -578,6 +580,47 @@ void gemm_kernel(GemmParams p) {
     }
   }
   __builtin_amdgcn_s_waitcnt(0);   // the wave's staged tile is complete (its own region)
+  if constexpr (QOUT) {
+    // SwiGLU -> MXFP8 in one pass: the wave's staged 64 x 64 bf16 tile of H is
+    // two 32-column blocks per row.  Lane l quantizes block l >> 5 of rows
+    // 16·i + l%16, i = 2·((l >> 4) & 1) + k for k = 0, 1, stores its 32 E4M3
+    // bytes, and drops each scale byte into LDS at its place in the scale
+    // layout (byte i of word 16·block + l%16).  The wave's 128 scale bytes are
+    // words 32·wn .. 32·wn + 31 of one (step, 64-row group) region and leave
+    // with one coalesced store.  Rows past M store no elements and scale 127.
+    static_assert(SWIGLU && OC == 64 && OROWS == 64, "one 64-row group, two blocks per wave");
+    uint8_t* sl = (uint8_t*)(lds + kWaves * OROWS * PITCH + wave * 128);
+    static_assert(kWaves * (OROWS * PITCH + 128) <= LDS_BYTES, "scale staging must fit in LDS");
+    const int qb = lane >> 5, qr = lane & 15, qi = (lane >> 4) & 1;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int i = 2 * qi + k;
+      const int row = 16 * i + qr;
+      uint32_t w[16];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const u32x4 v = *(const u32x4*)(ow + row * PITCH + pchunk(row, 4 * qb + c) * 16);
+        w[4 * c] = v.x; w[4 * c + 1] = v.y; w[4 * c + 2] = v.z; w[4 * c + 3] = v.w;
+      }
+      uint32_t q[8];
+      const uint32_t sbyte = mx_block_bf16(w, q);
+      const bool valid = tok0 + row < rows_valid;
+      if (valid) {
+        u32x4* dst = (u32x4*)(p.Yq + (m0 + tok0 + row) * p.ldyq + col0 + 32 * qb);
+        __builtin_nontemporal_store((u32x4){q[0], q[1], q[2], q[3]}, dst);
+        __builtin_nontemporal_store((u32x4){q[4], q[5], q[6], q[7]}, dst + 1);
+      }
+      sl[(16 * qb + qr) * 4 + i] = (uint8_t)(valid ? sbyte : 127u);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    if (lane < 32) {
+      const uint32_t word = *(const uint32_t*)(sl + lane * 4);
+      const int64_t g = (m0 + tok0) >> 6;                 // the wave's 64-row group
+      uint32_t* dst = (uint32_t*)p.Ys + ((int64_t)tn * (p.sYp >> 6) + g) * 64 + 32 * wn + lane;
+      __builtin_nontemporal_store(word, dst);
+    }
+    return;
+  }
   for (int idx = lane; idx < OROWS * OCH; idx += 64) {
     const int row = idx / OCH, pc = idx % OCH;
     const int64_t c = col0 + pchunk(row, pc) * 8;
@@ -588,7 +631,7 @@ void gemm_kernel(GemmParams p) {
   }
 }
 
-template <int WM, int WN, bool SWIGLU, bool MX>
+template <int WM, int WN, bool SWIGLU, bool MX, bool QOUT = false>
 hipError_t launch(const GemmParams& p, hipStream_t s) {
   constexpr int BM = kWaveRows * WM * 32;
   constexpr int TN = (SWIGLU ? 16 : 32) * kWaveCols * WN;
@@ -596,8 +639,8 @@ hipError_t launch(const GemmParams& p, hipStream_t s) {
   const int64_t tiles = ((p.M + BM - 1) / BM) * ((nout + TN - 1) / TN);
   if (tiles <= 0) return hipSuccess;
   if (tiles > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_kernel<WM, WN, SWIGLU, MX>), dim3((unsigned)tiles), dim3(kThreads), 0,
-                     s, p);
+  hipLaunchKernelGGL((gemm_kernel<WM, WN, SWIGLU, MX, QOUT>), dim3((unsigned)tiles),
+                     dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 
@@ -611,6 +654,7 @@ hipError_t launch_gemm(GemmKind kind, const GemmParams& p, hipStream_t s) {
     case GEMM_MX_DOWN: return launch<2, 3, false, true>(p, s);
     case GEMM_MX_UP: return launch<2, 4, false, true>(p, s);
     case GEMM_MX_UP_SWIGLU: return launch<2, 4, true, true>(p, s);
+    case GEMM_MX_UP_SWIGLU_MX: return launch<2, 4, true, true, true>(p, s);
   }
   return hipErrorInvalidValue;
 }

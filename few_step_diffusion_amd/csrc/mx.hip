@@ -22,6 +22,7 @@
 // scale of 1).  That is the order in which the GEMM's 64 lanes take a row
 // block's scales, with one dword serving four 16-row blocks.
 #include "fsd_internal.h"
+#include "mx_codec.h"
 
 namespace fsd {
 
@@ -30,24 +31,6 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
-
-// E4M3 byte of y (finite fp32), nearest-even, saturated to 448.
-__device__ __forceinline__ uint32_t to_e4m3(float y) {
-  const uint32_t u = __float_as_uint(y);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7fffffffu;
-  if (a >= 0x43e00000u) return sign | 0x7eu;          // |y| >= 448
-  if (a >= 0x3c800000u) {                              // |y| >= 2^-6: normal in E4M3
-    uint32_t q = a >> 20;                              // fp32 exponent and top 3 mantissa bits
-    const uint32_t rem = a & 0xfffffu;
-    q += (rem > 0x80000u || (rem == 0x80000u && (q & 1u))) ? 1u : 0u;
-    q -= 120u << 3;                                    // rebias 127 -> 7
-    return sign | (q > 0x7eu ? 0x7eu : q);
-  }
-  // subnormal in E4M3: k·2^-9 with k = nearest-even |y|·2^9 in 0..8 (8 = 2^-6)
-  const uint32_t k = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
-  return sign | k;
-}
 
 __global__ __launch_bounds__(kThreads) void mx_quantize_kernel(const bf16_t* X, int64_t ldx,
                                                                int64_t M, int64_t K, uint8_t* Q,
@@ -64,52 +47,22 @@ __global__ __launch_bounds__(kThreads) void mx_quantize_kernel(const bf16_t* X, 
     *s_out = 127;
     return;
   }
-  uint32_t w[16];                                      // 32 bf16, two per word
+  uint32_t out[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+  uint32_t sbyte = 127u;                               // a block past K: zeros, scale 1
   if (b * 32 < K) {
+    uint32_t w[16];                                    // 32 bf16, two per word
     const u32x4* src = (const u32x4*)(X + m * ldx + b * 32);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const u32x4 v = src[i];
       w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
     }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) w[i] = 0u;
-  }
-  // amax of the block from the bf16 bit patterns (exact in fp32)
-  uint32_t amax = 0;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const uint32_t lo = (w[i] << 16) & 0x7fffffffu, hi = w[i] & 0x7fff0000u;
-    amax = lo > amax ? lo : amax;
-    amax = hi > amax ? hi : amax;
-  }
-  int e = -127;
-  if (b * 32 >= K) {
-    e = 0;                                             // padded block: zeros, scale 1
-  } else if (amax != 0) {
-    const int ex = (int)(amax >> 23) - 127;            // floor(log2) for normal amax
-    e = ex - 8;
-    if (e < -127) e = -127;                            // (subnormal amax lands here too)
-    if (e > 127) e = 127;
-  }
-  const float inv = __uint_as_float((uint32_t)(127 - e) << 23);   // 2^-e, exact
-  uint32_t out[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    uint32_t word = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int idx = 4 * i + j;                       // element index in the block
-      const uint32_t bits = (idx & 1) ? (w[idx >> 1] & 0xffff0000u) : (w[idx >> 1] << 16);
-      word |= to_e4m3(__uint_as_float(bits) * inv) << (8 * j);
-    }
-    out[i] = word;
+    sbyte = mx_block_bf16(w, out);
   }
   u32x4* dst = (u32x4*)(Q + m * ldq + b * 32);
   dst[0] = (u32x4){out[0], out[1], out[2], out[3]};
   dst[1] = (u32x4){out[4], out[5], out[6], out[7]};
-  *s_out = (uint8_t)(e + 127);
+  *s_out = (uint8_t)sbyte;
 }
 
 }  // namespace

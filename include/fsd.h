@@ -248,7 +248,16 @@ int fsd_token_head_euler(const void* H, int64_t ldh, const void* P, float* z,
  *   N rows), rp = r rounded up to 128.  r a multiple of 32 (0: no LoRA term;
  *   Tq, Ts, Bq, Bs unused).  bias, residual, Y, ldy, epilogue as for
  *   fsd_lora_up; SwiGLU needs N a multiple of 128 (else FSD_EUNSUPPORTED).
- * In both, code arrays are 16-byte aligned with row strides multiples of 16,
+ * fsd_mx_lora_up_swiglu_mx: fsd_mx_lora_up with the SwiGLU epilogue whose
+ *   output leaves as MXFP8 in the same pass: H = SwiGLU(...) is rounded to
+ *   bf16 (exactly what fsd_mx_lora_up writes) and quantized as
+ *   fsd_mx_quantize would quantize it, so the bytes equal those of the two
+ *   calls in sequence.  Hq [M, F] E4M3 (F = N/2, row stride ldhq >= F,
+ *   multiple of 16), Hs its scales for M rows of F; N a multiple of 256
+ *   (else FSD_EUNSUPPORTED); no residual.  The pages fuse SwiGLU with the
+ *   activation quantizer ([EN] inference-configuration table, "Fused SwiGLU +
+ *   MXFP8 quantizer").
+ * In all three, code arrays are 16-byte aligned with row strides multiples of 16,
  * scale arrays 4-byte aligned; a weight operand must span less than 2 GiB with
  * 256 extra rows, an activation operand's 256-row tile likewise, and every
  * scale array less than 2 GiB (else FSD_EUNSUPPORTED). */
@@ -264,6 +273,12 @@ int fsd_mx_lora_up(const void* Xq, int64_t ldxq, const void* Xs, const void* W0q
                    const void* residual, int64_t ldr, void* Y, int64_t ldy,
                    int64_t M, int64_t N, int64_t K, int64_t r, int epilogue,
                    void* stream);
+int fsd_mx_lora_up_swiglu_mx(const void* Xq, int64_t ldxq, const void* Xs,
+                             const void* W0q, const void* W0s, const void* Tq,
+                             int64_t ldtq, const void* Ts, const void* Bq,
+                             const void* Bs, const float* bias, void* Hq,
+                             int64_t ldhq, void* Hs, int64_t M, int64_t N,
+                             int64_t K, int64_t r, void* stream);
 
 #ifdef __cplusplus
 }

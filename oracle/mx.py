@@ -120,35 +120,52 @@ def dequantize_rows(q, s, K):
 _E4M3_TABLE = np.array([e4m3_value(b) if (b & 0x7F) != 0x7F else 0.0 for b in range(256)])
 
 
-def quantize_rows_np(X):
-    """quantize_rows for K a multiple of 32, as array operations."""
+def e4m3_round_np(y):
+    """e4m3_round over an array (float64 in, float64 out)."""
+    y = np.asarray(y, dtype=np.float64)
+    a = np.abs(y)
+    _, ey = np.frexp(a)                             # a = m·2^ey, 0.5 <= m < 1
+    binade = np.maximum(ey.astype(np.int64) - 1, E4M3_EMIN)
+    quantum = np.ldexp(1.0, binade - 3)
+    v = np.minimum(np.rint(a / quantum) * quantum, E4M3_MAX)   # nearest-even, saturated
+    return np.copysign(v, y)
+
+
+def block_exponents_np(X):
+    """block_exponent of every 32-element block of the rows of X: int64 [rows, K/32]."""
     X = np.asarray(X, dtype=np.float64)
     rows, K = X.shape
     if K % MX_BLOCK:
         raise ValueError("K must be a multiple of 32")
-    Kp = (K + 127) // 128 * 128
-    blk = X.reshape(rows, K // MX_BLOCK, MX_BLOCK)
-    amax = np.abs(blk).max(axis=2)
+    amax = np.abs(X.reshape(rows, K // MX_BLOCK, MX_BLOCK)).max(axis=2)
     _, ex = np.frexp(amax)                          # amax = m·2^ex, 0.5 <= m < 1
     e = np.clip(ex.astype(np.int64) - 1 - E4M3_EMAX, -127, 127)
-    e = np.where(amax == 0.0, -127, e)
-    y = np.ldexp(blk, -e[..., None])                # exact: a power-of-two scaling
-    a = np.abs(y)
-    _, ey = np.frexp(a)
-    binade = np.maximum(ey.astype(np.int64) - 1, E4M3_EMIN)
-    quantum = np.ldexp(1.0, binade - 3)
-    v = np.minimum(np.rint(a / quantum) * quantum, E4M3_MAX)   # nearest-even, saturated
-    # bytes of the rounded magnitudes
-    _, ev = np.frexp(v)
+    return np.where(amax == 0.0, -127, e)
+
+
+def e4m3_bits_np(v):
+    """e4m3_bits over an array of E4M3-representable values."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    _, ev = np.frexp(a)
     ev = ev.astype(np.int64) - 1
-    normal = v >= math.ldexp(1.0, E4M3_EMIN)
+    normal = a >= math.ldexp(1.0, E4M3_EMIN)
     ev_n = np.where(normal, ev, 0)
-    mant_n = (np.ldexp(v, -ev_n) - 1.0) * 8.0
+    mant_n = (np.ldexp(a, -ev_n) - 1.0) * 8.0
     code_n = ((ev_n + 7) << 3) | mant_n.astype(np.int64)
-    code_s = (v / math.ldexp(1.0, E4M3_EMIN - 3)).astype(np.int64)
-    code = np.where(normal, code_n, code_s) | np.where(np.signbit(y), 0x80, 0)
+    code_s = (a / math.ldexp(1.0, E4M3_EMIN - 3)).astype(np.int64)
+    return (np.where(normal, code_n, code_s) | np.where(np.signbit(v), 0x80, 0)).astype(np.uint8)
+
+
+def quantize_rows_np(X):
+    """quantize_rows for K a multiple of 32, as array operations."""
+    X = np.asarray(X, dtype=np.float64)
+    rows, K = X.shape
+    Kp = (K + 127) // 128 * 128
+    e = block_exponents_np(X)
+    y = np.ldexp(X, -np.repeat(e, MX_BLOCK, axis=1))   # exact: power-of-two scaling
     q = np.zeros((rows, Kp), np.uint8)
-    q[:, :K] = code.reshape(rows, K).astype(np.uint8)
+    q[:, :K] = e4m3_bits_np(e4m3_round_np(y))
     s = np.full((rows, Kp // MX_BLOCK), 127, np.uint8)
     s[:, :K // MX_BLOCK] = (e + 127).astype(np.uint8)
     return q, s

@@ -207,6 +207,29 @@ def test_mx_validation(L):
     assert upm(Y=P(BASE + 7 * 0x10000000 + 4096)) == EINVAL   # Y overlaps Bq
     assert upm(M=0, res=a(9), ldr=1024) == OK            # in-place residual is legal
 
+    def upq(**kw):
+        args = dict(Xq=a(1), ldxq=1024, Xs=a(2), Wq=a(3), Ws=a(4), Tq=a(5), ldtq=640, Ts=a(6),
+                    Bq=a(7), Bs=a(8), bias=None, Hq=a(9), ldhq=512, Hs=a(10), M=300, N=1024,
+                    K=1024, r=576)
+        args.update(kw)
+        return L.fsd_mx_lora_up_swiglu_mx(args["Xq"], args["ldxq"], args["Xs"], args["Wq"],
+                                          args["Ws"], args["Tq"], args["ldtq"], args["Ts"],
+                                          args["Bq"], args["Bs"], args["bias"], args["Hq"],
+                                          args["ldhq"], args["Hs"], args["M"], args["N"],
+                                          args["K"], args["r"], None)
+    assert upq(M=0) == OK
+    assert upq(N=1152) == EUNSUP                         # fused quantizer: N % 256 == 0
+    assert upq(N=1032) == EINVAL
+    assert upq(ldhq=500) == EINVAL                       # ldhq < N/2
+    assert upq(ldhq=520) == EINVAL                       # ldhq % 16
+    assert upq(Hs=None) == EINVAL
+    assert upq(Hs=P(BASE + 10 * 0x10000000 + 2)) == EALIGN
+    assert upq(Hq=P(BASE + 9 * 0x10000000 + 8)) == EALIGN
+    assert upq(Hs=P(BASE + 9 * 0x10000000 + 4096)) == EINVAL   # Hs overlaps Hq
+    assert upq(Hq=P(BASE + 0x10000000 + 4096)) == EINVAL       # Hq overlaps Xq
+    assert upq(Hs=P(BASE + 4 * 0x10000000 + 64)) == EINVAL     # Hs overlaps W0s
+    assert upq(r=40) == EINVAL
+
 
 def test_mx_scale_layout_helpers():
     """The host pack / unpack helpers follow the documented layout: byte i of word

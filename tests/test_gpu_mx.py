@@ -147,3 +147,77 @@ def test_mx_chain_through_quantizer(gpu):
     Td = mx.dequantize_rows_np(qt, st, qt.shape[1])
     ref = oracle.lora_linear_rows(np.hstack([Xd, Td]), np.hstack([Wd, Bd]), None, None)
     assert_gemm(Y, ref, "chain Y")
+
+
+# ------------------------------------------------------- fused SwiGLU -> MXFP8
+def bf16_round(a):
+    return oracle.bf16_value(oracle.bf16_bits(np.asarray(a, np.float32))).reshape(
+        np.shape(a)).astype(np.float64)
+
+
+def assert_mx_valid(Hq, Hs, h, dh, what):
+    """GPU MXFP8 of H against the exact H (fp64) and a bound dh on the GPU's fp32 error.
+
+    The GPU rounds its fp32 H to bf16 and quantizes that; since every step is
+    monotone, its bf16 value lies in [bf16(h - dh), bf16(h + dh)].  So each block's
+    scale must be one that the block's amax can take over that interval, and each
+    code, under the GPU's scale, must lie between the E4M3 roundings of the
+    interval's ends.  Padding rows of the scale array must hold 127.
+    """
+    M, F = h.shape
+    lo, hi = bf16_round(h - dh), bf16_round(h + dh)
+    s_all = fsd.mx_unpack_scales(Hs, (M + 255) // 256 * 256, F)
+    assert np.all(s_all[M:] == 127), "padding rows of the scale array"
+    e_gpu = s_all[:M].astype(np.int64) - 127
+    straddle = (lo <= 0) & (hi >= 0)
+    mag_min = np.where(straddle, 0.0, np.minimum(np.abs(lo), np.abs(hi)))
+    mag_max = np.maximum(np.abs(lo), np.abs(hi))
+    e_lo, e_hi = mx.block_exponents_np(mag_min), mx.block_exponents_np(mag_max)
+    bad = (e_gpu < e_lo) | (e_gpu > e_hi)
+    assert not bad.any(), (what, "scale", np.argwhere(bad)[:5])
+    E = np.repeat(e_gpu, 32, axis=1)
+    v_lo = mx.e4m3_round_np(np.ldexp(lo, -E))
+    v_hi = mx.e4m3_round_np(np.ldexp(hi, -E))
+    q = Hq.cpu().numpy()
+    v = mx.dequantize_rows_np(q, np.full((M, F // 32), 127, np.uint8), F)   # unscaled E4M3
+    bad = (v < v_lo) | (v > v_hi)
+    assert not bad.any(), (what, "codes", np.argwhere(bad)[:5])
+    q_ref, s_ref = mx.quantize_rows_np(bf16_round(h))
+    say(f"{what}: scales equal to the oracle's {np.mean(s_all[:M] == s_ref):.6f}, "
+        f"codes equal {np.mean(q == q_ref):.6f}, codes with a two-code interval "
+        f"{np.mean(v_lo != v_hi):.4f}")
+
+
+@pytest.mark.parametrize("M,N,K,r,bias", [(300, 512, 1024, 576, True), (1, 256, 256, 0, False),
+                                          (513, 768, 384, 64, False)])
+def test_mx_swiglu_quantize_epilogue(gpu, M, N, K, r, bias):
+    say(f"mx fused swiglu->mx M={M} N={N} K={K} r={r} bias={bias}")
+    rng = np.random.default_rng(M + N + K + r)
+    Qx, Sx, Xd = mx_operand(rng.standard_normal((M, K)), gpu)
+    Qw, Sw, Wd = mx_operand(rng.standard_normal((N, K)) * 0.04, gpu)
+    if r:
+        Qt, St, Td = mx_operand(rng.standard_normal((M, r)) * 0.3, gpu)
+        Qb, Sb, Bd = mx_operand(rng.standard_normal((N, r)) * 0.02, gpu)
+        Xcat, Wcat = np.hstack([Xd, Td]), np.hstack([Wd, Bd])
+    else:
+        Qt = St = Qb = Sb = None
+        Xcat, Wcat = Xd, Wd
+    b = rng.standard_normal(N).astype(np.float32) * 0.1 if bias else None
+    bt = None if b is None else torch.from_numpy(b).to(gpu)
+    Hq, Hs = fsd.mx_lora_up_swiglu_mx(Qx, Sx, Qw, Sw, Qt, St, Qb, Sb, bias=bt)
+    # the same bytes as the unfused route: bf16 SwiGLU output, then the quantizer
+    H = fsd.mx_lora_up(Qx, Sx, Qw, Sw, Qt, St, Qb, Sb, bias=bt, epilogue="swiglu")
+    Hq2, Hs2 = fsd.mx_quantize(H)
+    assert torch.equal(Hq, Hq2) and torch.equal(Hs, Hs2), "fused != unfused"
+    F = N // 2
+    h = oracle.lora_linear_rows(Xcat, Wcat, None, None, bias=b, swiglu=True)
+    # error bound of the GPU's fp32 H: recursive-summation bound n·2^-24 on each
+    # sum of |terms| (exact fp8 products), silu' <= 1.1, a few ulps for silu itself
+    gu = oracle.lora_linear_rows(Xcat, Wcat, None, None, bias=b)
+    gu_abs = oracle.lora_linear_rows(np.abs(Xcat), np.abs(Wcat), None, None,
+                                     bias=None if b is None else np.abs(b))
+    g, u = gu[:, :F], gu[:, F:]
+    c = Xcat.shape[1] * 2.0 ** -24
+    dh = (1.1 * c * gu_abs[:, :F] * np.abs(u) + np.abs(g / (1 + np.exp(-g))) * c * gu_abs[:, F:]
+          + 2.0 ** -20 * np.abs(h) + 1e-30)
+    assert_mx_valid(Hq, Hs, h, dh, f"fused swiglu->mx M={M} N={N}")
