@@ -31,17 +31,26 @@ class StandinRefiner:
 
     def __init__(self, M: int, device="cuda:0", wid: int = 4, D: int = inputs.STANDIN_D,
                  F: int = inputs.STANDIN_F, ranks=inputs.RANKS, C: int = inputs.LATENT_C,
-                 scale: float = 1.0):
+                 scale: float = 1.0, mx: bool = False):
+        """mx: run the four linears as MXFP8 GEMMs.  The bf16 weights are quantized
+        once here; each linear quantizes its bf16 input and its bf16 LoRA down output,
+        and the gate/up GEMM hands SwiGLU's output to the down projection already
+        quantized."""
         dev = torch.device(device)
         self.M, self.D, self.F, self.C, self.dev = M, D, F, C, dev
         self.R = sum(ranks)
         self.scale = scale
+        self.mx = mx
         self.layers = []
         for L in inputs.standin_layers(wid, D, F, ranks):
             A, B = fsd.lora_merge([a.to(dev) for a in L["A_list"]],
                                   [b.to(dev) for b in L["B_list"]])
-            self.layers.append({"W0": L["W0"].to(dev), "A": A, "B": B,
-                                "K": L["K"], "N": L["N"]})
+            layer = {"W0": L["W0"].to(dev), "A": A, "B": B, "K": L["K"], "N": L["N"]}
+            if mx:
+                layer["W0q"] = fsd.mx_quantize(layer.pop("W0"))
+                layer["Aq"] = fsd.mx_quantize(layer.pop("A"))
+                layer["Bq"] = fsd.mx_quantize(layer.pop("B"))
+            self.layers.append(layer)
         E, P = inputs.standin_projections(wid, C, D)
         self.E, self.P = E.to(dev), P.to(dev)
         bf = torch.bfloat16
@@ -51,6 +60,16 @@ class StandinRefiner:
         self.T = torch.empty((M, self.R), dtype=bf, device=dev)      # LoRA down output
         self.v = torch.empty((M, C), dtype=torch.float32, device=dev)
         self.z = torch.empty((M, C), dtype=torch.float32, device=dev)
+        if mx:
+            u8 = torch.uint8
+            mxbuf = lambda K: (torch.empty((M, fsd.mx_padded_k(K)), dtype=u8, device=dev),
+                               torch.empty(max(fsd.mx_scale_bytes(M, K), 4), dtype=u8,
+                                           device=dev))
+            self.hq = mxbuf(D)           # linear inputs: h, then V
+            self.vq = mxbuf(D)
+            self.gq = mxbuf(F)           # SwiGLU output, quantized by the gate/up GEMM
+            self.tq = mxbuf(self.R)      # LoRA down output
+            del self.g
         self.events = None
 
     # one LoRA linear = phase A + phase B (two kernels)
@@ -68,15 +87,48 @@ class StandinRefiner:
             ev.record()
             self.events.append((name, ev))
 
-    def velocity(self):
-        """v = stand-in(z) for the current latent self.z."""
+    # one MXFP8 LoRA linear: phase A, quantize T, phase B (SwiGLU -> MXFP8 for gate/up)
+    def _mx_linear(self, idx, Xmx, out=None, residual=None, swiglu_mx=False):
+        L = self.layers[idx]
+        name = self.LAYER_NAMES[idx]
+        T = self.T[: Xmx[0].shape[0]]
+        self._mark(f"{name}.down")
+        fsd.mx_lora_down(*Xmx, *L["Aq"], self.scale, T)
+        self._mark(f"{name}.quant_t")
+        fsd.mx_quantize(T, *self.tq)
+        self._mark(f"{name}.up")
+        if swiglu_mx:
+            fsd.mx_lora_up_swiglu_mx(*Xmx, *L["W0q"], *self.tq, *L["Bq"], Hq=self.gq[0],
+                                     Hs=self.gq[1])
+        else:
+            fsd.mx_lora_up(*Xmx, *L["W0q"], *self.tq, *L["Bq"], residual=residual, out=out)
+
+    def _quantize(self, name, X, buf):
+        self._mark(name)
+        fsd.mx_quantize(X, *buf)
+        return buf
+
+    def _blocks(self):
+        """embed, then the four linears; leaves the block output in self.h."""
         D = self.D
         self._mark("embed")
         fsd.token_embed(self.z, self.E, out=self.h)
-        self._linear(0, self.h, self.qkv)
-        self._linear(1, self.qkv[:, 2 * D:3 * D], self.h, residual=self.h)
-        self._linear(2, self.h, self.g, epilogue=fsd.EPI_SWIGLU)
-        self._linear(3, self.g, self.h, residual=self.h)
+        if self.mx:
+            self._mx_linear(0, self._quantize("qkv.quant_x", self.h, self.hq), self.qkv)
+            V = self.qkv[:, 2 * D:3 * D]
+            self._mx_linear(1, self._quantize("o.quant_x", V, self.vq), self.h, residual=self.h)
+            self._mx_linear(2, self._quantize("gate_up.quant_x", self.h, self.hq),
+                            swiglu_mx=True)
+            self._mx_linear(3, self.gq, self.h, residual=self.h)
+        else:
+            self._linear(0, self.h, self.qkv)
+            self._linear(1, self.qkv[:, 2 * D:3 * D], self.h, residual=self.h)
+            self._linear(2, self.h, self.g, epilogue=fsd.EPI_SWIGLU)
+            self._linear(3, self.g, self.h, residual=self.h)
+
+    def velocity(self):
+        """v = stand-in(z) for the current latent self.z."""
+        self._blocks()
         self._mark("head")
         fsd.token_head(self.h, self.P, out=self.v)
         return self.v
@@ -84,13 +136,7 @@ class StandinRefiner:
     def velocity_euler(self, sigma, sigma_next):
         """The velocity with the Euler update fused into the head: z += (sigma_next - sigma)·v
         without v going through HBM (bitwise equal to velocity() then euler_step)."""
-        D = self.D
-        self._mark("embed")
-        fsd.token_embed(self.z, self.E, out=self.h)
-        self._linear(0, self.h, self.qkv)
-        self._linear(1, self.qkv[:, 2 * D:3 * D], self.h, residual=self.h)
-        self._linear(2, self.h, self.g, epilogue=fsd.EPI_SWIGLU)
-        self._linear(3, self.g, self.h, residual=self.h)
+        self._blocks()
         self._mark("head_euler")
         fsd.token_head_euler(self.h, self.P, self.z, sigma, sigma_next)
         return self.z

@@ -176,3 +176,70 @@ def dequantize_rows_np(q, s, K):
     q = np.asarray(q)[:, :K]
     sc = np.asarray(s, dtype=np.int64)[:, np.arange(K) // MX_BLOCK] - 127
     return np.ldexp(_E4M3_TABLE[q], sc)
+
+
+# ------------------------------------------------------- MXFP8 stand-in velocity
+# The velocity stand-in of the refine loop (see standin_velocity in this
+# package) with its four linears run as MXFP8 GEMMs, at the quantization points
+# the pages' MXFP8 inference path implies: activations live in bf16 between
+# operations and are quantized at each linear's input, the LoRA down output T
+# is rounded to bf16 and quantized before the up projection, SwiGLU's bf16
+# output is quantized for the down projection, and the weights (W0, A, B) are
+# quantized once from their bf16 values.  Sums are exact (fp64 matmul of the
+# dequantized values); every bf16 rounding is nearest-even.
+def bf16_round_np(x):
+    """Nearest-even bfloat16 value of float32(x), as float64 (x finite)."""
+    f = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    b = f.view(np.uint32).astype(np.uint64)
+    r = (((b + 0x7FFF + ((b >> 16) & 1)) >> 16) << 16).astype(np.uint32)
+    return r.view(np.float32).astype(np.float64)
+
+
+def mx_values(X):
+    """Dequantized MXFP8 of the rows of X ([rows, K], K a multiple of 32)."""
+    X = np.asarray(X, dtype=np.float64)
+    q, s = quantize_rows_np(X)
+    return dequantize_rows_np(q, s, X.shape[1])
+
+
+def standin_mx_weights(layers):
+    """(W0, A, B) of each layer as dequantized MXFP8 (from their bf16 values) plus scale."""
+    out = []
+    for L in layers:
+        out.append({"W0": mx_values(L["W0"]), "A": mx_values(L["A"]), "B": mx_values(L["B"]),
+                    "scale": float(L.get("scale", 1.0))})
+    return out
+
+
+def _mx_linear(Xb, L):
+    Xd = mx_values(Xb)
+    T = bf16_round_np(L["scale"] * (Xd @ L["A"].T))
+    return Xd @ L["W0"].T + mx_values(T) @ L["B"].T
+
+
+def standin_velocity_mx(z, E, P, wq):
+    """Velocity of float64 latent rows z [T, C]; E [D, C], P [C, D]; wq from
+    standin_mx_weights (qkv, o, gate/up, down).  Returns float64 [T, C]."""
+    z = np.asarray(z, dtype=np.float64)
+    E = np.asarray(E, dtype=np.float64)
+    P = np.asarray(P, dtype=np.float64)
+    D = E.shape[0]
+    F = wq[3]["W0"].shape[1]
+    h = bf16_round_np(z @ E.T)
+    qkv = bf16_round_np(_mx_linear(h, wq[0]))
+    h = bf16_round_np(_mx_linear(qkv[:, 2 * D:3 * D], wq[1]) + h)
+    y = _mx_linear(h, wq[2])
+    gate, up = y[:, :F], y[:, F:]
+    g = bf16_round_np(gate / (1.0 + np.exp(-gate)) * up)
+    h = bf16_round_np(_mx_linear(g, wq[3]) + h)
+    return h @ P.T
+
+
+def standin_refine_mx(x0, eps, E, P, wq, sigmas):
+    """Renoise at sigmas[0], then one MXFP8 stand-in velocity and Euler step per
+    sigma pair (fp64 latent).  Returns the final latent [T, C]."""
+    from . import euler_step, renoise
+    z = renoise(x0, eps, sigmas[0])
+    for k in range(len(sigmas) - 1):
+        z = euler_step(z, standin_velocity_mx(z, E, P, wq), sigmas[k], sigmas[k + 1])
+    return z

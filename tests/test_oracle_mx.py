@@ -112,3 +112,88 @@ def test_array_form_matches_element_loops():
     sc = np.array([[120, 127, 134, 2, 250, 127, 64]], np.uint8)
     assert np.array_equal(mx.dequantize_rows(codes, sc, 224),
                           mx.dequantize_rows_np(codes, sc, 224))
+
+
+def test_bf16_round_matches_the_c_oracle():
+    import oracle
+    rng = np.random.default_rng(8)
+    x = np.concatenate([rng.standard_normal(2000) * np.exp(rng.standard_normal(2000) * 6),
+                        # exact bf16 ties (even and odd) and their neighbours
+                        np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(1.0 + 2.0 ** -8),
+                                  1.0 + 2.0 ** -8 + 2.0 ** -20, 0.0, -0.0, 3.0e38])])
+    ref = oracle.bf16_value(oracle.bf16_bits(x.astype(np.float32))).astype(np.float64)
+    got = mx.bf16_round_np(x)
+    assert np.array_equal(got, ref)
+    assert np.array_equal(np.signbit(got), np.signbit(ref))
+
+
+def _tiny_standin(seed=3, T=3, C=4, D=32, F=64, r=32):
+    rng = np.random.default_rng(seed)
+    bf = mx.bf16_round_np
+    layers = []
+    for K, N in [(D, 3 * D), (D, D), (D, 2 * F), (F, D)]:
+        layers.append({"W0": bf(rng.standard_normal((N, K)) * 0.2),
+                       "A": bf(rng.standard_normal((r, K)) / math.sqrt(K)),
+                       "B": bf(rng.standard_normal((N, r)) * 0.1), "scale": 0.5})
+    E = bf(rng.standard_normal((D, C)))
+    P = bf(rng.standard_normal((C, D)) * 0.05)
+    z = rng.standard_normal((T, C))
+    return z, E, P, layers
+
+
+def test_mx_standin_velocity_by_element_loops():
+    """The array-form MXFP8 stand-in against the same data flow written with the
+    element-loop quantizer and explicit loops for every product (tiny shapes)."""
+    z, E, P, layers = _tiny_standin()
+    T, C = z.shape
+    D = E.shape[0]
+    F = layers[3]["W0"].shape[1]
+    bf = mx.bf16_round_np
+
+    def qd(X):                                   # element-loop quantize + dequantize
+        q, s = mx.quantize_rows(X)
+        return mx.dequantize_rows(q, s, X.shape[1])
+
+    def matT(X, W):                              # X·Wᵀ by loops
+        out = np.zeros((X.shape[0], W.shape[0]))
+        for i in range(X.shape[0]):
+            for j in range(W.shape[0]):
+                out[i, j] = sum(X[i, k] * W[j, k] for k in range(X.shape[1]))
+        return out
+
+    def lin(X, L):
+        Xd = qd(X)
+        Td = qd(bf(L["scale"] * matT(Xd, qd(L["A"]))))
+        return matT(Xd, qd(L["W0"])) + matT(Td, qd(L["B"]))
+
+    h = bf(matT(z, E))
+    qkv = bf(lin(h, layers[0]))
+    h = bf(lin(qkv[:, 2 * D:], layers[1]) + h)
+    y = lin(h, layers[2])
+    g = np.zeros((T, F))
+    for i in range(T):
+        for j in range(F):
+            a, b = y[i, j], y[i, F + j]
+            g[i, j] = a / (1.0 + math.exp(-a)) * b
+    h = bf(lin(bf(g), layers[3]) + h)
+    v_ref = matT(h, P)
+    v = mx.standin_velocity_mx(z, E, P, mx.standin_mx_weights(layers))
+    assert np.allclose(v, v_ref, rtol=1e-12, atol=1e-12)
+
+
+def test_mx_standin_velocity_within_the_mxfp8_budget_of_the_exact_one():
+    """Against the exact fp64 stand-in (the C oracle): quantizing every linear's
+    operands to MXFP8 (about 3% RMS per element, four chained linears and a
+    SwiGLU at this small width) moves the velocity by roughly 10-15% of its
+    norm, never by nothing, while a gross slip - the LoRA path dropped (half the
+    output here), a wrong slice or residual - moves it by far more."""
+    import oracle
+    z, E, P, layers = _tiny_standin(seed=4, T=64, D=64, F=128)
+    layers = [dict(L, scale=1.0, B=mx.bf16_round_np(L["B"] * 2)) for L in layers]
+    v = oracle.standin_velocity(z, E, P, layers)
+    v_mx = mx.standin_velocity_mx(z, E, P, mx.standin_mx_weights(layers))
+    err = np.linalg.norm(v_mx - v) / np.linalg.norm(v)
+    assert 0.01 < err < 0.25, err
+    no_lora = [dict(L, scale=0.0) for L in layers]
+    v_drop = mx.standin_velocity_mx(z, E, P, mx.standin_mx_weights(no_lora))
+    assert np.linalg.norm(v_drop - v) / np.linalg.norm(v) > 0.5
