@@ -15,6 +15,11 @@ Prints ONE JSON line on stdout (everything else goes to stderr):
   elementwise  renoise / Euler GB/s at the 768P, 2K and 4K latents, 12 bytes
              per element, cache-cold (a 1 GiB read between repetitions) and
              warm; median / min / max of 20 after 5 warm-ups
+  graph_fused  the step as one replayed HIP graph per sampler step with the
+             Euler update fused into the head
+  mxfp8      the step with the four linears as MXFP8 GEMMs (quantizers in the
+             step time), the fused SwiGLU->MXFP8 gate/up GEMM against the
+             5000 TFLOP/s fp8 peak
   cpu_baseline the fp64 oracle on a bounded sample of tokens on host cores
 """
 from __future__ import annotations
@@ -31,6 +36,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA (MXFP8 scaled MFMA included)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 DOMINANT = "gate_up.up"
 SPIN_CYCLES = 200_000          # ~0.1 ms GPU spin queued ahead of a timed region
@@ -49,6 +55,7 @@ def parse():
     ap.add_argument("--no-elementwise", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target host time of the oracle sample")
+    ap.add_argument("--no-mx", action="store_true", help="skip the MXFP8 step")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 1 GiB device copy first (a known-size kernel for counters)")
     return ap.parse_args()
@@ -58,23 +65,23 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_swiglu_2k_pmc_traffic.md")
 GEMM_SOURCE = os.path.join(ROOT, "few_step_diffusion_amd", "csrc", "gemm.hip")
 
 
-def measured_traffic():
-    """HBM-side bytes per launch of the dominant kernel from the committed
-    rocprofv3 FETCH_SIZE / WRITE_SIZE summary, or None when the GEMM source has
-    changed since those counters were taken."""
+def measured_traffic(kernel):
+    """HBM-side bytes per launch of `kernel` (a gemm_kernel template signature)
+    from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary, or None when
+    the GEMM source has changed since those counters were taken."""
     import hashlib
     try:
         fields = {}
         with open(TRAFFIC_FILE) as f:
             for line in f:
                 key, sep, val = line.strip().partition(": ")
-                if sep and key in ("source_sha256", "bytes_per_launch"):
+                if sep:
                     fields[key] = val.strip()
         with open(GEMM_SOURCE, "rb") as f:
             cur = hashlib.sha256(f.read()).hexdigest()
         if fields.get("source_sha256") != cur:
             return None
-        return int(float(fields["bytes_per_launch"]))
+        return int(float(fields["bytes_per_launch " + kernel]))
     except (OSError, KeyError, ValueError):
         return None
 
@@ -170,6 +177,59 @@ def cpu_baseline(model_flops_per_token, target_s):
                       f"velocity evaluations + Euler), fp64, {dt:.1f} s"}
 
 
+def mx_step(torch, M, u, eps, flops, bf16_ms, args):
+    """The same refine with the four linears as MXFP8 GEMMs (quantizers included in
+    the step time); per-kernel times and the fused SwiGLU->MXFP8 gate/up GEMM
+    against the fp8 MFMA peak."""
+    from few_step_diffusion_amd.refine import StandinRefiner
+    model = StandinRefiner(M, device=u.device, mx=True)
+    for _ in range(max(1, args.warmup)):
+        model.refine(u, eps)
+    torch.cuda.synchronize()
+    step_events = []
+    torch.cuda._sleep(SPIN_CYCLES)
+    for _ in range(args.steps):
+        model.events = []
+        model.refine(u, eps)
+        step_events.append(model.events)
+    torch.cuda.synchronize()
+    model.events = None
+    step_ms, per_kernel = [], {}
+    for ev in step_events:
+        step_ms.append(ev[0][1].elapsed_time(ev[-1][1]))
+        for k, v in kernel_times(ev).items():
+            per_kernel.setdefault(k, []).extend(v)
+    ms = statistics.mean(step_ms)
+    total = sum(flops.values())
+    kernels = {}
+    for name, ts in per_kernel.items():
+        ent = {"launches_per_step": len(ts) // args.steps,
+               "mean_us": round(statistics.mean(ts) * 1e3, 1),
+               "median_us": round(statistics.median(ts) * 1e3, 1)}
+        if name in flops:
+            ent["tflops"] = round(flops[name] / 3 / (statistics.mean(ts) * 1e-3) / 1e12, 1)
+            ent["frac_fp8_peak"] = round(ent["tflops"] / PEAK_FP8_TFLOPS, 4)
+        kernels[name] = ent
+    lin = [k for k in per_kernel if k.split(".")[0] in StandinRefiner.LAYER_NAMES]
+    lin_ms = sum(statistics.mean(per_kernel[k]) * len(per_kernel[k]) / args.steps for k in lin)
+    lin_flops = sum(v for k, v in flops.items() if k.endswith(".down") or k.endswith(".up"))
+    dom = kernels["gate_up.up"]
+    log(f"MXFP8 step {ms:.2f} ms (bf16 {bf16_ms:.2f} ms)")
+    del model
+    return {"ms_per_step": round(ms, 3), "tflops": round(total / (ms * 1e-3) / 1e12, 1),
+            "speedup_vs_bf16": round(bf16_ms / ms, 3),
+            "linears": {"ms_per_step": round(lin_ms, 3),
+                        "tflops": round(lin_flops / (lin_ms * 1e-3) / 1e12, 1),
+                        "note": "phase A + phase B + activation and T quantizers"},
+            "dominant": {"kernel": "gate/up phase B, MXFP8 operands, SwiGLU -> MXFP8 epilogue",
+                         "bound": "mfma", "achieved": dom["tflops"], "peak": PEAK_FP8_TFLOPS,
+                         "unit": "TFLOP/s", "frac": dom["frac_fp8_peak"],
+                         "traffic": measured_traffic("gemm_kernel<2, 4, true, true, true>")},
+            "kernels": kernels,
+            "note": "E4M3 elements with E8M0 scales per 32 along K; weights quantized once "
+                    "outside the step; flops counted as the bf16 step's (rank 576, K unpadded)"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -245,7 +305,7 @@ def main():
     dom = kernels[DOMINANT]
     L = model.layers[2]
     dom_flops = 2 * M * (L["K"] + model.R) * L["N"]
-    traffic = measured_traffic()
+    traffic = measured_traffic("gemm_kernel<2, 4, true, false, false>")
     roofline = {"kernel": "lora_up (phase B) of the gate/up linear, SwiGLU epilogue: "
                           f"M={M} K={L['K']}+{model.R} N={L['N']}",
                 "bound": "mfma", "achieved": round(dom_flops / (dom["mean_us"] * 1e-6) / 1e12, 1),
@@ -291,6 +351,10 @@ def main():
     log(f"graph + fused head/Euler: {g_ms:.2f} ms per step")
     del graphs, model
     torch.cuda.empty_cache()
+    if not args.no_mx:
+        log("MXFP8 step ...")
+        out["mxfp8"] = mx_step(torch, M, u, eps, flops, ms, args)
+        torch.cuda.empty_cache()
     if not args.no_elementwise:
         log("elementwise cold-cache timing ...")
         out["elementwise"] = elementwise(torch, fsd, inputs)
