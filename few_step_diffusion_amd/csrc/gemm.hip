@@ -546,7 +546,10 @@ void gemm_kernel(GemmParams p) {
         for (int k = 0; k < 4; ++k) {
           const float gt = acc[i][j][k] * alpha + bg[k];
           const float up = acc[i][j + HALFB][k] * alpha + bu[k];
-          h[k] = gt / (1.0f + __expf(-gt)) * up;
+          // silu(g)·u with a hardware reciprocal (1 ulp) instead of an IEEE
+          // divide (ten VALU ops of 4 cycles each per wave64): the product
+          // is rounded to bf16 right after, and g -> -inf still gives -0
+          h[k] = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;
         }
         u32x2 pk;
         pk.x = f32_to_bf16(h[0]) | (f32_to_bf16(h[1]) << 16);
