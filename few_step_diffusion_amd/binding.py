@@ -18,7 +18,7 @@ __all__ = [
     "lora_down", "lora_up", "lora_linear", "renoise", "euler_step", "token_embed",
     "token_head", "token_head_euler", "mx_quantize", "mx_padded_k", "mx_scale_bytes",
     "mx_scale_offsets", "mx_pack_scales", "mx_unpack_scales", "mx_lora_down", "mx_lora_up",
-    "mx_lora_up_swiglu_mx",
+    "mx_lora_up_swiglu_mx", "attention_workspace_bytes", "attention",
     "EPI_NONE", "EPI_SWIGLU",
 ]
 
@@ -79,6 +79,9 @@ _SIGS = {
     "fsd_mx_lora_up": ([_c_void_p, _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64,
                         _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _c_void_p,
                         _i64, _i64, _i64, _i64, _i64, _int, _c_void_p], _int),
+    "fsd_attention_workspace_bytes": ([_i64, _i64, _i64], ctypes.c_size_t),
+    "fsd_attention": ([_c_void_p, _c_void_p, _c_void_p, _i64, _c_void_p, _i64, _i64, _i64, _i64,
+                       _f32, _c_void_p, ctypes.c_size_t, _c_void_p], _int),
     "fsd_mx_lora_up_swiglu_mx": ([_c_void_p, _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                   _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                   _i64, _c_void_p, _i64, _i64, _i64, _i64, _c_void_p], _int),
@@ -484,3 +487,35 @@ def mx_lora_up_swiglu_mx(Xq, Xs, W0q, W0s, Tq=None, Ts=None, Bq=None, Bs=None, b
                                         _stream(Xq))
     _check("fsd_mx_lora_up_swiglu_mx", st)
     return Hq, Hs
+
+
+# ------------------------------------------------------------ attention
+def attention_workspace_bytes(S: int, H: int, D: int = 128) -> int:
+    return int(lib().fsd_attention_workspace_bytes(S, H, D))
+
+
+def attention(Q, K, V, heads, scale=None, out=None, workspace=None):
+    """O = softmax(Q·Kᵀ·scale)·V per head.  Q, K, V bf16 [S, heads·128] views with
+    one row stride (e.g. slices of a QKV output); returns O bf16 [S, heads·128]."""
+    for t, nm in ((Q, "Q"), (K, "K"), (V, "V")):
+        _need(t, nm, torch.bfloat16)
+    S, HD = Q.shape
+    if K.shape != (S, HD) or V.shape != (S, HD):
+        raise ValueError("Q, K and V must have one shape")
+    if not (_ld(Q) == _ld(K) == _ld(V)):
+        raise ValueError("Q, K and V must share one row stride")
+    if HD % heads:
+        raise ValueError("columns must be heads x head_dim")
+    D = HD // heads
+    scale = 1.0 / D ** 0.5 if scale is None else float(scale)
+    if out is None:
+        out = torch.empty((S, HD), dtype=torch.bfloat16, device=Q.device)
+    _need(out, "out", torch.bfloat16)
+    if workspace is None:
+        workspace = torch.empty(max(attention_workspace_bytes(S, heads, D), 16), dtype=torch.uint8,
+                                device=Q.device)
+    st = lib().fsd_attention(_ptr(Q), _ptr(K), _ptr(V), _ld(Q), _ptr(out), _ld(out), S, heads, D,
+                             float(scale), _ptr(workspace),
+                             workspace.numel() * workspace.element_size(), _stream(Q))
+    _check("fsd_attention", st)
+    return out

@@ -496,4 +496,37 @@ int fsd_mx_lora_up_swiglu_mx(const void* Xq, int64_t ldxq, const void* Xs, const
   return from_hip(fsd::launch_gemm(fsd::GEMM_MX_UP_SWIGLU_MX, p, as_stream(stream)));
 }
 
+size_t fsd_attention_workspace_bytes(int64_t S, int64_t H, int64_t D) {
+  if (S <= 0 || H <= 0 || D <= 0) return 0;
+  return (size_t)(H * D * fsd::attention_padded_tokens(S) * 2);
+}
+
+int fsd_attention(const void* Q, const void* K, const void* V, int64_t ld, void* O, int64_t ldo,
+                  int64_t S, int64_t H, int64_t D, float scale, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  if (S < 0 || H < 1 || D < 1 || !isfinite(scale) || !(scale > 0.0f)) return FSD_EINVAL;
+  if (D != 128) return FSD_EUNSUPPORTED;
+  if (H > 0x7fffffffLL / 128) return FSD_EINVAL;
+  if (ld < H * D || ld % 8 || ldo < H * D || ldo % 8) return FSD_EINVAL;
+  if (S == 0) return FSD_OK;
+  if (!Q || !K || !V || !O) return FSD_EINVAL;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O)) return FSD_EALIGN;
+  const int64_t Sp = fsd::attention_padded_tokens(S);
+  const int64_t need = H * D * Sp * 2;
+  if (!workspace || (int64_t)workspace_bytes < need) return FSD_EWORKSPACE;
+  if (!aligned16(workspace)) return FSD_EALIGN;
+  // 32-bit buffer offsets: a 256-row tile of Q / K / V, one head of the transpose
+  if (256 * ld * 2 > kMaxOffsetBytes || D * Sp * 2 > kMaxOffsetBytes) return FSD_EUNSUPPORTED;
+  if ((S + 255) / 256 * H > 0x7fffffffLL) return FSD_EUNSUPPORTED;
+  const int64_t in_b = span_bytes(S, H * D, ld, 2);
+  const int64_t ob = span_bytes(S, H * D, ldo, 2);
+  if (overlap(O, ob, Q, in_b) || overlap(O, ob, K, in_b) || overlap(O, ob, V, in_b) ||
+      overlap(O, ob, workspace, need) || overlap(workspace, need, Q, in_b) ||
+      overlap(workspace, need, K, in_b) || overlap(workspace, need, V, in_b))
+    return FSD_EINVAL;
+  return from_hip(fsd::launch_attention((const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V, ld,
+                                        (bf16_t*)O, ldo, S, (int)H, scale, (bf16_t*)workspace,
+                                        as_stream(stream)));
+}
+
 }  // extern "C"

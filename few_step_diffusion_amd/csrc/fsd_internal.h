@@ -62,6 +62,12 @@ hipError_t launch_head(const bf16_t* H, int64_t ldh, const bf16_t* P, float* v, 
                        int64_t D, int C, hipStream_t s);
 hipError_t launch_head_euler(const bf16_t* H, int64_t ldh, const bf16_t* P, float* z,
                              float dsigma, int64_t M, int64_t D, int C, hipStream_t s);
+// Dense attention over S tokens, H heads of 128: O = softmax(Q·Kᵀ·scale)·V per
+// head; V is first transposed per head into Vt ([H·128][attention_padded_tokens(S)]).
+int64_t attention_padded_tokens(int64_t S);
+hipError_t launch_attention(const bf16_t* Q, const bf16_t* K, const bf16_t* V, int64_t ld,
+                            bf16_t* O, int64_t ldo, int64_t S, int H, float scale,
+                            bf16_t* Vt, hipStream_t s);
 hipError_t launch_mx_quantize(const bf16_t* X, int64_t ldx, int64_t M, int64_t K, uint8_t* Q,
                               int64_t ldq, uint8_t* S, hipStream_t s);
 

@@ -280,6 +280,32 @@ int fsd_mx_lora_up_swiglu_mx(const void* Xq, int64_t ldxq, const void* Xs,
                              int64_t ldhq, void* Hs, int64_t M, int64_t N,
                              int64_t K, int64_t r, void* stream);
 
+/* ------------------------------------------------------------------------ *
+ * Dense attention (NEXT step: the refine path's baseline attention)          *
+ * ------------------------------------------------------------------------ *
+ * The pages' baseline refine runs the transformer's attention densely in
+ * bf16 ([EN] "Where the 3.9x speedup comes from", dense-BF16 baseline row);
+ * the operation is textbook scaled dot-product attention, per head h:
+ *   O_h = softmax(Q_h · K_hᵀ · scale) · V_h,
+ * the softmax over all S keys of the sequence, fp32 statistics, P rounded to
+ * bf16 before the P·V product, O rounded to bf16.
+ *
+ * fsd_attention_workspace_bytes: bytes of the workspace (V transposed per
+ *   head, H·D·round_up(S, 64)·2).
+ * fsd_attention: Q, K, V bf16 [S, H·D] (head h in columns h·D .. h·D+D-1; the
+ *   Q, K and V slices of a QKV projection output can be passed in place), row
+ *   stride ld >= H·D (multiple of 8); O bf16 [S, H·D], row stride ldo >= H·D
+ *   (multiple of 8).  D must be 128 (else FSD_EUNSUPPORTED); scale finite and
+ *   > 0 (1/sqrt(D) for the standard form).  All pointers 16-byte aligned; O
+ *   and the workspace must not overlap the inputs or each other.  Errors:
+ *   FSD_EINVAL, FSD_EALIGN, FSD_EUNSUPPORTED (also for a 256-row tile or one
+ *   transposed head spanning 2 GiB), FSD_EWORKSPACE. */
+size_t fsd_attention_workspace_bytes(int64_t S, int64_t H, int64_t D);
+int fsd_attention(const void* Q, const void* K, const void* V, int64_t ld,
+                  void* O, int64_t ldo, int64_t S, int64_t H, int64_t D,
+                  float scale, void* workspace, size_t workspace_bytes,
+                  void* stream);
+
 #ifdef __cplusplus
 }
 #endif

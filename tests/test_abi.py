@@ -251,6 +251,33 @@ def test_mx_scale_layout_helpers():
     assert int((S.numpy() == 127).sum()) >= (Mp - M) * 20   # padding rows
 
 
+def test_attention_validation(L):
+    f = ctypes.c_float
+
+    def att(**kw):
+        args = dict(Q=a(1), K=a(2), V=a(3), ld=9216, O=a(4), ldo=3072, S=1000, H=24, D=128,
+                    scale=0.0883883, ws=a(5), wsb=10 ** 9)
+        args.update(kw)
+        return L.fsd_attention(args["Q"], args["K"], args["V"], args["ld"], args["O"], args["ldo"],
+                               args["S"], args["H"], args["D"], f(args["scale"]), args["ws"],
+                               args["wsb"], None)
+    assert L.fsd_attention_workspace_bytes(1000, 24, 128) == 24 * 128 * 1024 * 2
+    assert L.fsd_attention_workspace_bytes(0, 24, 128) == 0
+    assert att(S=0) == OK
+    assert att(D=64, ldo=1536) == EUNSUP                  # head dim 128 only
+    assert att(scale=0.0) == EINVAL
+    assert att(scale=math.nan) == EINVAL
+    assert att(ld=3000) == EINVAL                         # ld < H·D
+    assert att(ldo=3076) == EINVAL                        # ldo % 8
+    assert att(ws=None, wsb=0) == EWS
+    assert att(wsb=24 * 128 * 1024 * 2 - 2) == EWS
+    assert att(O=P(BASE + 4 * 0x10000000 + 8)) == EALIGN
+    assert att(ws=P(BASE + 5 * 0x10000000 + 4)) == EALIGN
+    assert att(O=P(BASE + 0x10000000 + 4096)) == EINVAL   # O overlaps Q
+    assert att(ws=P(BASE + 3 * 0x10000000 + 4096)) == EINVAL   # workspace overlaps V
+    assert att(H=0) == EINVAL
+
+
 def test_python_binding_rejects_cpu_tensors():
     import torch
     with pytest.raises(ValueError):
