@@ -13,7 +13,13 @@
 // in the exp2 domain, rescales its fp32 output and adds P·V with P rounded to
 // bf16.  Lane l of a 16x16 block holds query l%16 and four consecutive keys (S)
 // or head dims (O) 4·(l/16)..+3, so a query's row statistics reduce over the
-// four lanes l%16 + 16c.
+// four lanes l%16 + 16c.  As the P·V operand a lane then holds keys 4c..4c+3 of
+// two adjacent 16-key blocks; the transposed V stores each 32-key group in that
+// order (4-key quarters of its two halves interleaved), so the matching V
+// fragment is one 16-byte read.  The running maximum is kept until a block's
+// maximum exceeds it by more than 2^8 (P stays <= 256, exact enough for bf16
+// and fp32 sums), so the fp32 output is rescaled only in the rare blocks where
+// some row of the wave needs it.
 #include <math.h>
 
 #include "fsd_internal.h"
@@ -99,6 +105,15 @@ void attention_kernel(AttnParams p) {
   // Each wave issues two 1 KB loads of each tile.
   const __amdgpu_buffer_rsrc_t rV =
       make_rsrc(p.Vt + (int64_t)h * kD * p.Sp, (int64_t)kD * p.Sp * 2);
+  uint32_t k_off[2], v_off[2];             // per-lane byte offsets within a block
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int i = 2 * wave + t;
+    const int krow = 4 * i + c4;                                // key within the block
+    k_off[t] = (uint32_t)(((int64_t)krow * p.ld + 8 * (r16 ^ (krow & 15))) * 2);
+    const int vrow = 8 * i + (lane >> 3);                      // head dim
+    v_off[t] = (uint32_t)(((int64_t)vrow * p.Sp + 8 * ((lane & 7) ^ (vrow & 7))) * 2);
+  }
   auto issue_block = [&](int j, int buf) {
     const int64_t k0 = (int64_t)j * kBK;
     const int64_t krows = (S - k0) < kBK ? (S - k0) : kBK;
@@ -106,22 +121,13 @@ void attention_kernel(AttnParams p) {
         make_rsrc(p.K + k0 * p.ld + (int64_t)h * kD, krows * p.ld * 2 - (int64_t)h * kD * 2);
     char* st = lds + buf * kStage;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int i = 2 * wave + t;
-      const int row = 4 * i + c4;                           // key within the block
-      const int lc = r16 ^ (row & 15);
-      const uint32_t off = (uint32_t)(((int64_t)row * p.ld + 8 * lc) * 2);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rK, (lds_ptr_t)(st + i * 1024), 16, off, 0, 0, 0);
-    }
+    for (int t = 0; t < 2; ++t)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rK, (lds_ptr_t)(st + (2 * wave + t) * 1024), 16,
+                                               k_off[t], 0, 0, 0);
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int i = 2 * wave + t;
-      const int row = 8 * i + (lane >> 3);                  // head dim
-      const int lc = (lane & 7) ^ (row & 7);
-      const uint32_t off = (uint32_t)(((int64_t)row * p.Sp + k0 + 8 * lc) * 2);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rV, (lds_ptr_t)(st + kKTile + i * 1024), 16, off,
-                                               0, 0, 0);
-    }
+    for (int t = 0; t < 2; ++t)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rV, (lds_ptr_t)(st + kKTile + (2 * wave + t) * 1024),
+                                               16, v_off[t] + (uint32_t)(k0 * 2), 0, 0, 0);
   };
 
   f32x4 o[2][8];
@@ -161,14 +167,13 @@ void attention_kernel(AttnParams p) {
           s[qi][kj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qi][kk], s[qi][kj], 0, 0, 0);
       }
     // keys past S (last block only) take no weight
-    if ((int64_t)(j + 1) * kBK > S) {
+    if (j == nkb - 1) {
+      const int kvalid = (int)(S - (int64_t)j * kBK);
 #pragma unroll
       for (int kj = 0; kj < 4; ++kj)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int64_t key = (int64_t)j * kBK + 16 * kj + 4 * c4 + t;
-          if (key >= S) { s[0][kj][t] = -INFINITY; s[1][kj][t] = -INFINITY; }
-        }
+        for (int t = 0; t < 4; ++t)
+          if (16 * kj + 4 * c4 + t >= kvalid) { s[0][kj][t] = -INFINITY; s[1][kj][t] = -INFINITY; }
     }
     // online softmax in the exp2 domain
     bf16x8 pf[2][2];
@@ -181,23 +186,29 @@ void attention_kernel(AttnParams p) {
         for (int t = 0; t < 4; ++t) mx = fmaxf(mx, s[qi][kj][t]);
       mx = fmaxf(mx, shfl_xor_f(mx, 16));
       mx = fmaxf(mx, shfl_xor_f(mx, 32));
-      const float m_new = fmaxf(m_run[qi], mx * p.scale_log2);
-      const float alpha = __builtin_amdgcn_exp2f(m_run[qi] - m_new);
+      const float m_blk = mx * p.scale_log2;
+      const bool grow = m_blk > m_run[qi] + 8.0f;       // (always true for the first block)
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {     // wave-uniform, rare
+        const float m_new = grow ? m_blk : m_run[qi];
+        const float alpha = __builtin_amdgcn_exp2f(m_run[qi] - m_new);
+        l_run[qi] *= alpha;
+#pragma unroll
+        for (int dj = 0; dj < 8; ++dj) o[qi][dj] *= alpha;
+        m_run[qi] = m_new;
+      }
+      const float m_use = m_run[qi];
       float sum = 0.0f;
       float pv[4][4];
 #pragma unroll
       for (int kj = 0; kj < 4; ++kj)
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          pv[kj][t] = __builtin_amdgcn_exp2f(fmaf(s[qi][kj][t], p.scale_log2, -m_new));
+          pv[kj][t] = __builtin_amdgcn_exp2f(fmaf(s[qi][kj][t], p.scale_log2, -m_use));
           sum += pv[kj][t];
         }
       sum += shfl_xor_f(sum, 16);
       sum += shfl_xor_f(sum, 32);
-      l_run[qi] = fmaf(l_run[qi], alpha, sum);
-      m_run[qi] = m_new;
-#pragma unroll
-      for (int dj = 0; dj < 8; ++dj) o[qi][dj] *= alpha;
+      l_run[qi] += sum;
       // P as the PV operand: slots 0..3 = keys 4c..4c+3 of key block 2·kk2,
       // slots 4..7 = the same of block 2·kk2 + 1 (the Vᵀ fragment matches)
 #pragma unroll
@@ -208,18 +219,14 @@ void attention_kernel(AttnParams p) {
                                (__bf16)pv[2 * kk2 + 1][2], (__bf16)pv[2 * kk2 + 1][3]};
     }
     // O += P·V: Vᵀ fragment of head dims 16·dj + l%16, keys 32·kk2 + 4c + 0..3
-    // and 32·kk2 + 16 + 4c + 0..3, two 8-byte reads
+    // and 32·kk2 + 16 + 4c + 0..3: chunk 4·kk2 + c of the interleaved row
 #pragma unroll
     for (int kk2 = 0; kk2 < 2; ++kk2)
 #pragma unroll
       for (int dj = 0; dj < 8; ++dj) {
         const int row = 16 * dj + r16;
-        const int sw = row & 7;
-        const int b1 = (((4 * kk2 + (c4 >> 1)) ^ sw) << 4) + ((c4 & 1) << 3);
-        const int b2 = (((4 * kk2 + 2 + (c4 >> 1)) ^ sw) << 4) + ((c4 & 1) << 3);
-        const u32x2 lo = *(const u32x2*)(vt + row * kVRow + b1);
-        const u32x2 hi = *(const u32x2*)(vt + row * kVRow + b2);
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, (u32x4){lo.x, lo.y, hi.x, hi.y});
+        const bf16x8 vf =
+            *(const bf16x8*)(vt + row * kVRow + (((4 * kk2 + c4) ^ (row & 7)) << 4));
 #pragma unroll
         for (int qi = 0; qi < 2; ++qi)
           o[qi][dj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[qi][kk2], o[qi][dj], 0, 0, 0);
@@ -246,7 +253,9 @@ void attention_kernel(AttnParams p) {
   }
 }
 
-// Vᵀ per head: Vt[(h·D + d)·Sp + s] = V[s·ld + h·D + d], zeros for s >= S.
+// Vᵀ per head: Vt[(h·D + d)·Sp + perm(s)] = V[s·ld + h·D + d], zeros for
+// s >= S, where perm interleaves the 4-key quarters of the two 16-key halves of
+// each 32-key group: s = 32g + 16a + 4c + t  ->  32g + 8c + 4a + t.
 // One 64-token x 64-dim tile per workgroup through LDS.
 constexpr int kTT = 64;
 __global__ __launch_bounds__(256) void transpose_v_kernel(const bf16_t* V, int64_t ld, int64_t S,
@@ -263,9 +272,10 @@ __global__ __launch_bounds__(256) void transpose_v_kernel(const bf16_t* V, int64
     u32x4 v = {0u, 0u, 0u, 0u};
     if (s0 + r < S) v = *(const u32x4*)(V + (s0 + r) * ld + (int64_t)h * kD + d0 + 8 * c);
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    const int rp = (r & 32) | ((r & 12) << 1) | ((r & 16) >> 2) | (r & 3);   // perm within 64
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-      tile[8 * c + e][r] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+      tile[8 * c + e][rp] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
   }
   __syncthreads();
   // write 64 head-dim rows x 128 bytes
