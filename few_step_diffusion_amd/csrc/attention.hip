@@ -19,7 +19,9 @@
 // fragment is one 16-byte read.  The running maximum is kept until a block's
 // maximum exceeds it by more than 2^8 (P stays <= 256, exact enough for bf16
 // and fp32 sums), so the fp32 output is rescaled only in the rare blocks where
-// some row of the wave needs it.
+// some row of the wave needs it.  The row sums of P come from the matrix pipe:
+// a ninth 16-column output block is P times a block of ones, so the softmax
+// denominator uses the same bf16 P as the numerator and costs no VALU adds.
 #include <math.h>
 
 #include "fsd_internal.h"
@@ -130,12 +132,16 @@ void attention_kernel(AttnParams p) {
                                                16, v_off[t] + (uint32_t)(k0 * 2), 0, 0, 0);
   };
 
-  f32x4 o[2][8];
+  // o[qi][0..7]: the output's 128 head dims; o[qi][8]: every column holds the
+  // running sum of P over the keys (P times a block of ones)
+  f32x4 o[2][9];
 #pragma unroll
   for (int qi = 0; qi < 2; ++qi)
 #pragma unroll
-    for (int dj = 0; dj < 8; ++dj) o[qi][dj] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
-  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.0f, 0.0f};
+    for (int dj = 0; dj < 9; ++dj) o[qi][dj] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+  float m_run[2] = {-INFINITY, -INFINITY};
+  const bf16x8 ones = {(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f,
+                       (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
 
   const int nkb = (int)((S + kBK - 1) / kBK);
   issue_block(0, 0);
@@ -191,24 +197,17 @@ void attention_kernel(AttnParams p) {
       if (__builtin_amdgcn_ballot_w64(grow) != 0) {     // wave-uniform, rare
         const float m_new = grow ? m_blk : m_run[qi];
         const float alpha = __builtin_amdgcn_exp2f(m_run[qi] - m_new);
-        l_run[qi] *= alpha;
 #pragma unroll
-        for (int dj = 0; dj < 8; ++dj) o[qi][dj] *= alpha;
+        for (int dj = 0; dj < 9; ++dj) o[qi][dj] *= alpha;
         m_run[qi] = m_new;
       }
       const float m_use = m_run[qi];
-      float sum = 0.0f;
       float pv[4][4];
 #pragma unroll
       for (int kj = 0; kj < 4; ++kj)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
+        for (int t = 0; t < 4; ++t)
           pv[kj][t] = __builtin_amdgcn_exp2f(fmaf(s[qi][kj][t], p.scale_log2, -m_use));
-          sum += pv[kj][t];
-        }
-      sum += shfl_xor_f(sum, 16);
-      sum += shfl_xor_f(sum, 32);
-      l_run[qi] += sum;
       // P as the PV operand: slots 0..3 = keys 4c..4c+3 of key block 2·kk2,
       // slots 4..7 = the same of block 2·kk2 + 1 (the Vᵀ fragment matches)
 #pragma unroll
@@ -231,6 +230,11 @@ void attention_kernel(AttnParams p) {
         for (int qi = 0; qi < 2; ++qi)
           o[qi][dj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[qi][kk2], o[qi][dj], 0, 0, 0);
       }
+#pragma unroll
+    for (int kk2 = 0; kk2 < 2; ++kk2)
+#pragma unroll
+      for (int qi = 0; qi < 2; ++qi)
+        o[qi][8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[qi][kk2], o[qi][8], 0, 0, 0);
   }
 
   // O / l, rounded to bf16: lane l writes query 16·qi + l%16, head dims
@@ -239,7 +243,7 @@ void attention_kernel(AttnParams p) {
   for (int qi = 0; qi < 2; ++qi) {
     const int64_t q = q0 + 32 * wave + 16 * qi + r16;
     if (q >= S) continue;
-    const float inv = 1.0f / l_run[qi];
+    const float inv = 1.0f / o[qi][8][0];
     bf16_t* dst = p.O + q * p.ldo + (int64_t)h * kD + 4 * c4;
 #pragma unroll
     for (int dj = 0; dj < 8; ++dj) {
