@@ -20,6 +20,8 @@ Prints ONE JSON line on stdout (everything else goes to stderr):
   mxfp8      the step with the four linears as MXFP8 GEMMs (quantizers in the
              step time), the fused SwiGLU->MXFP8 gate/up GEMM against the
              5000 TFLOP/s fp8 peak
+  attention  one dense attention call over the 2K grid as one sequence
+             (532,800 tokens, 24 heads of 128), against 2500 TFLOP/s
   cpu_baseline the fp64 oracle on a bounded sample of tokens on host cores
 """
 from __future__ import annotations
@@ -56,6 +58,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target host time of the oracle sample")
     ap.add_argument("--no-mx", action="store_true", help="skip the MXFP8 step")
+    ap.add_argument("--no-attention", action="store_true", help="skip the dense attention call")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 1 GiB device copy first (a known-size kernel for counters)")
     return ap.parse_args()
@@ -175,6 +178,40 @@ def cpu_baseline(model_flops_per_token, target_s):
     return {"value": round(tflops, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{tokens} of 532,800 tokens of the same step (renoise + 3 stand-in "
                       f"velocity evaluations + Euler), fp64, {dt:.1f} s"}
+
+
+def attention_2k(torch, fsd, M, args):
+    """One dense attention call over the 2K grid as one sequence (the refine
+    path's baseline attention): 532,800 tokens, 24 heads of 128 read in place
+    from a QKV buffer; V's per-head transpose included in the call."""
+    H, D = 24, 128
+    g = torch.Generator(device="cuda:0")
+    g.manual_seed(4242)
+    qkv = torch.randn((M, 3 * H * D), generator=g, device="cuda:0").to(torch.bfloat16)
+    Q, K, V = qkv[:, :H * D], qkv[:, H * D:2 * H * D], qkv[:, 2 * H * D:]
+    O = torch.empty((M, H * D), dtype=torch.bfloat16, device="cuda:0")
+    ws = torch.empty(fsd.attention_workspace_bytes(M, H, D), dtype=torch.uint8, device="cuda:0")
+    fsd.attention(Q, K, V, H, out=O, workspace=ws)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    reps = 2
+    torch.cuda._sleep(SPIN_CYCLES)
+    a.record()
+    for _ in range(reps):
+        fsd.attention(Q, K, V, H, out=O, workspace=ws)
+    b.record()
+    b.synchronize()
+    ms = a.elapsed_time(b) / reps
+    flops = 4.0 * M * M * H * D
+    tf = flops / (ms * 1e-3) / 1e12
+    log(f"attention: {ms:.1f} ms, {tf:.0f} TFLOP/s")
+    del qkv, O, ws
+    return {"ms_per_call": round(ms, 2), "tflops": round(tf, 1),
+            "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4), "bound": "mfma",
+            "flops_per_call": flops, "tokens": M, "heads": H, "head_dim": D,
+            "note": "softmax(Q·Kᵀ/sqrt(128))·V per head over all 532,800 tokens; algorithmic "
+                    "flops 4·S²·H·D; includes the per-head transpose of V (one pass over V)"}
 
 
 def mx_step(torch, M, u, eps, flops, bf16_ms, args):
@@ -354,6 +391,10 @@ def main():
     if not args.no_mx:
         log("MXFP8 step ...")
         out["mxfp8"] = mx_step(torch, M, u, eps, flops, ms, args)
+        torch.cuda.empty_cache()
+    if not args.no_attention:
+        log("dense attention at the 2K grid ...")
+        out["attention"] = attention_2k(torch, fsd, M, args)
         torch.cuda.empty_cache()
     if not args.no_elementwise:
         log("elementwise cold-cache timing ...")
