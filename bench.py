@@ -13,8 +13,9 @@ Prints ONE JSON line on stdout (everything else goes to stderr):
              time from HIP events on its stream, against 2500 TFLOP/s bf16
   kernels    the same for every kernel of the step
   elementwise  renoise / Euler GB/s at the 768P, 2K and 4K latents, 12 bytes
-             per element, cache-cold (a 1 GiB read between repetitions) and
-             warm; median / min / max of 20 after 5 warm-ups
+             per element: batches of back-to-back launches, cache-cold
+             (launches cycle through >= 2 GiB of distinct buffers) and warm;
+             median / min / max of 5 batches
   graph_fused  the step as one replayed HIP graph per sampler step with the
              Euler update fused into the head
   mxfp8      the step with the four linears as MXFP8 GEMMs (quantizers in the
@@ -97,54 +98,54 @@ def kernel_times(events):
     return out
 
 
-def elementwise(torch, fsd, inputs, warmup=5, reps=20):
+def elementwise(torch, fsd, inputs, batches=5, per_batch=24):
     """Renoise / Euler bandwidth at the 768P, 2K and 4K latents.
 
-    cold: before every repetition a 1 GiB buffer is read (not written), so
-    none of the operands is in L2 or the Infinity Cache and no dirty lines of
-    the flush are left for the timed kernel to write back; warm: the same
-    launch repeated with nothing in between.  Median, min and max of `reps`
-    repetitions after `warmup` untimed ones, HIP events on the current stream.
+    Each batch is `per_batch` launches back to back between one pair of HIP
+    events, so the figure is the sustained per-launch time, gaps between
+    launches included, without a per-launch event overhead (a few us against
+    a 25 us kernel at 2K).  cold: consecutive launches cycle through enough
+    distinct buffer sets (>= 2 GiB together) that none finds its operands in L2
+    or the 256 MB Infinity Cache; warm: every launch reuses one set.  Median,
+    min and max of `batches` batches after one untimed batch.
     """
     dev = torch.device("cuda:0")
-    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
     res = {}
     for wid, tag in ((1, "768p"), (2, "2k"), (3, "4k")):
         n = inputs.WORKLOADS[wid].latent_elems
-        u = torch.randn(n, device=dev)
-        e = torch.randn(n, device=dev)
-        z = torch.empty(n, device=dev)
+        nbytes = 12 * n
+        nsets = min(64, max(4, -(-(2 << 30) // nbytes)))
+        sets = [(torch.randn(n, device=dev), torch.randn(n, device=dev),
+                 torch.empty(n, device=dev)) for _ in range(nsets)]
         for name in ("renoise", "euler"):
             for mode in ("cold", "warm"):
-                ts = []
-                for rep in range(warmup + reps):
-                    # keep the GPU busy while the timed launch is enqueued, so the
-                    # interval holds the kernel and not the host's launch latency:
-                    # the 1 GiB read does it for the cold runs, a spin for the warm
-                    if mode == "cold":
-                        flush.sum()
-                    else:
-                        torch.cuda._sleep(SPIN_CYCLES)
-                    a = torch.cuda.Event(enable_timing=True)
-                    b = torch.cuda.Event(enable_timing=True)
-                    a.record()
+                def launch(k):
+                    u, e, z = sets[k % nsets] if mode == "cold" else sets[0]
                     if name == "renoise":
                         fsd.renoise(u, e, 0.909, out=z)
                     else:
                         fsd.euler_step(z, e, 0.909, 0.857)
+                ts = []
+                for rep in range(batches + 1):
+                    torch.cuda._sleep(SPIN_CYCLES)
+                    a = torch.cuda.Event(enable_timing=True)
+                    b = torch.cuda.Event(enable_timing=True)
+                    a.record()
+                    for k in range(per_batch):
+                        launch(k)
                     b.record()
                     torch.cuda.synchronize()
-                    if rep >= warmup:
-                        ts.append(a.elapsed_time(b))
+                    if rep > 0:
+                        ts.append(a.elapsed_time(b) / per_batch)
                 med = statistics.median(ts)
-                gbs = 12.0 * n / (med * 1e-3) / 1e9
+                gbs = nbytes / (med * 1e-3) / 1e9
                 key = f"{name}_{tag}" if mode == "cold" else f"{name}_{tag}_warm"
                 res[key] = {"us": round(med * 1e3, 2), "min_us": round(min(ts) * 1e3, 2),
                             "max_us": round(max(ts) * 1e3, 2), "GB/s": round(gbs, 1),
-                            "frac_hbm": round(gbs / PEAK_HBM_GBS, 3), "bytes": 12 * n}
-        del u, e, z
-    del flush
-    torch.cuda.empty_cache()
+                            "frac_hbm": round(gbs / PEAK_HBM_GBS, 3), "bytes": nbytes,
+                            "buffer_sets": nsets if mode == "cold" else 1}
+        del sets
+        torch.cuda.empty_cache()
     return res
 
 
