@@ -223,6 +223,47 @@ def test_mx_swiglu_quantize_epilogue(gpu, M, N, K, r, bias):
     assert_mx_valid(Hq, Hs, h, dh, f"fused swiglu->mx M={M} N={N}")
 
 
+# ------------------------------------------------- full-size MXFP8 linear
+def test_mx_linear_2k_qkv_sampled_rows(gpu):
+    """The 2K QKV linear (M = 532,800, K = 3072, N = 9216, rank 576) on the MXFP8
+    path as the stand-in runs it: quantize X, phase A, quantize T, phase B, all
+    on the GPU.  The oracle quantizes the sampled rows of X and the weights
+    itself (from the bf16 values), rounds its T to bf16 like the GPU, and is
+    compared row by row at the bf16 GEMM gate."""
+    from few_step_diffusion_amd import inputs
+    wl = inputs.WORKLOADS[2]
+    label, K, N, _ = wl.linears[0]
+    M, wid = wl.tokens, 2
+    say(f"mx 2K {label}: M={M} K={K} N={N} r=576")
+    X = inputs.activations(wid, M, K, device=gpu)
+    W0 = inputs.base_weight(wid, K, N)
+    A_l, B_l = inputs.adapters(wid, K, N)
+    A, B = fsd.lora_merge([a.to(gpu) for a in A_l], [b.to(gpu) for b in B_l])
+    Qw, Sw = fsd.mx_quantize(W0.to(gpu))
+    Qa, Sa = fsd.mx_quantize(A)
+    Qb, Sb = fsd.mx_quantize(B)
+    Qx, Sx = fsd.mx_quantize(X)
+    T = fsd.mx_lora_down(Qx, Sx, Qa, Sa)
+    Qt, St = fsd.mx_quantize(T)
+    Y = fsd.mx_lora_up(Qx, Sx, Qw, Sw, Qt, St, Qb, Sb)
+    torch.cuda.synchronize()
+    rows = inputs.sample_rows(M, 96, seed=21)
+    got = Y[torch.from_numpy(rows).to(gpu)].float().cpu().numpy()
+    del Y, T, Qx, Sx, Qt, St
+    Ab, Bb = oracle.merge_bf16([a.numpy() for a in A_l], [b.numpy() for b in B_l])
+    Ad = mx.mx_values(oracle.bf16_value(Ab).reshape(Ab.shape))
+    Bd = mx.mx_values(oracle.bf16_value(Bb).reshape(Bb.shape))
+    Wd = mx.mx_values(W0.float().numpy())
+    Xd = mx.mx_values(X[torch.from_numpy(rows).to(gpu)].float().cpu().numpy())
+    T_ref = bf16_round(oracle.lora_linear_rows(Xd, Ad, None, None))
+    ref = Xd @ Wd.T + mx.mx_values(T_ref) @ Bd.T
+    ok, err = metrics.gemm_ok(got, ref)
+    say(f"  rel_l2 {err[0]:.3e} rel_max {err[1]:.3e} over {len(rows)} rows")
+    assert ok, err
+    del X
+    torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------------ MXFP8 stand-in
 def _oracle_standin_layers(D, F):
     """bf16 values of the stand-in's weights as the GPU holds them before quantizing."""
