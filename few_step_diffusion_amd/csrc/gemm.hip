@@ -40,6 +40,11 @@
 //   * workgroup ids are remapped so that each XCD (ids round-robin over 8)
 //     gets a contiguous run of tiles, ordered in groups of 4 tile-rows: the
 //     32 tiles an XCD runs at once share 4 X tiles and 8 W tiles in its L2.
+//   * residual: the loads the last two K steps issue for the steps past the
+//     end land in four slots that are no longer read, so for plain 256 x 256
+//     tiles they carry the tile's residual into the epilogue's staging layout
+//     instead of zeros (measured at M = 532,800, K = 3072 + 576, N = 3072: the
+//     residual's cost fell from 0.75 to 0.23 ms of 9.2).
 //   * epilogue: each wave stages its bf16 results (and the residual) through
 //     LDS and writes whole row segments with 16-byte non-temporal stores: the
 //     output is written once and not re-read by this kernel, so it should not
@@ -207,6 +212,37 @@ void gemm_kernel(GemmParams p) {
   const int nk1 = (K1 + KSTEP - 1) / KSTEP;
   const int nk = nk0 + nk1;
 
+  // Residual prefetch (plain 256 x 256 tiles with a residual).  The loads a
+  // loader issues for the steps nk and nk + 1 past the end of the K loop land
+  // in four 32 KB slots that nothing reads any more (A slots nk % 3 and
+  // (nk + 1) % 3, B slots nk % 2 and (nk + 1) % 2); instead of zeros they
+  // bring the tile's 256 x 256 bf16 residual straight into the epilogue's
+  // staging layout, so its latency overlaps the last two K steps.  Part g of
+  // the residual (tile rows 64g .. 64g + 63, i.e. wave row g) goes to step
+  // nk + g of A for g < 2 and to step nk + g - 2 of B; each part is two 16 KB
+  // wave regions (wave columns 0 and 1) of 64 rows x 256 bytes whose 16-byte
+  // chunks are XOR-swizzled by the row's low 4 bits.  The same number of
+  // loads is issued as for a K step, so the loaders' vmcnt waits are unchanged.
+  constexpr bool RES_PF = !SWIGLU && !QOUT && WM == 2 && WN == 4 && A_STAGE == 32768 &&
+                          B_STAGE == 32768 && A_PER == 8 && B_PER == 8;
+  const bool res_pf = RES_PF && p.res != nullptr;
+  const __amdgpu_buffer_rsrc_t rR =
+      res_pf ? make_rsrc(p.res + m0 * p.ldr, rows_valid * p.ldr * 2) : rA0;
+  auto issue_res = [&](int g, int slot_bytes) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int q = 4 * i + wl;                      // 1 KB piece of the 32 KB part
+      const int hh = q >> 4;                          // wave column of the region
+      const int r = ((q & 15) << 2) + (lane >> 4);    // row within the region
+      const int lc = (lane & 15) ^ (r & 15);          // logical chunk of physical lane & 15
+      const int64_t c = (int64_t)tn * 256 + 128 * hh + 8 * lc;
+      const uint32_t off =
+          c < N ? (uint32_t)((((int64_t)(64 * g + r)) * p.ldr + c) * 2) : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rR, (lds_ptr_t)(lds + slot_bytes + q * 1024), 16, off, 0, 0, 0);
+    }
+  };
+
   // This wave's LDS-DMA loads of its operand for K-step kt into slot `slot`.
   // Branch-free but for the wave-uniform check of a partial last round:
   // chunks past the segment's K (a partial last step) and every chunk of a
@@ -249,6 +285,17 @@ void gemm_kernel(GemmParams p) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           r, (lds_ptr_t)(lds + B_BASE + slot * B_STAGE + q * 1024), 16, off, 0, 0, 0);
     }
+  };
+
+  // the loads of steps that may lie past the end (the prologue and the last two
+  // iterations): the residual parts instead of zeros when it is prefetched
+  auto issue_a_tail = [&](int kt, int slot) {
+    if (RES_PF && res_pf && kt >= nk) issue_res(kt - nk, slot * A_STAGE);
+    else issue_a(kt, slot);
+  };
+  auto issue_b_tail = [&](int kt, int slot) {
+    if (RES_PF && res_pf && kt >= nk) issue_res(2 + kt - nk, B_BASE + slot * B_STAGE);
+    else issue_b(kt, slot);
   };
 
   // ---- LDS -> MFMA fragments -----------------------------------------------------
@@ -412,24 +459,28 @@ void gemm_kernel(GemmParams p) {
   //   reader (vector-memory loads retire in order).
   constexpr int A_WAIT = A_TOT / 4;        // A loads a group-1 wave issues per step
   static_assert(A_TOT % 4 == 0, "every loader issues the same number of A loads");
+  // The last two iterations issue the loads of steps nk and nk + 1; they run
+  // as a separate copy of the loop body so that the steady-state loop keeps
+  // no residual test.
   if (wgrp == 1) {
-    issue_a(0, 0);
-    issue_a(1, 1);
+    issue_a_tail(0, 0);
+    issue_a_tail(1, 1);
     wait_vm_lgkm0<A_WAIT>();               // A(0) has landed
   } else {
-    issue_b(0, 0);
-    issue_b(1, 1);
+    issue_b_tail(0, 0);
+    issue_b_tail(1, 1);
     wait_vm_lgkm0<B_PER>();                // B(0) has landed (over-waits if partial)
   }
   __builtin_amdgcn_s_barrier();
   int sa = 0;                              // A slot of step kt (kt % 3)
+  const int nk_main = nk - 2;              // iterations whose loads are all in range
   if (wgrp == 0) {
     load_scales(0);
     read_step(0, 0);
     if constexpr (MX) wait_vm_lgkm0<0>();    // the scales were issued after B(1)
     else wait_vm_lgkm0<B_PER>();
     __builtin_amdgcn_s_barrier();
-    for (int kt = 0; kt < nk; ++kt) {
+    auto body0 = [&](int kt, auto tail) {
       const int sb = kt & 1;
       const int sa_next = sa == NSLOT_A - 1 ? 0 : sa + 1;
       __builtin_amdgcn_sched_barrier(0);
@@ -443,22 +494,27 @@ void gemm_kernel(GemmParams p) {
       // MX reads unconditionally (after the last step: stale LDS and scales that
       // are never used), which keeps the 8-register fragments out of phis
       if (MX || kt + 1 < nk) load_scales(kt + 1);   // before the B loads: retire first
-      issue_b(kt + 2, sb);
+      if constexpr (decltype(tail)::value) issue_b_tail(kt + 2, sb);
+      else issue_b(kt + 2, sb);
       if (MX || kt + 1 < nk) read_step(sa_next, sb ^ 1);
       wait_vm_lgkm0<B_PER>();              // fragments (and scales) in registers
       __builtin_amdgcn_s_barrier();
       sa = sa_next;
-    }
+    };
+    int kt = 0;
+    for (; kt < nk_main; ++kt) body0(kt, std::false_type{});
+    for (; kt < nk; ++kt) body0(kt, std::true_type{});
   } else {
     __builtin_amdgcn_s_barrier();
-    for (int kt = 0; kt < nk; ++kt) {
+    auto body1 = [&](int kt, auto tail) {
       const int sb = kt & 1;
       const int sa_next = sa == NSLOT_A - 1 ? 0 : sa + 1;
       const int sa_load = sa_next == NSLOT_A - 1 ? 0 : sa_next + 1;   // (kt + 2) % 3
       __builtin_amdgcn_sched_barrier(0);
       load_scales(kt);                     // (MX) before the A loads: retire first
       read_step(sa, sb);
-      issue_a(kt + 2, sa_load);
+      if constexpr (decltype(tail)::value) issue_a_tail(kt + 2, sa_load);
+      else issue_a(kt + 2, sa_load);
       wait_vm_lgkm0<A_WAIT>();             // A(kt+1) has landed; fragments in registers
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
@@ -468,7 +524,10 @@ void gemm_kernel(GemmParams p) {
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_barrier();
       sa = sa_next;
-    }
+    };
+    int kt = 0;
+    for (; kt < nk_main; ++kt) body1(kt, std::false_type{});
+    for (; kt < nk; ++kt) body1(kt, std::true_type{});
   }
   // all LDS-DMA writes (including the out-of-range loads past the end) have
   // landed and every wave is done with the rings before LDS is reused below
@@ -493,7 +552,16 @@ void gemm_kernel(GemmParams p) {
   constexpr int RP = POW2 ? (256 / ORB > 0 ? 256 / ORB : 1) : 1;   // staged rows per 256 B
   constexpr int OROWS = WM * 32;                    // tokens per wave
   static_assert(kWaves * OROWS * PITCH <= LDS_BYTES, "epilogue staging must fit in LDS");
-  char* ow = lds + wave * OROWS * PITCH;
+  // (with the residual prefetch, wave row g's regions are the slots that
+  // received residual part g)
+  int ow_bytes = wave * OROWS * PITCH;
+  if constexpr (RES_PF) {
+    const int g = wm, n3 = nk % 3;
+    const int a_slot = g == 0 ? n3 : (n3 == 2 ? 0 : n3 + 1);
+    const int b_slot = (nk + (g - 2)) & 1;
+    ow_bytes = (g < 2 ? a_slot * A_STAGE : B_BASE + b_slot * B_STAGE) + wn * (OROWS * PITCH);
+  }
+  char* ow = lds + ow_bytes;
   auto pchunk = [&](int row, int c) -> int {      // physical chunk of logical chunk c
     if constexpr (POW2) return c ^ ((row / RP) & (OCH - 1));
     else return c;
@@ -502,7 +570,7 @@ void gemm_kernel(GemmParams p) {
   const int64_t tok0 = (int64_t)wm * OROWS;            // first tile row of the wave
   const float alpha = p.alpha;
 
-  if (p.res) {
+  if (!RES_PF && p.res) {
     // residual tile -> LDS (same layout), one 16-byte chunk per lane
     for (int idx = lane; idx < OROWS * OCH; idx += 64) {
       const int row = idx / OCH, pc = idx % OCH;

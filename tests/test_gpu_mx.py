@@ -94,6 +94,7 @@ def test_mx_lora_down(gpu, M, K, r):
     (300, 512, 1024, 576, "none", False),
     (300, 200, 256, 0, "none", True),
     (1, 384, 128, 64, "none", True),
+    (70, 320, 128, 0, "none", True),      # one K step with a residual
     (130, 256, 512, 576, "swiglu", True),
     (513, 384, 384, 576, "swiglu", False),
 ])

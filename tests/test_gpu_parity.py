@@ -151,6 +151,33 @@ def test_residual_separate_and_in_place(gpu):
     assert torch.equal(Y2.cpu(), Y.cpu())
 
 
+@pytest.mark.parametrize("M,K,N,r", [
+    (300, 64, 320, 0),      # one K step; a partial second N tile
+    (257, 64, 320, 16),     # two K steps
+    (513, 128, 256, 64),    # three K steps
+    (1, 512, 576, 576),     # one token, 17 K steps, partial third N tile
+])
+def test_residual_short_k_and_tails(gpu, M, K, N, r):
+    """The residual tile rides on the loads of the steps past the end of the
+    K loop: short K loops, ragged M and partial N tiles, separate and in place."""
+    say(f"residual short K M={M} K={K} N={N} r={r}")
+    X = inputs.normal((M, K), 1.0, 51 + M, dtype=torch.bfloat16)
+    W0 = inputs.normal((N, K), 0.05, 52, dtype=torch.bfloat16)
+    R = inputs.normal((M, N), 1.0, 53, dtype=torch.bfloat16)
+    bias = inputs.normal((N,), 0.1, 54)
+    if r:
+        A, B, Af, Bf = merged(11, K, N, gpu, ranks=(r // 2, r // 4, r // 4))
+    else:
+        A = B = Af = Bf = None
+    ref = oracle.lora_linear_rows(f32(X), f32(W0), Af, Bf, bias=bias.numpy(), residual=f32(R))
+    Y = fsd.lora_linear(X.to(gpu), W0.to(gpu), A, B, bias=bias.to(gpu), residual=R.to(gpu))
+    assert_gemm(f32(Y), ref, f"residual M={M} K={K} N={N} r={r}")
+    Rd = R.to(gpu)
+    Y2 = fsd.lora_linear(X.to(gpu), W0.to(gpu), A, B, bias=bias.to(gpu), residual=Rd, out=Rd)
+    assert Y2.data_ptr() == Rd.data_ptr()
+    assert torch.equal(Y2.cpu(), Y.cpu())
+
+
 def test_strided_input_slice(gpu):
     M, D = 300, 256
     say(f"V-slice input M={M} D={D} ld=3D")
