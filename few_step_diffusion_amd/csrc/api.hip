@@ -69,6 +69,8 @@ int validate_up(const UpShape& a, bool has_t) {
     return FSD_EUNSUPPORTED;
   if (kTileM * a.ldx * 2 > kMaxOffsetBytes || kTileM * a.ldt * 2 > kMaxOffsetBytes)
     return FSD_EUNSUPPORTED;
+  // the residual is fetched through one 256-row tile's buffer resource
+  if (a.residual && kTileM * a.ldr * 2 > kMaxOffsetBytes) return FSD_EUNSUPPORTED;
   // aliasing
   const int64_t ybytes = span_bytes(a.M, nout, a.ldy, 2);
   if (overlap(a.Y, ybytes, a.X, span_bytes(a.M, a.K, a.ldx, 2)) ||
@@ -453,6 +455,7 @@ int fsd_mx_lora_up(const void* Xq, int64_t ldxq, const void* Xs, const void* W0q
   if (!Y || ldy < nout || ldy % 8) return FSD_EINVAL;
   if (residual && (ldr < nout || ldr % 8)) return FSD_EINVAL;
   if (!aligned16(Y) || (residual && !aligned16(residual))) return FSD_EALIGN;
+  if (residual && kTileM * ldr * 2 > kMaxOffsetBytes) return FSD_EUNSUPPORTED;
   const int64_t yb = span_bytes(M, nout, ldy, 2);
   const int st = validate_mx_up_inputs(Xq, ldxq, Xs, W0q, W0s, Tq, ldtq, Ts, Bq, Bs, bias, M, N,
                                        K, r, Y, yb);

@@ -121,6 +121,8 @@ int fsd_lora_merge(int n_adapters, const float* const* A_list,
  * Accumulation is fp32; Y is rounded to bf16 (round-to-nearest-even).
  * Sizes: M >= 0 (M == 0 is a no-op), K >= 8, N >= 8, r >= 0 (r == 0 gives the
  * plain GEMM), K, N, r multiples of 8, SWIGLU needs N a multiple of 16.
+ * Buffer offsets are 32-bit: (N + 256)·K·2, (N + 256)·r·2 and 256·ld·2 for
+ * each of ldx, ldt and ldr must stay below 2^31 (else FSD_EUNSUPPORTED).
  * Aliasing: Y must not overlap X, W0, A, B, bias or the workspace.
  */
 
@@ -259,8 +261,9 @@ int fsd_token_head_euler(const void* H, int64_t ldh, const void* P, float* z,
  *   MXFP8 quantizer").
  * In all three, code arrays are 16-byte aligned with row strides multiples of 16,
  * scale arrays 4-byte aligned; a weight operand must span less than 2 GiB with
- * 256 extra rows, an activation operand's 256-row tile likewise, and every
- * scale array less than 2 GiB (else FSD_EUNSUPPORTED). */
+ * 256 extra rows, an activation operand's 256-row tile likewise (and 256
+ * rows of the residual, 256·ldr·2 bytes), and every scale array less than
+ * 2 GiB (else FSD_EUNSUPPORTED). */
 size_t fsd_mx_scale_bytes(int64_t M, int64_t K);
 int fsd_mx_quantize(const void* X, int64_t ldx, int64_t M, int64_t K, void* Q,
                     int64_t ldq, void* S, void* stream);

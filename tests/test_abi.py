@@ -84,6 +84,8 @@ def test_lora_up_validation(L):
     assert up(L, M=0) == OK                               # empty: no launch
     assert up(L, M=0, res=a(5), ldr=1024) == OK           # in-place residual is legal
     assert up(L, N=65536, K=32768, ldx=32768, ldy=65536) == EUNSUP   # > 32-bit offsets
+    assert up(L, res=a(6), ldr=1 << 22) == EUNSUP          # 256 residual rows span 2 GiB
+    assert up(L, M=0, res=a(6), ldr=(1 << 22) - 8) == OK  # just inside
 
 
 def test_lora_linear_workspace(L):
@@ -206,6 +208,7 @@ def test_mx_validation(L):
     assert upm(epi=3) == EINVAL
     assert upm(Y=P(BASE + 7 * 0x10000000 + 4096)) == EINVAL   # Y overlaps Bq
     assert upm(M=0, res=a(9), ldr=1024) == OK            # in-place residual is legal
+    assert upm(res=a(10), ldr=1 << 22) == EUNSUP         # 256 residual rows span 2 GiB
 
     def upq(**kw):
         args = dict(Xq=a(1), ldxq=1024, Xs=a(2), Wq=a(3), Ws=a(4), Tq=a(5), ldtq=640, Ts=a(6),
