@@ -60,6 +60,8 @@ def parse():
                     help="target host time of the oracle sample")
     ap.add_argument("--no-mx", action="store_true", help="skip the MXFP8 step")
     ap.add_argument("--no-attention", action="store_true", help="skip the dense attention call")
+    ap.add_argument("--no-shard", action="store_true",
+                    help="skip the step over one GPU's 1/8 share of the tokens")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 1 GiB device copy first (a known-size kernel for counters)")
     return ap.parse_args()
@@ -268,6 +270,45 @@ def mx_step(torch, M, u, eps, flops, bf16_ms, args):
                     "outside the step; flops counted as the bf16 step's (rank 576, K unpadded)"}
 
 
+def shard_step(torch, M, u, eps, args, shards=8):
+    """The bf16 step on one GPU's share of the 2K grid when the tokens are split
+    over `shards` GPUs (contiguous token ranges, weights replicated): the kernels
+    at the shape each GPU would run.  Nothing is exchanged between shards on
+    this path, so this is the per-GPU work of that configuration."""
+    from few_step_diffusion_amd.refine import StandinRefiner
+    Ms = M // shards
+    model = StandinRefiner(Ms, device=u.device)
+    us, es = u[:Ms].contiguous(), eps[:Ms].contiguous()
+    for _ in range(max(1, args.warmup)):
+        model.refine(us, es)
+    torch.cuda.synchronize()
+    step_events = []
+    torch.cuda._sleep(SPIN_CYCLES)
+    for _ in range(args.steps):
+        model.events = []
+        model.refine(us, es)
+        step_events.append(model.events)
+    torch.cuda.synchronize()
+    model.events = None
+    step_ms, per_kernel = [], {}
+    for ev in step_events:
+        step_ms.append(ev[0][1].elapsed_time(ev[-1][1]))
+        for k, v in kernel_times(ev).items():
+            per_kernel.setdefault(k, []).extend(v)
+    flops = model.flops_per_step()
+    ms = statistics.mean(step_ms)
+    dom_ms = statistics.mean(per_kernel[DOMINANT])
+    dom_tf = flops[DOMINANT] / 3 / (dom_ms * 1e-3) / 1e12
+    log(f"shard of 1/{shards}: {Ms} tokens, {ms:.2f} ms per step")
+    del model
+    return {"tokens": Ms, "shards": shards, "ms_per_step": round(ms, 3),
+            "tflops": round(sum(flops.values()) / (ms * 1e-3) / 1e12, 1),
+            "gate_up_up_tflops": round(dom_tf, 1),
+            "gate_up_up_frac_peak": round(dom_tf / PEAK_BF16_TFLOPS, 4),
+            "note": "the same step over one GPU's contiguous 1/8 of the 2K tokens; per-GPU "
+                    "figure, no collective on this path (not a measured multi-GPU run)"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -389,6 +430,10 @@ def main():
     log(f"graph + fused head/Euler: {g_ms:.2f} ms per step")
     del graphs, model
     torch.cuda.empty_cache()
+    if not args.no_shard:
+        log("step on a 1/8 token shard ...")
+        out["shard_2k_of_8"] = shard_step(torch, M, u, eps, args)
+        torch.cuda.empty_cache()
     if not args.no_mx:
         log("MXFP8 step ...")
         out["mxfp8"] = mx_step(torch, M, u, eps, flops, ms, args)
