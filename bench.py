@@ -52,7 +52,7 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=7)     # 21 launches of each linear kernel
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-elementwise", action="store_true")
@@ -179,6 +179,7 @@ def cpu_baseline(model_flops_per_token, target_s):
     dt = time.perf_counter() - t0
     tflops = tokens * model_flops_per_token / dt / 1e12
     return {"value": round(tflops, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "extrapolated_full_step_s": round(dt * 532800 / tokens, 1),
             "sample": f"{tokens} of 532,800 tokens of the same step (renoise + 3 stand-in "
                       f"velocity evaluations + Euler), fp64, {dt:.1f} s"}
 
