@@ -168,20 +168,26 @@ def cpu_baseline(model_flops_per_token, target_s):
     u, eps = inputs.latent(4, tokens=4096)
     u, eps = u.numpy(), eps.numpy()
     threads = oracle.default_threads()
-    # calibrate on one token per thread, then size the sample to the target time
+    # warm up and calibrate on one token per thread, then size the sample so
+    # that three timed runs take about target_s together; report their median
     t0 = time.perf_counter()
     oracle.standin_refine(u[:threads], eps[:threads], E, P, layers, nthreads=threads)
     t1 = time.perf_counter() - t0
-    tokens = int(max(threads, min(4096, threads * max(1.0, target_s / max(t1, 1e-3)))))
+    per_run = target_s / 3
+    tokens = int(max(threads, min(4096, threads * max(1.0, per_run / max(t1, 1e-3)))))
     tokens = (tokens // threads) * threads
-    t0 = time.perf_counter()
-    oracle.standin_refine(u[:tokens], eps[:tokens], E, P, layers, nthreads=threads)
-    dt = time.perf_counter() - t0
+    runs = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        oracle.standin_refine(u[:tokens], eps[:tokens], E, P, layers, nthreads=threads)
+        runs.append(time.perf_counter() - t0)
+    dt = statistics.median(runs)
     tflops = tokens * model_flops_per_token / dt / 1e12
     return {"value": round(tflops, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "extrapolated_full_step_s": round(dt * 532800 / tokens, 1),
             "sample": f"{tokens} of 532,800 tokens of the same step (renoise + 3 stand-in "
-                      f"velocity evaluations + Euler), fp64, {dt:.1f} s"}
+                      f"velocity evaluations + Euler), fp64; median of 3 runs of "
+                      f"{min(runs):.1f}-{max(runs):.1f} s after one warm-up"}
 
 
 def attention_2k(torch, fsd, M, args):
