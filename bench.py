@@ -319,8 +319,8 @@ def shard_step(torch, M, u, eps, args, shards=8):
 def main():
     args = parse()
     if args.gpus != 1:
-        sys.exit("bench.py runs on one GPU only: this build has no multi-GPU path "
-                 "(each GPU would take a contiguous token range; see DESIGN.md)")
+        sys.exit("bench.py runs on one GPU only: there is no multi-GPU path (each GPU "
+                 "would take a contiguous token range of the latent and exchange nothing)")
     import torch
     import few_step_diffusion_amd as fsd
     from few_step_diffusion_amd import inputs

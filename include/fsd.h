@@ -44,7 +44,7 @@ typedef enum {
   FSD_OK = 0,
   FSD_EINVAL = 1,        /* null pointer, bad size, bad ld, illegal aliasing, non-finite sigma */
   FSD_EALIGN = 2,        /* pointer or ld not 16-byte aligned                                   */
-  FSD_EUNSUPPORTED = 3,  /* valid request that this build does not implement                    */
+  FSD_EUNSUPPORTED = 3,  /* valid request that this library does not implement                  */
   FSD_EWORKSPACE = 4,    /* workspace null or too small                                         */
   FSD_EHIP = 5           /* the HIP runtime reported an error when launching                    */
 } fsd_status;
