@@ -178,6 +178,26 @@ def test_residual_short_k_and_tails(gpu, M, K, N, r):
     assert torch.equal(Y2.cpu(), Y.cpu())
 
 
+@pytest.mark.parametrize("epi", ["none", "swiglu"])
+def test_row_permutation_equivariance(gpu, epi):
+    """Permuting the rows of X permutes the rows of Y, bit for bit: a token's
+    output does not depend on where its row falls within a 256-row tile (ragged
+    M, a partial N tile, bias, LoRA; residual on the plain epilogue)."""
+    M, K, N = 700, 320, 320 if epi == "none" else 640
+    say(f"row permutation M={M} K={K} N={N} {epi}")
+    X = inputs.normal((M, K), 1.0, 61, dtype=torch.bfloat16).to(gpu)
+    W0 = inputs.normal((N, K), 0.05, 62, dtype=torch.bfloat16).to(gpu)
+    bias = inputs.normal((N,), 0.1, 63).to(gpu)
+    A, B, _, _ = merged(12, K, N, gpu, ranks=(32, 16, 16))
+    nout = N if epi == "none" else N // 2
+    R = inputs.normal((M, nout), 1.0, 64, dtype=torch.bfloat16).to(gpu) if epi == "none" else None
+    perm = torch.from_numpy(np.random.default_rng(65).permutation(M)).to(gpu)
+    Y = fsd.lora_linear(X, W0, A, B, bias=bias, residual=R, epilogue=epi)
+    Yp = fsd.lora_linear(X[perm].contiguous(), W0, A, B, bias=bias,
+                         residual=None if R is None else R[perm].contiguous(), epilogue=epi)
+    assert torch.equal(Yp, Y[perm])
+
+
 def test_strided_input_slice(gpu):
     M, D = 300, 256
     say(f"V-slice input M={M} D={D} ld=3D")
