@@ -277,6 +277,24 @@ def mx_step(torch, M, u, eps, flops, bf16_ms, args):
                     "outside the step; flops counted as the bf16 step's (rank 576, K unpadded)"}
 
 
+def lora_linear_shapes(per_kernel, flops, steps):
+    """The whole LoRA-fused linear (phase A + phase B) at the 2K grid's two
+    shapes, QKV (K = 3072, N = 9216) and O (K = N = 3072), from the step's own
+    launches: mean time per call and 2·M·(K·N + K·r + r·N) flops per call."""
+    out = {}
+    for name in ("qkv", "o"):
+        down, up = per_kernel[name + ".down"], per_kernel[name + ".up"]
+        ms = statistics.mean(down) + statistics.mean(up)
+        fl = (flops[name + ".down"] + flops[name + ".up"]) / 3
+        tf = fl / (ms * 1e-3) / 1e12
+        out[name] = {"ms_per_call": round(ms, 3), "tflops": round(tf, 1),
+                     "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4), "flops_per_call": fl,
+                     "calls_timed": len(up)}
+    out["note"] = ("phase A + phase B of one linear over 532,800 tokens, rank 576; the O "
+                   "linear's input is the V slice of the QKV output and it adds the residual")
+    return out
+
+
 def shard_step(torch, M, u, eps, args, shards=8):
     """The bf16 step on one GPU's share of the 2K grid when the tokens are split
     over `shards` GPUs (contiguous token ranges, weights replicated): the kernels
@@ -413,6 +431,7 @@ def main():
                                            PEAK_BF16_TFLOPS, 4),
                         "ms_per_step": round(lora_ms, 3)},
         "roofline": roofline,
+        "lora_linear_2k": lora_linear_shapes(per_kernel, flops, args.steps),
         "kernels": kernels,
     }
     # the same step as one HIP graph per sampler step with the Euler update fused
