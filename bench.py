@@ -43,6 +43,10 @@ PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA (MXFP8 scaled MFMA includ
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 DOMINANT = "gate_up.up"
 SPIN_CYCLES = 200_000          # ~0.1 ms GPU spin queued ahead of a timed region
+# ahead of a batch of short launches: long enough (~2 ms) for the host to queue
+# the whole batch through the binding before the GPU reaches the first event,
+# so the batch runs back to back without waiting on the host
+BATCH_SPIN_CYCLES = 4_000_000
 
 
 def log(*a):
@@ -129,7 +133,7 @@ def elementwise(torch, fsd, inputs, batches=5, per_batch=24):
                         fsd.euler_step(z, e, 0.909, 0.857)
                 ts = []
                 for rep in range(batches + 1):
-                    torch.cuda._sleep(SPIN_CYCLES)
+                    torch.cuda._sleep(BATCH_SPIN_CYCLES)
                     a = torch.cuda.Event(enable_timing=True)
                     b = torch.cuda.Event(enable_timing=True)
                     a.record()
