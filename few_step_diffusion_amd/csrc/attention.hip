@@ -53,11 +53,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
 }
 
-__device__ __forceinline__ float shfl_xor_f(float v, int mask) {
-  const int lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
-  return __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, __float_as_int(v)));
-}
-
 struct AttnParams {
   const bf16_t* Q; const bf16_t* K; const bf16_t* Vt;
   bf16_t* O;
@@ -190,8 +185,16 @@ void attention_kernel(AttnParams p) {
       for (int kj = 0; kj < 4; ++kj)
 #pragma unroll
         for (int t = 0; t < 4; ++t) mx = fmaxf(mx, s[qi][kj][t]);
-      mx = fmaxf(mx, shfl_xor_f(mx, 16));
-      mx = fmaxf(mx, shfl_xor_f(mx, 32));
+      // row maximum over lanes l, l^16, l^32, l^48: gfx950's row swaps give each
+      // lane the pair {x[l], x[l^16]} (then {x[l], x[l^32]}) without LDS
+      {
+        const auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                          false, false);
+        mx = fmaxf(__uint_as_float(p16[0]), __uint_as_float(p16[1]));
+        const auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                          false, false);
+        mx = fmaxf(__uint_as_float(p32[0]), __uint_as_float(p32[1]));
+      }
       const float m_blk = mx * p.scale_log2;
       const bool grow = m_blk > m_run[qi] + 8.0f;       // (always true for the first block)
       if (__builtin_amdgcn_ballot_w64(grow) != 0) {     // wave-uniform, rare
