@@ -21,6 +21,9 @@ Prints ONE JSON line on stdout (everything else goes to stderr):
   mxfp8      the step with the four linears as MXFP8 GEMMs (quantizers in the
              step time), the fused SwiGLU->MXFP8 gate/up GEMM against the
              5000 TFLOP/s fp8 peak
+  lora_linear_configs  the whole LoRA-fused linear at the 768P shape and on one
+             4K chunk (gate/up with SwiGLU chained into down with the
+             residual): median / min / max of 20 calls, and the median of 3
   attention  one dense attention call over the 2K grid as one sequence
              (532,800 tokens, 24 heads of 128), against 2500 TFLOP/s
   cpu_baseline the fp64 oracle on a bounded sample of tokens on host cores
@@ -64,6 +67,8 @@ def parse():
                     help="target host time of the oracle sample")
     ap.add_argument("--no-mx", action="store_true", help="skip the MXFP8 step")
     ap.add_argument("--no-attention", action="store_true", help="skip the dense attention call")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the LoRA linears at the 768P and 4K-chunk shapes")
     ap.add_argument("--no-shard", action="store_true",
                     help="skip the step over one GPU's 1/8 share of the tokens")
     ap.add_argument("--calib-copy", action="store_true",
@@ -299,6 +304,81 @@ def lora_linear_shapes(per_kernel, flops, steps):
     return out
 
 
+def lora_linear_configs(torch, fsd, reps=20, warm=5):
+    """The whole LoRA-fused linear (phase A + phase B in one library call) at
+    the 768P shape (149,184 tokens, K = N = 3072) and on one chunk of the 4K
+    grid (299,700 tokens): gate/up (K = 3072, N = 16384, SwiGLU to 8192)
+    chained into down (K = 8192, N = 3072) with the gate/up input as residual.
+    Seeded inputs of the workloads' shapes and distributions (activations drawn
+    on the device); each call is timed with HIP events on its stream; median,
+    min and max over `reps` calls after `warm` warm-up calls, plus the median
+    of the first 3 timed calls."""
+    from few_step_diffusion_amd import inputs
+    dev = torch.device("cuda:0")
+
+    def weights(wid, K, N, layer):
+        W0 = inputs.base_weight(wid, K, N, layer).to(dev)
+        A_l, B_l = inputs.adapters(wid, K, N, layer)
+        A, B = fsd.lora_merge([a.to(dev) for a in A_l], [b.to(dev) for b in B_l])
+        return W0, A, B
+
+    def timed(call):
+        for _ in range(warm):
+            call()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        torch.cuda._sleep(SPIN_CYCLES)
+        ev[0].record()
+        for i in range(reps):
+            call()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        return [ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]
+
+    def entry(ts, M, K, N, r):
+        fl = 2.0 * M * (K * N + K * r + r * N)
+        med = statistics.median(ts)
+        tf = fl / (med * 1e-3) / 1e12
+        return {"tokens": M, "K": K, "N": N, "r": r, "flops_per_call": fl,
+                "ms_median": round(med, 3), "ms_min": round(min(ts), 3),
+                "ms_max": round(max(ts), 3), "ms_median_of_3": round(statistics.median(ts[:3]), 3),
+                "tflops": round(tf, 1), "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                "base_equiv_frac_peak": round(2.0 * M * K * N / (med * 1e-3) / 1e12 /
+                                              PEAK_BF16_TFLOPS, 4)}
+
+    out = {}
+    wl = inputs.WORKLOADS[1]
+    M, (_, K, N, _) = wl.tokens, wl.linears[0]
+    W0, A, B = weights(1, K, N, 0)
+    X = inputs.activations(1, M, K, device=dev)
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(fsd.workspace_bytes(M, A.shape[0]), dtype=torch.uint8, device=dev)
+    ts = timed(lambda: fsd.lora_linear(X, W0, A, B, out=Y, workspace=ws))
+    out["768p"] = entry(ts, M, K, N, A.shape[0])
+    log(f"768P LoRA linear: {out['768p']['ms_median']:.3f} ms, {out['768p']['tflops']} TFLOP/s")
+    del W0, A, B, X, Y, ws
+
+    wl = inputs.WORKLOADS[3]
+    M = wl.tokens // wl.chunks
+    (_, K1, N1, _), (_, K2, N2, _) = wl.linears
+    Wg, Ag, Bg = weights(3, K1, N1, 1)
+    Wd, Ad, Bd = weights(3, K2, N2, 2)
+    X = inputs.activations(3, M, K1, device=dev)
+    H = torch.empty((M, N1 // 2), dtype=torch.bfloat16, device=dev)
+    Y = torch.empty((M, N2), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(fsd.workspace_bytes(M, Ag.shape[0]), dtype=torch.uint8, device=dev)
+    tg = timed(lambda: fsd.lora_linear(X, Wg, Ag, Bg, epilogue="swiglu", out=H, workspace=ws))
+    td = timed(lambda: fsd.lora_linear(H, Wd, Ad, Bd, residual=X, out=Y, workspace=ws))
+    out["4k_chunk_gate_up"] = entry(tg, M, K1, N1, Ag.shape[0])
+    out["4k_chunk_down"] = entry(td, M, K2, N2, Ad.shape[0])
+    log(f"4K chunk: gate/up {out['4k_chunk_gate_up']['ms_median']:.3f} ms, "
+        f"down {out['4k_chunk_down']['ms_median']:.3f} ms")
+    out["note"] = ("fsd_lora_linear calls (phase A + phase B); flops 2·M·(K·N + K·r + r·N) with "
+                   "r = 576; base_equiv_frac_peak counts 2·M·K·N only")
+    del Wg, Ag, Bg, Wd, Ad, Bd, X, H, Y, ws
+    return out
+
+
 def shard_step(torch, M, u, eps, args, shards=8):
     """The bf16 step on one GPU's share of the 2K grid when the tokens are split
     over `shards` GPUs (contiguous token ranges, weights replicated): the kernels
@@ -460,6 +540,10 @@ def main():
     log(f"graph + fused head/Euler: {g_ms:.2f} ms per step")
     del graphs, model
     torch.cuda.empty_cache()
+    if not args.no_configs:
+        log("LoRA linears at the 768P and 4K-chunk shapes ...")
+        out["lora_linear_configs"] = lora_linear_configs(torch, fsd)
+        torch.cuda.empty_cache()
     if not args.no_shard:
         log("step on a 1/8 token shard ...")
         out["shard_2k_of_8"] = shard_step(torch, M, u, eps, args)
