@@ -8,9 +8,11 @@ Euler update], sigma 0.909 -> 0.857 -> 0.667 -> 0.
 
 Prints ONE JSON line on stdout (everything else goes to stderr):
   value      algorithmic TFLOP/s of the whole step (inputs resident in HBM)
-  roofline   the dominant kernel (phase B of the gate/up linear, SwiGLU
-             epilogue): its algorithmic flops per launch / its mean launch
-             time from HIP events on its stream, against 2500 TFLOP/s bf16
+  roofline   the dominant kernel: the gate/up linear's pair launches (phase B
+             of a 21,760-token chunk with the SwiGLU epilogue, together with
+             phase A of the next chunk): their algorithmic flops per launch /
+             their mean launch time from HIP events on their stream, against
+             2500 TFLOP/s bf16
   kernels    the same for every kernel of the step
   elementwise  renoise / Euler GB/s at the 768P, 2K and 4K latents, 12 bytes
              per element: batches of back-to-back launches, cache-cold
@@ -44,7 +46,7 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA (MXFP8 scaled MFMA included)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
-DOMINANT = "gate_up.up"
+DOMINANT = "gate_up.pair"     # phase B of a gate/up chunk + phase A of the next, one launch
 SPIN_CYCLES = 200_000          # ~0.1 ms GPU spin queued ahead of a timed region
 # ahead of a batch of short launches: long enough (~2 ms) for the host to queue
 # the whole batch through the binding before the GPU reaches the first event,
@@ -239,6 +241,7 @@ def mx_step(torch, M, u, eps, flops, bf16_ms, args):
     against the fp8 MFMA peak."""
     from few_step_diffusion_amd.refine import StandinRefiner
     model = StandinRefiner(M, device=u.device, mx=True)
+    flops = model.flops_per_step()
     for _ in range(max(1, args.warmup)):
         model.refine(u, eps)
     torch.cuda.synchronize()
@@ -286,21 +289,32 @@ def mx_step(torch, M, u, eps, flops, bf16_ms, args):
                     "outside the step; flops counted as the bf16 step's (rank 576, K unpadded)"}
 
 
-def lora_linear_shapes(per_kernel, flops, steps):
-    """The whole LoRA-fused linear (phase A + phase B) at the 2K grid's two
-    shapes, QKV (K = 3072, N = 9216) and O (K = N = 3072), from the step's own
-    launches: mean time per call and 2·M·(K·N + K·r + r·N) flops per call."""
+def layer_ms_per_call(per_kernel, layer, steps, calls_per_step=3):
+    """Mean time of one call of a linear: all of its launches in the timed steps."""
+    tot = sum(sum(ts) for k, ts in per_kernel.items() if k.split(".")[0] == layer)
+    return tot / (steps * calls_per_step)
+
+
+def lora_linear_shapes(per_kernel, model, steps):
+    """The whole LoRA-fused linear (phase A + phase B, every launch of its
+    chunked schedule) at the 2K grid's two shapes, QKV (K = 3072, N = 9216) and
+    O (K = N = 3072), from the step's own launches: mean time per call and
+    2·M·(K·N + K·r + r·N) flops per call."""
     out = {}
+    lf = model.linear_flops()
     for name in ("qkv", "o"):
-        down, up = per_kernel[name + ".down"], per_kernel[name + ".up"]
-        ms = statistics.mean(down) + statistics.mean(up)
-        fl = (flops[name + ".down"] + flops[name + ".up"]) / 3
+        ms = layer_ms_per_call(per_kernel, name, steps)
+        fl = lf[name]
         tf = fl / (ms * 1e-3) / 1e12
         out[name] = {"ms_per_call": round(ms, 3), "tflops": round(tf, 1),
                      "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4), "flops_per_call": fl,
-                     "calls_timed": len(up)}
-    out["note"] = ("phase A + phase B of one linear over 532,800 tokens, rank 576; the O "
-                   "linear's input is the V slice of the QKV output and it adds the residual")
+                     "calls_timed": 3 * steps}
+    n, R, _ = __import__("few_step_diffusion_amd").lora_linear_plan(model.M, model.R,
+                                                                   model.ws.numel())
+    out["note"] = (f"phase A + phase B of one linear over {model.M:,} tokens, rank 576, in "
+                   f"{n} launches (chunks of {R} tokens, T in a {model.ws.numel() / 1e6:.1f} MB "
+                   "workspace); the O linear's input is the V slice of the QKV output and it "
+                   "adds the residual in place")
     return out
 
 
@@ -406,14 +420,14 @@ def shard_step(torch, M, u, eps, args, shards=8):
             per_kernel.setdefault(k, []).extend(v)
     flops = model.flops_per_step()
     ms = statistics.mean(step_ms)
-    dom_ms = statistics.mean(per_kernel[DOMINANT])
-    dom_tf = flops[DOMINANT] / 3 / (dom_ms * 1e-3) / 1e12
+    gu_ms = layer_ms_per_call(per_kernel, "gate_up", args.steps)
+    dom_tf = model.linear_flops()["gate_up"] / (gu_ms * 1e-3) / 1e12
     log(f"shard of 1/{shards}: {Ms} tokens, {ms:.2f} ms per step")
     del model
     return {"tokens": Ms, "shards": shards, "ms_per_step": round(ms, 3),
             "tflops": round(sum(flops.values()) / (ms * 1e-3) / 1e12, 1),
-            "gate_up_up_tflops": round(dom_tf, 1),
-            "gate_up_up_frac_peak": round(dom_tf / PEAK_BF16_TFLOPS, 4),
+            "gate_up_linear_tflops": round(dom_tf, 1),
+            "gate_up_linear_frac_peak": round(dom_tf / PEAK_BF16_TFLOPS, 4),
             "note": "the same step over one GPU's contiguous 1/8 of the 2K tokens; per-GPU "
                     "figure, no collective on this path (not a measured multi-GPU run)"}
 
@@ -481,25 +495,29 @@ def main():
                "median_us": round(statistics.median(ts) * 1e3, 1),
                "min_us": round(min(ts) * 1e3, 1), "max_us": round(max(ts) * 1e3, 1)}
         if name in flops:
-            per_launch = flops[name] / steps_per_refine
+            per_launch = flops[name] / (len(ts) / args.steps)
+            ent["flops_per_launch"] = per_launch
             ent["tflops"] = round(per_launch / (mean * 1e-3) / 1e12, 1)
             ent["frac_peak"] = round(ent["tflops"] / PEAK_BF16_TFLOPS, 4)
         if name in ("renoise", "euler"):
             ent["GB/s"] = round(12.0 * model.M * model.C / (mean * 1e-3) / 1e9, 1)
         kernels[name] = ent
-    lora_flops = sum(v for k, v in flops.items() if k.endswith(".down") or k.endswith(".up"))
-    lora_ms = sum(statistics.mean(per_kernel[k]) * len(per_kernel[k]) / args.steps
-                  for k in per_kernel if k.endswith(".down") or k.endswith(".up"))
+    lin_names = [k for k in per_kernel if k.split(".")[0] in StandinRefiner.LAYER_NAMES]
+    lora_flops = sum(v for k, v in flops.items() if k.split(".")[0] in StandinRefiner.LAYER_NAMES)
+    lora_ms = sum(sum(per_kernel[k]) / args.steps for k in lin_names)
     dom = kernels[DOMINANT]
+    dom_flops = dom["flops_per_launch"]
     L = model.layers[2]
-    dom_flops = 2 * M * (L["K"] + model.R) * L["N"]
-    traffic = measured_traffic("gemm_kernel<2, 4, true, false, false>")
-    roofline = {"kernel": "lora_up (phase B) of the gate/up linear, SwiGLU epilogue: "
-                          f"M={M} K={L['K']}+{model.R} N={L['N']}",
+    _, R, _ = fsd.lora_linear_plan(M, model.R, model.ws.numel())
+    traffic = measured_traffic("gemm_pair_kernel<true>")
+    roofline = {"kernel": "gate/up linear, one pair launch: phase B (SwiGLU epilogue) of a "
+                          f"{R}-token chunk, K={L['K']}+{model.R} N={L['N']}, with phase A "
+                          f"(K={L['K']} r={model.R}) of the next chunk",
                 "bound": "mfma", "achieved": round(dom_flops / (dom["mean_us"] * 1e-6) / 1e12, 1),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(dom_flops / (dom["mean_us"] * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                "traffic": traffic, "flops_per_launch": dom_flops}
+                "traffic": traffic, "flops_per_launch": dom_flops,
+                "launches_per_step": dom["launches_per_step"]}
     out = {
         "metric": "LoRA-linear TFLOP/s & % bf16 MFMA peak at 2K grid; renoise/Euler HBM GB/s",
         "value": round(value, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -515,7 +533,7 @@ def main():
                                            PEAK_BF16_TFLOPS, 4),
                         "ms_per_step": round(lora_ms, 3)},
         "roofline": roofline,
-        "lora_linear_2k": lora_linear_shapes(per_kernel, flops, args.steps),
+        "lora_linear_2k": lora_linear_shapes(per_kernel, model, args.steps),
         "kernels": kernels,
     }
     # the same step as one HIP graph per sampler step with the Euler update fused

@@ -15,7 +15,7 @@ import torch
 
 __all__ = [
     "FsdError", "library_path", "lib", "abi_version", "lora_merge", "workspace_bytes",
-    "lora_down", "lora_up", "lora_linear", "renoise", "euler_step", "token_embed",
+    "lora_down", "lora_up", "lora_linear", "lora_linear_plan", "renoise", "euler_step", "token_embed",
     "token_head", "token_head_euler", "mx_quantize", "mx_padded_k", "mx_scale_bytes",
     "mx_scale_offsets", "mx_pack_scales", "mx_unpack_scales", "mx_lora_down", "mx_lora_up",
     "mx_lora_up_swiglu_mx", "attention_workspace_bytes", "attention",
@@ -63,6 +63,11 @@ _SIGS = {
     "fsd_lora_linear": ([_c_void_p, _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                          _c_void_p, _i64, _f32, _c_void_p, _i64, _i64, _i64, _i64, _i64, _int,
                          _c_void_p, ctypes.c_size_t, _c_void_p], _int),
+    "fsd_lora_linear_plan": ([_i64, _i64, ctypes.c_size_t, ctypes.POINTER(_i64),
+                              ctypes.POINTER(_int)], _i64),
+    "fsd_lora_linear_launch": ([_c_void_p, _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                _c_void_p, _i64, _f32, _c_void_p, _i64, _i64, _i64, _i64, _i64,
+                                _int, _c_void_p, ctypes.c_size_t, _i64, _c_void_p], _int),
     "fsd_renoise": ([_c_void_p, _c_void_p, _f32, _c_void_p, _i64, _c_void_p], _int),
     "fsd_euler_step": ([_c_void_p, _c_void_p, _f32, _f32, _i64, _c_void_p], _int),
     "fsd_token_embed": ([_c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64, _i64, _c_void_p],
@@ -137,6 +142,19 @@ def _need(t: torch.Tensor, name: str, dtype, dims=2):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _shape(t: torch.Tensor, name: str, shape, contiguous=False, device=None):
+    """Raise ValueError unless t has exactly `shape` (and, if asked, is contiguous
+    and on `device`).  The C library sees only pointers and sizes, so a wrongly
+    sized buffer would be read or written out of bounds on the device: every
+    tensor's extent is checked here, before any launch."""
+    if tuple(t.shape) != tuple(int(d) for d in shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+
+
 def _ld(t: torch.Tensor) -> int:
     return t.stride(0) if t.size(0) > 1 else max(t.stride(0), t.size(1))
 
@@ -159,10 +177,17 @@ def lora_merge(A_list, B_list, scales=None, out_A=None, out_B=None):
             raise ValueError("inconsistent adapter shapes")
     R = sum(ranks)
     dev = A_list[0].device
+    for t in (*A_list, *B_list):
+        if t.device != dev:
+            raise ValueError("adapter factors must share one device")
     if out_A is None:
         out_A = torch.empty((R, K), dtype=torch.bfloat16, device=dev)
     if out_B is None:
         out_B = torch.empty((N, R), dtype=torch.bfloat16, device=dev)
+    _need(out_A, "out_A", torch.bfloat16)
+    _need(out_B, "out_B", torch.bfloat16)
+    _shape(out_A, "out_A", (R, K), contiguous=True, device=dev)
+    _shape(out_B, "out_B", (N, R), contiguous=True, device=dev)
     ap = (_c_void_p * n)(*[a.data_ptr() for a in A_list])
     bp = (_c_void_p * n)(*[b.data_ptr() for b in B_list])
     rk = (_i64 * n)(*ranks)
@@ -187,9 +212,11 @@ def lora_down(X, A, scale=1.0, T=None):
     _need(A, "A", torch.bfloat16)
     M, K = X.shape
     r = A.shape[0]
+    _shape(A, "A", (r, K), contiguous=True, device=X.device)
     if T is None:
         T = torch.empty((M, r), dtype=torch.bfloat16, device=X.device)
     _need(T, "T", torch.bfloat16)
+    _shape(T, "T", (M, r), device=X.device)
     st = lib().fsd_lora_down(_ptr(X), _ld(X), _ptr(A), float(scale), _ptr(T), _ld(T), M, K, r,
                              _stream(X))
     _check("fsd_lora_down", st)
@@ -206,6 +233,26 @@ def _epi(epilogue):
     return int(epilogue)
 
 
+def _linear_operands(X, W0, A, B, bias, residual, epilogue, r):
+    """Shape checks shared by the bf16 linear entry points (X, W0 already typed)."""
+    M, K = X.shape
+    N = W0.shape[0]
+    dev = X.device
+    _shape(W0, "W0", (N, K), contiguous=True, device=dev)
+    if r:
+        if A is not None:
+            _need(A, "A", torch.bfloat16)
+            _shape(A, "A", (r, K), contiguous=True, device=dev)
+        _need(B, "B", torch.bfloat16)
+        _shape(B, "B", (N, r), contiguous=True, device=dev)
+    if bias is not None:
+        _need(bias, "bias", torch.float32, dims=1)
+        _shape(bias, "bias", (N,), device=dev)
+    if residual is not None:
+        _need(residual, "residual", torch.bfloat16)
+        _shape(residual, "residual", (M, _out_cols(N, epilogue)), device=dev)
+
+
 def lora_up(X, W0, T, B, bias=None, residual=None, epilogue=EPI_NONE, out=None):
     """Phase B: Y = epi([X | T]·[W0 | B]ᵀ + bias) (+ residual)."""
     epilogue = _epi(epilogue)
@@ -214,16 +261,14 @@ def lora_up(X, W0, T, B, bias=None, residual=None, epilogue=EPI_NONE, out=None):
     M, K = X.shape
     N = W0.shape[0]
     r = 0 if B is None else B.shape[1]
+    _linear_operands(X, W0, None, B, bias, residual, epilogue, r)
     if r:
         _need(T, "T", torch.bfloat16)
-        _need(B, "B", torch.bfloat16)
-    if bias is not None:
-        _need(bias, "bias", torch.float32, dims=1)
-    if residual is not None:
-        _need(residual, "residual", torch.bfloat16)
+        _shape(T, "T", (M, r), device=X.device)
     if out is None:
         out = torch.empty((M, _out_cols(N, epilogue)), dtype=torch.bfloat16, device=X.device)
     _need(out, "out", torch.bfloat16)
+    _shape(out, "out", (M, _out_cols(N, epilogue)), device=X.device)
     st = lib().fsd_lora_up(_ptr(X), _ld(X), _ptr(W0), _ptr(T) if r else None,
                            _ld(T) if r else 0, _ptr(B) if r else None, _ptr(bias),
                            _ptr(residual), _ld(residual) if residual is not None else 0,
@@ -232,35 +277,56 @@ def lora_up(X, W0, T, B, bias=None, residual=None, epilogue=EPI_NONE, out=None):
     return out
 
 
+def lora_linear_plan(M: int, r: int, ws_bytes: int):
+    """(launches, rows per chunk, schedule) of fsd_lora_linear (see include/fsd.h)."""
+    R = _i64(0)
+    sched = _int(0)
+    n = lib().fsd_lora_linear_plan(int(M), int(r), int(ws_bytes), ctypes.byref(R),
+                                   ctypes.byref(sched))
+    if n < 0:
+        raise ValueError("negative M or r")
+    return int(n), int(R.value), int(sched.value)
+
+
 def lora_linear(X, W0, A, B, scale=1.0, bias=None, residual=None, epilogue=EPI_NONE,
-                out=None, workspace=None):
-    """Y = epi(X·W0ᵀ + scale·(X·Aᵀ)·Bᵀ + bias) (+ residual), phase A then phase B."""
+                out=None, workspace=None, on_launch=None):
+    """Y = epi(X·W0ᵀ + scale·(X·Aᵀ)·Bᵀ + bias) (+ residual): phase A then phase B,
+    chunked through a small workspace of T (fsd_lora_linear).
+
+    workspace: uint8 device tensor; default: workspace_bytes(M, r) (the library's
+    preferred size, 50.1 MB at r = 576 for M > 43,520).
+    on_launch: optional callable(index) run on the host before each kernel launch
+    of the schedule (e.g. to record timing events between launches); the
+    launches are then issued one by one through fsd_lora_linear_launch."""
     epilogue = _epi(epilogue)
     _need(X, "X", torch.bfloat16)
     _need(W0, "W0", torch.bfloat16)
     M, K = X.shape
     N = W0.shape[0]
     r = 0 if A is None else A.shape[0]
-    if r:
-        _need(A, "A", torch.bfloat16)
-        _need(B, "B", torch.bfloat16)
-    if bias is not None:
-        _need(bias, "bias", torch.float32, dims=1)
-    if residual is not None:
-        _need(residual, "residual", torch.bfloat16)
+    _linear_operands(X, W0, A, B, bias, residual, epilogue, r)
     if out is None:
         out = torch.empty((M, _out_cols(N, epilogue)), dtype=torch.bfloat16, device=X.device)
     _need(out, "out", torch.bfloat16)
+    _shape(out, "out", (M, _out_cols(N, epilogue)), device=X.device)
+    if workspace is not None and (workspace.device != X.device or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous tensor on X's device")
     if workspace is None and r:
         workspace = torch.empty(max(workspace_bytes(M, r), 16), dtype=torch.uint8,
                                 device=X.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib().fsd_lora_linear(_ptr(X), _ld(X), _ptr(W0), _ptr(A) if r else None,
-                               _ptr(B) if r else None, _ptr(bias), _ptr(residual),
-                               _ld(residual) if residual is not None else 0, float(scale),
-                               _ptr(out), _ld(out), M, N, K, r, epilogue, _ptr(workspace),
-                               ws_bytes, _stream(X))
-    _check("fsd_lora_linear", st)
+    args = (_ptr(X), _ld(X), _ptr(W0), _ptr(A) if r else None, _ptr(B) if r else None,
+            _ptr(bias), _ptr(residual), _ld(residual) if residual is not None else 0,
+            float(scale), _ptr(out), _ld(out), M, N, K, r, epilogue, _ptr(workspace), ws_bytes)
+    if on_launch is None:
+        st = lib().fsd_lora_linear(*args, _stream(X))
+        _check("fsd_lora_linear", st)
+        return out
+    n, _, _ = lora_linear_plan(M, r, ws_bytes)
+    for i in range(n):
+        on_launch(i)
+        st = lib().fsd_lora_linear_launch(*args, i, _stream(X))
+        _check("fsd_lora_linear_launch", st)
     return out
 
 
@@ -270,11 +336,12 @@ def renoise(u, eps, sigma, out=None):
     for t, nm in ((u, "u"), (eps, "eps")):
         if t.device.type != "cuda" or t.dtype != torch.float32 or not t.is_contiguous():
             raise ValueError(f"{nm} must be a contiguous fp32 GPU tensor")
-    if u.shape != eps.shape:
-        raise ValueError("u and eps shapes differ")
+    if u.shape != eps.shape or u.device != eps.device:
+        raise ValueError("u and eps shapes or devices differ")
     if out is None:
         out = torch.empty_like(u)
-    if out.shape != u.shape or out.dtype != torch.float32 or not out.is_contiguous():
+    if (out.shape != u.shape or out.dtype != torch.float32 or not out.is_contiguous()
+            or out.device != u.device):
         raise ValueError("out must be a contiguous fp32 tensor shaped like u")
     st = lib().fsd_renoise(_ptr(u), _ptr(eps), float(sigma), _ptr(out), u.numel(), _stream(u))
     _check("fsd_renoise", st)
@@ -286,8 +353,8 @@ def euler_step(z, v, sigma, sigma_next):
     for t, nm in ((z, "z"), (v, "v")):
         if t.device.type != "cuda" or t.dtype != torch.float32 or not t.is_contiguous():
             raise ValueError(f"{nm} must be a contiguous fp32 GPU tensor")
-    if z.numel() != v.numel():
-        raise ValueError("z and v sizes differ")
+    if z.numel() != v.numel() or z.device != v.device:
+        raise ValueError("z and v sizes or devices differ")
     st = lib().fsd_euler_step(_ptr(z), _ptr(v), float(sigma), float(sigma_next), z.numel(),
                               _stream(z))
     _check("fsd_euler_step", st)
@@ -302,9 +369,11 @@ def token_embed(z, E, out=None):
     _need(E, "E", torch.bfloat16)
     M, C = z.shape
     D = E.shape[0]
+    _shape(E, "E", (D, C), contiguous=True, device=z.device)
     if out is None:
         out = torch.empty((M, D), dtype=torch.bfloat16, device=z.device)
     _need(out, "out", torch.bfloat16)
+    _shape(out, "out", (M, D), device=z.device)
     st = lib().fsd_token_embed(_ptr(z), _ptr(E), _ptr(out), _ld(out), M, C, D, _stream(z))
     _check("fsd_token_embed", st)
     return out
@@ -316,10 +385,12 @@ def token_head(H, P, out=None):
     _need(P, "P", torch.bfloat16)
     M, D = H.shape
     C = P.shape[0]
+    _shape(P, "P", (C, D), contiguous=True, device=H.device)
     if out is None:
         out = torch.empty((M, C), dtype=torch.float32, device=H.device)
     if out.dtype != torch.float32 or not out.is_contiguous():
         raise ValueError("out must be a contiguous fp32 tensor")
+    _shape(out, "out", (M, C), device=H.device)
     st = lib().fsd_token_head(_ptr(H), _ld(H), _ptr(P), _ptr(out), M, D, C, _stream(H))
     _check("fsd_token_head", st)
     return out
@@ -331,8 +402,10 @@ def token_head_euler(H, P, z, sigma, sigma_next):
     _need(P, "P", torch.bfloat16)
     M, D = H.shape
     C = P.shape[0]
-    if z.dtype != torch.float32 or not z.is_contiguous() or tuple(z.shape[-2:]) != (M, C):
+    _shape(P, "P", (C, D), contiguous=True, device=H.device)
+    if z.dtype != torch.float32 or not z.is_contiguous():
         raise ValueError("z must be a contiguous fp32 [M, C] tensor")
+    _shape(z, "z", (M, C), device=H.device)
     st = lib().fsd_token_head_euler(_ptr(H), _ld(H), _ptr(P), _ptr(z), M, D, C, float(sigma),
                                     float(sigma_next), _stream(H))
     _check("fsd_token_head_euler", st)
@@ -353,6 +426,11 @@ def mx_quantize(X, Q=None, S=None):
         Q = torch.empty((M, Kp), dtype=torch.uint8, device=X.device)
     if S is None:
         S = torch.empty(int(lib().fsd_mx_scale_bytes(M, K)), dtype=torch.uint8, device=X.device)
+    _need(Q, "Q", torch.uint8)
+    _shape(Q, "Q", (M, Kp), device=X.device)
+    _need_scales(S, "S", M, Kp)
+    if S.device != X.device:
+        raise ValueError("S must be on X's device")
     st = lib().fsd_mx_quantize(_ptr(X), _ld(X), M, K, _ptr(Q), Q.stride(0), _ptr(S), _stream(X))
     _check("fsd_mx_quantize", st)
     return Q, S
@@ -412,9 +490,13 @@ def mx_lora_down(Xq, Xs, Aq, As, scale=1.0, T=None):
         raise ValueError("Aq must be a contiguous [r, Kp] tensor with Xq's Kp")
     _need_scales(Xs, "Xs", M, Kp)
     _need_scales(As, "As", r, Kp)
+    for t, nm in ((Aq, "Aq"), (Xs, "Xs"), (As, "As")):
+        if t.device != Xq.device:
+            raise ValueError(f"{nm} must be on Xq's device")
     if T is None:
         T = torch.empty((M, r), dtype=torch.bfloat16, device=Xq.device)
     _need(T, "T", torch.bfloat16)
+    _shape(T, "T", (M, r), device=Xq.device)
     st = lib().fsd_mx_lora_down(_ptr(Xq), _ld(Xq), _ptr(Xs), _ptr(Aq), _ptr(As), float(scale),
                                 _ptr(T), _ld(T), M, Kp, r, _stream(Xq))
     _check("fsd_mx_lora_down", st)
@@ -440,6 +522,11 @@ def _mx_up_operands(Xq, Xs, W0q, W0s, Tq, Ts, Bq, Bs, bias):
         _need_scales(Bs, "Bs", N, rp)
     if bias is not None:
         _need(bias, "bias", torch.float32, dims=1)
+        _shape(bias, "bias", (N,), device=Xq.device)
+    for t, nm in ((W0q, "W0q"), (Xs, "Xs"), (W0s, "W0s"), (Tq, "Tq"), (Ts, "Ts"), (Bq, "Bq"),
+                  (Bs, "Bs")):
+        if t is not None and t.device != Xq.device:
+            raise ValueError(f"{nm} must be on Xq's device")
     ops = (_ptr(Xq), _ld(Xq), _ptr(Xs), _ptr(W0q), _ptr(W0s), _ptr(Tq) if rp else None,
            _ld(Tq) if rp else 0, _ptr(Ts) if rp else None, _ptr(Bq) if rp else None,
            _ptr(Bs) if rp else None, _ptr(bias))
@@ -458,9 +545,11 @@ def mx_lora_up(Xq, Xs, W0q, W0s, Tq=None, Ts=None, Bq=None, Bs=None, bias=None,
     M, N, Kp, rp, ops = _mx_up_operands(Xq, Xs, W0q, W0s, Tq, Ts, Bq, Bs, bias)
     if residual is not None:
         _need(residual, "residual", torch.bfloat16)
+        _shape(residual, "residual", (M, _out_cols(N, epilogue)), device=Xq.device)
     if out is None:
         out = torch.empty((M, _out_cols(N, epilogue)), dtype=torch.bfloat16, device=Xq.device)
     _need(out, "out", torch.bfloat16)
+    _shape(out, "out", (M, _out_cols(N, epilogue)), device=Xq.device)
     st = lib().fsd_mx_lora_up(*ops, _ptr(residual),
                               _ld(residual) if residual is not None else 0, _ptr(out), _ld(out),
                               M, N, Kp, rp, epilogue, _stream(Xq))
@@ -482,6 +571,7 @@ def mx_lora_up_swiglu_mx(Xq, Xs, W0q, W0s, Tq=None, Ts=None, Bq=None, Bs=None, b
     if Hs is None:
         Hs = torch.empty(max(mx_scale_bytes(M, F), 4), dtype=torch.uint8, device=Xq.device)
     _need(Hq, "Hq", torch.uint8)
+    _shape(Hq, "Hq", (M, F), device=Xq.device)
     _need_scales(Hs, "Hs", M, F)
     st = lib().fsd_mx_lora_up_swiglu_mx(*ops, _ptr(Hq), _ld(Hq), _ptr(Hs), M, N, Kp, rp,
                                         _stream(Xq))
@@ -508,9 +598,14 @@ def attention(Q, K, V, heads, scale=None, out=None, workspace=None):
         raise ValueError("columns must be heads x head_dim")
     D = HD // heads
     scale = 1.0 / D ** 0.5 if scale is None else float(scale)
+    if K.device != Q.device or V.device != Q.device:
+        raise ValueError("Q, K and V must share one device")
     if out is None:
         out = torch.empty((S, HD), dtype=torch.bfloat16, device=Q.device)
     _need(out, "out", torch.bfloat16)
+    _shape(out, "out", (S, HD), device=Q.device)
+    if workspace is not None and (workspace.device != Q.device or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous tensor on Q's device")
     if workspace is None:
         workspace = torch.empty(max(attention_workspace_bytes(S, heads, D), 16), dtype=torch.uint8,
                                 device=Q.device)

@@ -15,6 +15,11 @@ using fsd::bf16_t;
 namespace {
 
 constexpr int64_t kTileM = 256;            // rows per GEMM tile: the chunk granule
+// Rows per chunk of the pipelined LoRA linear: 85 tile-rows, so that the 255
+// phase-A tiles (3 column tiles of 192 at rank 576) of the next chunk fill the
+// last wave of the current chunk's phase-B tiles on 256 CUs.  Two chunks of T
+// at rank 576 take 50.1 MB.
+constexpr int64_t kPairChunkRows = 85 * kTileM;
 constexpr int64_t kMaxOffsetBytes = 0x7fffffffLL;
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -207,8 +212,8 @@ extern "C" {
 
 int fsd_abi_version(void) { return FSD_ABI_VERSION; }
 
-const char* fsd_status_str(int status) {
-  switch (status) {
+const char* fsd_status_str(fsd_status status) {
+  switch ((int)status) {
     case FSD_OK: return "FSD_OK";
     case FSD_EINVAL: return "FSD_EINVAL";
     case FSD_EALIGN: return "FSD_EALIGN";
@@ -255,7 +260,8 @@ int fsd_lora_merge(int n_adapters, const float* const* A_list, const float* cons
 
 size_t fsd_lora_linear_workspace_bytes(int64_t M, int64_t r) {
   if (M <= 0 || r <= 0) return 0;
-  return (size_t)M * (size_t)r * 2u;
+  const int64_t rows = M < 2 * kPairChunkRows ? M : 2 * kPairChunkRows;
+  return (size_t)rows * (size_t)r * 2u;
 }
 
 int fsd_lora_down(const void* X, int64_t ldx, const void* A, float scale, void* T, int64_t ldt,
@@ -280,53 +286,168 @@ int fsd_lora_up(const void* X, int64_t ldx, const void* W0, const void* T, int64
   return from_hip(fsd::launch_gemm(kind, up_params(a), as_stream(stream)));
 }
 
+}  // extern "C"
+
+namespace {
+
+// The launch plan of the chunked LoRA linear (fsd_lora_linear): M rows at rank
+// r through a workspace that holds `fit` rows of T (at least min(M, 256)).
+//   SCHED_WHOLE: all M rows of T fit: phase A over all rows, then phase B;
+//   SCHED_PAIRS: two chunks of at least 256 rows fit: chunks of R <=
+//     kPairChunkRows rows (a multiple of 256) through two alternating halves of
+//     the workspace; launch 0 is phase A of chunk 0, launch c + 1 is phase B of
+//     chunk c together with phase A of chunk c + 1 (launch_gemm_pair);
+//   SCHED_CHUNKS: 256-row multiples through one buffer, phase A then phase B
+//     of each chunk.
+// Chunks start on 256-row boundaries, so every output row is computed by the
+// same tile arithmetic as without chunking: the result is bitwise identical.
+enum { SCHED_WHOLE = 0, SCHED_PAIRS = 1, SCHED_CHUNKS = 2 };
+struct Plan {
+  int sched;
+  int64_t R;         // rows per chunk
+  int64_t nc;        // chunks
+  int64_t launches;
+};
+
+Plan make_plan(int64_t M, int64_t r, int64_t ws_bytes) {
+  Plan pl{SCHED_WHOLE, M, M > 0 ? 1 : 0, 0};
+  if (M <= 0) return pl;
+  if (r == 0) { pl.launches = 1; return pl; }
+  const int64_t fit = ws_bytes / (r * 2);
+  if (fit >= M) { pl.launches = 2; return pl; }
+  if (fit >= 2 * kTileM) {
+    pl.sched = SCHED_PAIRS;
+    pl.R = (fit / 2) / kTileM * kTileM;
+    if (pl.R > kPairChunkRows) pl.R = kPairChunkRows;
+    pl.nc = (M + pl.R - 1) / pl.R;
+    pl.launches = pl.nc + 1;
+    return pl;
+  }
+  pl.sched = SCHED_CHUNKS;
+  pl.R = fit / kTileM * kTileM;
+  pl.nc = (M + pl.R - 1) / pl.R;
+  pl.launches = 2 * pl.nc;
+  return pl;
+}
+
+// Bytes of the workspace the plan touches.
+int64_t plan_workspace_bytes(const Plan& pl, int64_t M, int64_t r) {
+  if (r == 0 || M <= 0) return 0;
+  if (pl.sched == SCHED_WHOLE) return M * r * 2;
+  return (pl.sched == SCHED_PAIRS ? 2 : 1) * pl.R * r * 2;
+}
+
+// Launch `index` of the plan (arguments already validated).
+int lora_linear_launch(const UpShape& a, const void* A, float scale, void* workspace,
+                       const Plan& pl, int64_t index, hipStream_t s) {
+  const int64_t M = a.M, r = a.r, K = a.K;
+  const bool swiglu = a.epi == FSD_EPI_SWIGLU;
+  const fsd::GemmKind kind = swiglu ? fsd::GEMM_UP_SWIGLU : fsd::GEMM_UP;
+  auto rows = [&](int64_t c) { return c < pl.nc ? ((M - c * pl.R) < pl.R ? (M - c * pl.R) : pl.R) : 0; };
+  auto chunk_up = [&](int64_t c, const void* T) {
+    const int64_t m = c * pl.R;
+    UpShape u = a;
+    u.X = (const bf16_t*)a.X + m * a.ldx;
+    u.M = rows(c);
+    u.T = T;
+    u.ldt = r;
+    u.Y = (bf16_t*)a.Y + m * a.ldy;
+    if (a.residual) u.residual = (const bf16_t*)a.residual + m * a.ldr;
+    return up_params(u);
+  };
+  auto chunk_down = [&](int64_t c, void* T) {
+    const int64_t mc = rows(c);
+    const int64_t m = mc > 0 ? c * pl.R : 0;
+    return down_params((const bf16_t*)a.X + m * a.ldx, a.ldx, A, scale, T, r, mc, K, r);
+  };
+  if (index < 0 || index >= pl.launches) return FSD_EINVAL;
+  if (r == 0) return from_hip(fsd::launch_gemm(kind, chunk_up(0, nullptr), s));
+  switch (pl.sched) {
+    case SCHED_WHOLE:
+      return from_hip(index == 0 ? fsd::launch_gemm(fsd::GEMM_DOWN, chunk_down(0, workspace), s)
+                                 : fsd::launch_gemm(kind, chunk_up(0, workspace), s));
+    case SCHED_PAIRS: {
+      void* buf[2] = {workspace, (char*)workspace + pl.R * r * 2};
+      if (index == 0) return from_hip(fsd::launch_gemm(fsd::GEMM_DOWN, chunk_down(0, buf[0]), s));
+      const int64_t c = index - 1;
+      return from_hip(fsd::launch_gemm_pair(swiglu, chunk_up(c, buf[c & 1]),
+                                            chunk_down(c + 1, buf[(c + 1) & 1]), s));
+    }
+    default: {
+      const int64_t c = index / 2;
+      return from_hip((index & 1) == 0
+                          ? fsd::launch_gemm(fsd::GEMM_DOWN, chunk_down(c, workspace), s)
+                          : fsd::launch_gemm(kind, chunk_up(c, workspace), s));
+    }
+  }
+}
+
+// Validation of fsd_lora_linear's arguments against a workspace of ws_bytes.
+int validate_linear(const UpShape& a, const void* A, float scale, const void* workspace,
+                    int64_t ws_bytes) {
+  int st = validate_up(a, false);
+  if (st != FSD_OK) return st;
+  if (!isfinite(scale)) return FSD_EINVAL;
+  if (a.r == 0) return FSD_OK;
+  const int64_t M = a.M, N = a.N, K = a.K, r = a.r;
+  if (!A) return FSD_EINVAL;
+  if (!aligned16(A)) return FSD_EALIGN;
+  if ((r + kTileM) * K * 2 > kMaxOffsetBytes) return FSD_EUNSUPPORTED;
+  const int64_t need_min = (M < kTileM ? M : kTileM) * r * 2;
+  if (M > 0 && (!workspace || ws_bytes < need_min)) return FSD_EWORKSPACE;
+  if (workspace && !aligned16(workspace)) return FSD_EALIGN;
+  const int64_t nout = a.epi == FSD_EPI_SWIGLU ? N / 2 : N;
+  const int64_t wbytes = plan_workspace_bytes(make_plan(M, r, ws_bytes), M, r);
+  if (overlap(a.Y, span_bytes(M, nout, a.ldy, 2), workspace, wbytes) ||
+      overlap(workspace, wbytes, a.X, span_bytes(M, K, a.ldx, 2)) ||
+      overlap(workspace, wbytes, a.W0, N * K * 2) || overlap(workspace, wbytes, A, r * K * 2) ||
+      overlap(workspace, wbytes, a.B, N * r * 2) ||
+      overlap(workspace, wbytes, a.bias, a.bias ? N * 4 : 0) ||
+      overlap(workspace, wbytes, a.residual, a.residual ? span_bytes(M, nout, a.ldr, 2) : 0))
+    return FSD_EINVAL;
+  return FSD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t fsd_lora_linear_plan(int64_t M, int64_t r, size_t workspace_bytes, int64_t* chunk_rows,
+                             int* schedule) {
+  if (M < 0 || r < 0) return -1;
+  const int64_t ws = workspace_bytes > (size_t)INT64_MAX ? INT64_MAX : (int64_t)workspace_bytes;
+  const Plan pl = make_plan(M, r, ws);
+  if (chunk_rows) *chunk_rows = pl.R;
+  if (schedule) *schedule = pl.sched;
+  return pl.launches;
+}
+
+int fsd_lora_linear_launch(const void* X, int64_t ldx, const void* W0, const void* A,
+                           const void* B, const float* bias, const void* residual, int64_t ldr,
+                           float scale, void* Y, int64_t ldy, int64_t M, int64_t N, int64_t K,
+                           int64_t r, int epilogue, void* workspace, size_t workspace_bytes,
+                           int64_t index, void* stream) {
+  const UpShape a{X, W0, workspace, B, ldx, r, bias, residual, ldr, Y, ldy, M, N, K, r, epilogue};
+  const int64_t ws = workspace_bytes > (size_t)INT64_MAX ? INT64_MAX : (int64_t)workspace_bytes;
+  const int st = validate_linear(a, A, scale, workspace, ws);
+  if (st != FSD_OK) return st;
+  const Plan pl = make_plan(M, r, ws);
+  if (index < 0 || index >= pl.launches) return M == 0 && index == 0 ? FSD_OK : FSD_EINVAL;
+  return lora_linear_launch(a, A, scale, workspace, pl, index, as_stream(stream));
+}
+
 int fsd_lora_linear(const void* X, int64_t ldx, const void* W0, const void* A, const void* B,
                     const float* bias, const void* residual, int64_t ldr, float scale, void* Y,
                     int64_t ldy, int64_t M, int64_t N, int64_t K, int64_t r, int epilogue,
                     void* workspace, size_t workspace_bytes, void* stream) {
-  UpShape a{X, W0, workspace, B, ldx, r, bias, residual, ldr, Y, ldy, M, N, K, r, epilogue};
-  int st = validate_up(a, false);
+  const UpShape a{X, W0, workspace, B, ldx, r, bias, residual, ldr, Y, ldy, M, N, K, r, epilogue};
+  const int64_t ws = workspace_bytes > (size_t)INT64_MAX ? INT64_MAX : (int64_t)workspace_bytes;
+  const int st = validate_linear(a, A, scale, workspace, ws);
   if (st != FSD_OK) return st;
-  if (!isfinite(scale)) return FSD_EINVAL;
-  int64_t chunk = M;
-  if (r > 0) {
-    if (!A) return FSD_EINVAL;
-    if (!aligned16(A)) return FSD_EALIGN;
-    if ((r + kTileM) * K * 2 > kMaxOffsetBytes) return FSD_EUNSUPPORTED;
-    const int64_t need_min = (M < kTileM ? M : kTileM) * r * 2;
-    if (M > 0 && (!workspace || (int64_t)workspace_bytes < need_min)) return FSD_EWORKSPACE;
-    if (workspace && !aligned16(workspace)) return FSD_EALIGN;
-    const int64_t fit = (int64_t)(workspace_bytes / (size_t)(r * 2));
-    if (fit < M) chunk = (fit / kTileM) * kTileM;
-    if (M > 0 && chunk < 1) return FSD_EWORKSPACE;
-    const int64_t nout = epilogue == FSD_EPI_SWIGLU ? N / 2 : N;
-    const int64_t wbytes = (chunk < M ? chunk : M) * r * 2;
-    if (overlap(Y, span_bytes(M, nout, ldy, 2), workspace, wbytes) ||
-        overlap(workspace, wbytes, X, span_bytes(M, K, ldx, 2)) ||
-        overlap(workspace, wbytes, W0, N * K * 2) || overlap(workspace, wbytes, A, r * K * 2) ||
-        overlap(workspace, wbytes, B, N * r * 2) ||
-        overlap(workspace, wbytes, bias, bias ? N * 4 : 0) ||
-        overlap(workspace, wbytes, residual, residual ? span_bytes(M, nout, ldr, 2) : 0))
-      return FSD_EINVAL;
-  }
-  if (M == 0) return FSD_OK;
-  hipStream_t s = as_stream(stream);
-  const fsd::GemmKind kind = epilogue == FSD_EPI_SWIGLU ? fsd::GEMM_UP_SWIGLU : fsd::GEMM_UP;
-  for (int64_t m = 0; m < M; m += chunk) {
-    const int64_t mc = (M - m) < chunk ? (M - m) : chunk;
-    const bf16_t* Xc = (const bf16_t*)X + m * ldx;
-    if (r > 0) {
-      const hipError_t e = fsd::launch_gemm(
-          fsd::GEMM_DOWN, down_params(Xc, ldx, A, scale, workspace, r, mc, K, r), s);
-      if (e != hipSuccess) return FSD_EHIP;
-    }
-    UpShape c = a;
-    c.X = Xc;
-    c.M = mc;
-    c.Y = (bf16_t*)Y + m * ldy;
-    if (residual) c.residual = (const bf16_t*)residual + m * ldr;
-    const hipError_t e = fsd::launch_gemm(kind, up_params(c), s);
-    if (e != hipSuccess) return FSD_EHIP;
+  const Plan pl = make_plan(M, r, ws);
+  for (int64_t i = 0; i < pl.launches; ++i) {
+    const int e = lora_linear_launch(a, A, scale, workspace, pl, i, as_stream(stream));
+    if (e != FSD_OK) return e;
   }
   return FSD_OK;
 }

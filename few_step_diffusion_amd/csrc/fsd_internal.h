@@ -48,6 +48,10 @@ enum GemmKind {
 };
 
 hipError_t launch_gemm(GemmKind kind, const GemmParams& p, hipStream_t s);
+// Phase B of one chunk (pb: GEMM_UP, or GEMM_UP_SWIGLU when swiglu) and phase A
+// of the next (pa: GEMM_DOWN) in one launch; either may have M == 0.
+hipError_t launch_gemm_pair(bool swiglu, const GemmParams& pb, const GemmParams& pa,
+                            hipStream_t s);
 
 hipError_t launch_renoise(const float* u, const float* eps, float sigma, float* z,
                           int64_t n, hipStream_t s);

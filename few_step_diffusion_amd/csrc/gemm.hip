@@ -116,9 +116,12 @@ __device__ __forceinline__ void static_for(Fn&& fn) {
 // MX: E4M3 operands with E8M0 block scales (v_mfma_scale_f32_16x16x128_f8f6f4):
 // a K step is 128 elements, still one 128-byte line per tile row.
 // QOUT (with SWIGLU): H leaves as MXFP8 (E4M3 bytes and scales) instead of bf16.
+constexpr int kLdsBytes = 160 * 1024;      // gfx950's LDS per CU: every tile shape fits
+
+// One output tile of one GEMM (workgroup `wg` of the launch's tiles of this
+// GEMM), staged through `lds` (kLdsBytes).
 template <int WM, int WN, bool SWIGLU, bool MX, bool QOUT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void gemm_kernel(GemmParams p) {
+__device__ __forceinline__ void gemm_tile(const GemmParams& p, const int wg, char* lds) {
   constexpr int ESZ = MX ? 1 : 2;           // bytes per element
   constexpr int KSTEP = ROWB / ESZ;         // elements per K step
   constexpr int BM = kWaveRows * WM * 32;
@@ -129,9 +132,8 @@ void gemm_kernel(GemmParams p) {
   constexpr int B_STAGE = BN * ROWB;
   constexpr int B_BASE = NSLOT_A * A_STAGE; // LDS: [A slots | B slots]
   constexpr int LDS_BYTES = NSLOT_A * A_STAGE + NSLOT_B * B_STAGE;
-  static_assert(LDS_BYTES <= 160 * 1024, "gfx950 has 160 KB of LDS per CU");
+  static_assert(LDS_BYTES <= kLdsBytes, "gfx950 has 160 KB of LDS per CU");
   static_assert(!SWIGLU || (WN % 2 == 0), "SwiGLU pairs gate and up blocks within a wave");
-  __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
 
   // ---- which tile ---------------------------------------------------------
   const int64_t M = p.M;
@@ -142,7 +144,6 @@ void gemm_kernel(GemmParams p) {
   const int tiles_m = (int)((M + BM - 1) / BM);
   const int tiles_n = (int)((Nout + TN - 1) / TN);
   const int total = tiles_m * tiles_n;
-  const int wg = blockIdx.x;
   const int xcd = wg & 7, local = wg >> 3;
   const int per = total >> 3, rem = total & 7;
   const int L = xcd * per + (xcd < rem ? xcd : rem) + local;
@@ -702,6 +703,38 @@ void gemm_kernel(GemmParams p) {
   }
 }
 
+template <int WM, int WN, bool SWIGLU, bool MX, bool QOUT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_kernel(GemmParams p) {
+  __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
+  gemm_tile<WM, WN, SWIGLU, MX, QOUT>(p, blockIdx.x, lds);
+}
+
+// Two independent GEMMs in one launch: workgroups [0, nb) are the tiles of
+// phase B (pb: 256 x 256 tiles, plain or SwiGLU epilogue) of one chunk of rows,
+// workgroups [nb, nb + na) the phase-A tiles (pa: 256 x 192) of the next
+// chunk.  Workgroups start in id order, so the shorter phase-A tiles fill the
+// CUs that phase B's last wave leaves idle, instead of a launch of their own
+// ramping up and draining.  The two GEMMs share no buffer: phase B reads the T
+// that the previous launch wrote, phase A writes the other half of the
+// workspace.
+template <bool SWIGLU>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_pair_kernel(GemmParams pb, GemmParams pa, int nb) {
+  __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
+  const int wg = blockIdx.x;
+  if (wg < nb) gemm_tile<2, 4, SWIGLU, false, false>(pb, wg, lds);
+  else gemm_tile<2, 3, false, false, false>(pa, wg - nb, lds);
+}
+
+template <int WM, int WN, bool SWIGLU>
+int64_t tile_count(const GemmParams& p) {
+  constexpr int BM = kWaveRows * WM * 32;
+  constexpr int TN = (SWIGLU ? 16 : 32) * kWaveCols * WN;
+  const int64_t nout = SWIGLU ? p.N / 2 : p.N;
+  return ((p.M + BM - 1) / BM) * ((nout + TN - 1) / TN);
+}
+
 template <int WM, int WN, bool SWIGLU, bool MX, bool QOUT = false>
 hipError_t launch(const GemmParams& p, hipStream_t s) {
   constexpr int BM = kWaveRows * WM * 32;
@@ -728,6 +761,18 @@ hipError_t launch_gemm(GemmKind kind, const GemmParams& p, hipStream_t s) {
     case GEMM_MX_UP_SWIGLU_MX: return launch<2, 4, true, true, true>(p, s);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm_pair(bool swiglu, const GemmParams& pb, const GemmParams& pa,
+                            hipStream_t s) {
+  const int64_t nb = swiglu ? tile_count<2, 4, true>(pb) : tile_count<2, 4, false>(pb);
+  const int64_t na = tile_count<2, 3, false>(pa);
+  if (nb <= 0 && na <= 0) return hipSuccess;
+  if (nb + na > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(nb + na));
+  if (swiglu) hipLaunchKernelGGL(gemm_pair_kernel<true>, grid, dim3(kThreads), 0, s, pb, pa, (int)nb);
+  else hipLaunchKernelGGL(gemm_pair_kernel<false>, grid, dim3(kThreads), 0, s, pb, pa, (int)nb);
+  return hipGetLastError();
 }
 
 }  // namespace fsd

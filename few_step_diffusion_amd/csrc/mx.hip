@@ -1,8 +1,8 @@
 // MXFP8 (E4M3 elements, E8M0 scales per 32 elements) for the linears of the
 // refiner.
 //
-// The pages run the refiner's linears as "MXFP8 linear layers: FP8 GEMMs,
-// re-quantized per stage", with SwiGLU fused into a one-pass activation
+// The pages run the refiner's linears in MXFP8 (FP8 GEMMs whose operands are
+// quantized again at every stage), with SwiGLU fused into a one-pass activation
 // quantizer ("Open-H3-Regenerate-2K: High-Resolution Video Refinement with
 // Few-Step Diffusion", agientry.com, section "Where the 3.9x speedup comes
 // from", inference-configuration table).  They fix no block size, scale rule or

@@ -57,7 +57,13 @@ class StandinRefiner:
         self.h = torch.empty((M, D), dtype=bf, device=dev)            # residual stream
         self.qkv = torch.empty((M, 3 * D), dtype=bf, device=dev)
         self.g = torch.empty((M, F), dtype=bf, device=dev)            # SwiGLU output
-        self.T = torch.empty((M, self.R), dtype=bf, device=dev)      # LoRA down output
+        if mx:
+            self.T = torch.empty((M, self.R), dtype=bf, device=dev)  # LoRA down output
+        else:
+            # T of the bf16 linears: two chunks of 21,760 rows (50 MB at rank 576),
+            # shared by the four linears (they run one after another on one stream)
+            self.ws = torch.empty(max(fsd.workspace_bytes(M, self.R), 16), dtype=torch.uint8,
+                                  device=dev)
         self.v = torch.empty((M, C), dtype=torch.float32, device=dev)
         self.z = torch.empty((M, C), dtype=torch.float32, device=dev)
         if mx:
@@ -72,14 +78,24 @@ class StandinRefiner:
             del self.g
         self.events = None
 
-    # one LoRA linear = phase A + phase B (two kernels)
+    def launch_names(self):
+        """Mark name of each launch of one bf16 LoRA linear over this refiner's
+        tokens: phase A then phase B ('down', 'up'), or, chunked, phase A of the
+        first chunk ('down0') followed by phase-B / next-phase-A pairs ('pair')."""
+        n, _, sched = fsd.lora_linear_plan(self.M, self.R, self.ws.numel())
+        if sched == 1:
+            return ["down0"] + ["pair"] * (n - 1)
+        return ["down", "up"] * (n // 2)
+
+    # one LoRA linear = phase A + phase B through the chunked schedule
     def _linear(self, idx, X, out, residual=None, epilogue=fsd.EPI_NONE):
         L = self.layers[idx]
-        T = self.T[: X.shape[0]]
-        self._mark(f"{self.LAYER_NAMES[idx]}.down")
-        fsd.lora_down(X, L["A"], self.scale, T)
-        self._mark(f"{self.LAYER_NAMES[idx]}.up")
-        fsd.lora_up(X, L["W0"], T, L["B"], residual=residual, epilogue=epilogue, out=out)
+        hook = None
+        if self.events is not None:
+            names = self.launch_names()
+            hook = lambda i: self._mark(f"{self.LAYER_NAMES[idx]}.{names[i]}")
+        fsd.lora_linear(X, L["W0"], L["A"], L["B"], self.scale, residual=residual,
+                        epilogue=epilogue, out=out, workspace=self.ws, on_launch=hook)
 
     def _mark(self, name):
         if self.events is not None:
@@ -183,14 +199,32 @@ class StandinRefiner:
         return self.z
 
     def flops_per_step(self) -> dict:
-        """Algorithmic flops of one refine (all sigma steps): 2M(KN + Kr + rN) per linear."""
+        """Algorithmic flops of one refine (all sigma steps) per launch mark name:
+        2M(KN + Kr + rN) per linear, split over its launches (phase A of a chunk
+        2·Mc·K·r, phase B 2·Mc·(K + r)·N), plus embed and head."""
         M, D, F, C, r = self.M, self.D, self.F, self.C, self.R
         steps = len(SIGMAS) - 1
         out = {}
         for L, name in zip(self.layers, self.LAYER_NAMES):
             K, N = L["K"], L["N"]
-            out[name + ".down"] = 2 * M * K * r * steps
-            out[name + ".up"] = 2 * M * (K + r) * N * steps
+            down, up = 2 * M * K * r, 2 * M * (K + r) * N
+            if self.mx:
+                out[name + ".down"] = down * steps
+                out[name + ".up"] = up * steps
+                continue
+            n, R, sched = fsd.lora_linear_plan(M, r, self.ws.numel())
+            if sched == 1:
+                first = 2 * min(M, R) * K * r
+                out[name + ".down0"] = first * steps
+                out[name + ".pair"] = (down - first + up) * steps
+            else:
+                out[name + ".down"] = down * steps
+                out[name + ".up"] = up * steps
         out["embed"] = 2 * M * C * D * steps
         out["head"] = 2 * M * D * C * steps
         return out
+
+    def linear_flops(self) -> dict:
+        """Algorithmic flops of one call of each linear, 2M(KN + Kr + rN)."""
+        return {name: 2 * self.M * (L["K"] * L["N"] + L["K"] * self.R + self.R * L["N"])
+                for L, name in zip(self.layers, self.LAYER_NAMES)}

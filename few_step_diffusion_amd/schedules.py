@@ -4,8 +4,8 @@ REFINE: the three-step refiner, 0.909 -> 0.857 -> 0.667 -> 0 ("Open-H3-Regenerat
 High-Resolution Video Refinement with Few-Step Diffusion", agientry.com, section
 "Three steps instead of dozens", schedule equation).
 
-In-context routes ("Open-H3-Regenerate-2K：MiniMax H3 的开源 4K 精修方案", comfyui-wiki.com,
-section "三步接着放大的草稿画，八步从噪声重画"): one 8-step noise table with video shift 12;
+In-context routes ("Open-H3-Regenerate-2K-IC:草稿留在上下文里,2K 与 4K 重绘仍对着原来的脸、口型和字",
+wujieai.com, section "三步接着放大的草稿画,八步从噪声重画"): one 8-step noise table with video shift 12;
 up3 mixes the upscaled draft latent to sigma 0.835 and takes the table's last three
 steps, up4 mixes to 0.923 and takes four, hf8 starts from noise at sigma 1 and takes
 all eight; the reference row is renoised at sigma 0.001 (99.9% draft).  The pages

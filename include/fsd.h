@@ -57,8 +57,9 @@ typedef enum {
 /* Version of this header's ABI (FSD_ABI_VERSION). */
 int fsd_abi_version(void);
 
-/* Static, NUL-terminated name of a status code ("FSD_OK", ...); never NULL. */
-const char* fsd_status_str(int status);
+/* Static, NUL-terminated name of a status code ("FSD_OK", ...); never NULL
+ * (values outside fsd_status give "FSD_UNKNOWN"). */
+const char* fsd_status_str(fsd_status status);
 
 /* ------------------------------------------------------------------------ *
  * a0. Rank-axis merge of several LoRA adapters into one                      *
@@ -126,7 +127,9 @@ int fsd_lora_merge(int n_adapters, const float* const* A_list,
  * Aliasing: Y must not overlap X, W0, A, B, bias or the workspace.
  */
 
-/* Bytes of workspace phase A needs for M rows at rank r (M*r*2). */
+/* Bytes of workspace with which fsd_lora_linear runs its preferred schedule
+ * for M rows at rank r: min(M, 43,520)·r·2 (50.1 MB at r = 576, all rows of T
+ * when M <= 43,520).  0 when M <= 0 or r <= 0. */
 size_t fsd_lora_linear_workspace_bytes(int64_t M, int64_t r);
 
 /* Phase A alone.  T: bf16 [M, r] with row stride ldt >= r. */
@@ -142,16 +145,49 @@ int fsd_lora_up(const void* X, int64_t ldx, const void* W0, const void* T,
                 int64_t M, int64_t N, int64_t K, int64_t r, int epilogue,
                 void* stream);
 
-/* Phase A then phase B, chunked over M so that T fits in the workspace.
- * workspace_bytes must hold at least min(M, 256) rows of T
- * (fsd_lora_linear_workspace_bytes(min(M, 256), r)); more lets the chunks be
- * larger (one chunk when it holds all M rows).  With r == 0 the workspace
- * may be NULL. */
+/* Phase A then phase B, chunked over M so that T stays in a small workspace
+ * (bf16, T of a chunk at row stride r).  workspace_bytes must hold at least
+ * min(M, 256) rows of T (fsd_lora_linear_workspace_bytes(min(M, 256), r),
+ * else FSD_EWORKSPACE); with r == 0 the workspace may be NULL.  Schedule,
+ * from the rows of T that fit ("fit"):
+ *   fit >= M: phase A over all rows, then phase B (two launches);
+ *   fit >= 512: chunks of R rows, R = min(21,760, 256·floor(fit/512)), through
+ *     two alternating halves of the workspace: launch 0 is phase A of chunk 0,
+ *     launch c + 1 is phase B of chunk c together with phase A of chunk c + 1
+ *     in one grid, so phase A's tiles fill the CUs that phase B's last wave
+ *     leaves idle (21,760 rows = 85 row tiles: its 255 phase-A tiles fill one
+ *     wave of 256 CUs);
+ *   otherwise: 256-row chunks, phase A then phase B each.
+ * Chunks start on 256-row boundaries, so the result is bitwise identical to
+ * the unchunked one whatever the workspace size.  The workspace is read and
+ * written only by this call's kernels; it need not be initialised. */
 int fsd_lora_linear(const void* X, int64_t ldx, const void* W0, const void* A,
                     const void* B, const float* bias, const void* residual,
                     int64_t ldr, float scale, void* Y, int64_t ldy, int64_t M,
                     int64_t N, int64_t K, int64_t r, int epilogue,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* The schedule of fsd_lora_linear for M rows at rank r and a workspace of
+ * workspace_bytes bytes: returns its number of kernel launches (0 when
+ * M == 0; -1 for M < 0 or r < 0) and stores the rows per chunk in *chunk_rows
+ * and the schedule in *schedule (0: phase A then phase B over all rows;
+ * 1: pipelined pairs; 2: chunks of phase A then phase B), each when non-NULL.
+ * Host-only arithmetic: no HIP call. */
+int64_t fsd_lora_linear_plan(int64_t M, int64_t r, size_t workspace_bytes,
+                             int64_t* chunk_rows, int* schedule);
+
+/* Launch number `index` (0 <= index < fsd_lora_linear_plan(...)) of
+ * fsd_lora_linear with the same arguments; calling every index in order, on one
+ * stream, is exactly fsd_lora_linear.  Lets a caller place its own work (timing
+ * events, captures) between the launches.  Same validation and errors as
+ * fsd_lora_linear, plus FSD_EINVAL for an index out of range (index 0 with
+ * M == 0 is a no-op). */
+int fsd_lora_linear_launch(const void* X, int64_t ldx, const void* W0,
+                           const void* A, const void* B, const float* bias,
+                           const void* residual, int64_t ldr, float scale,
+                           void* Y, int64_t ldy, int64_t M, int64_t N,
+                           int64_t K, int64_t r, int epilogue, void* workspace,
+                           size_t workspace_bytes, int64_t index, void* stream);
 
 /* ------------------------------------------------------------------------ *
  * a1. Partial renoise                                                        *
@@ -216,7 +252,7 @@ int fsd_token_head_euler(const void* H, int64_t ldh, const void* P, float* z,
 /* ------------------------------------------------------------------------ *
  * MXFP8 linears (NEXT step of the pages' own optimisation)                   *
  * ------------------------------------------------------------------------ *
- * The pages run the linears as MXFP8 FP8 GEMMs re-quantized per stage, with
+ * The pages run the linears as MXFP8 FP8 GEMMs, quantized again per stage, with
  * SwiGLU fused into a one-pass activation quantizer ([EN] section "Where the
  * 3.9x speedup comes from", inference-configuration table).  Format (OCP MX
  * v1.0, the pages fix none of it): blocks of 32 elements along K, shared

@@ -8,6 +8,8 @@ Sources:
   [EN] "Open-H3-Regenerate-2K: High-Resolution Video Refinement with Few-Step
        Diffusion" (agientry.com, English article)
   [CW] "Open-H3-Regenerate-2K：MiniMax H3 的开源 4K 精修方案" (comfyui-wiki.com)
+  [IC] "Open-H3-Regenerate-2K-IC:草稿留在上下文里,2K 与 4K 重绘仍对着原来的脸、口型和字"
+       (wujieai.com)
 
 Functions take numpy arrays; bf16 tensors are passed as float32 arrays holding
 the exact bf16 values.  Every result is float64.
@@ -217,6 +219,23 @@ def lora_linear_drows(Xd, W0, A, B, scale=1.0, nthreads=0):
     return Y
 
 
+def lora_linear_adjoint(U, W0, A, B, scale=1.0, bias=None):
+    """The LoRA linear's adjoint applied to k column vectors U [N, k]:
+    G = W0ᵀ·U + scale·Aᵀ·(Bᵀ·U)  [K, k]  and  c = biasᵀ·U  [k]  (zeros without bias),
+    so that for every row x:  (x·W0ᵀ + scale·(x·Aᵀ)·Bᵀ + bias)·U = x·G + c.
+    Freivalds' identity with the projection on the output columns: checking one
+    row of a full-size output then costs K multiply-adds instead of K·N.  Steps
+    are float64 matrix products of the given factors (no rounding of its own).
+    Pinned against lora_linear_rows(X)·U on random cases (tests/test_checks.py)."""
+    U = _f64(U)
+    W0 = _f64(W0)
+    G = W0.T @ U
+    if A is not None and np.asarray(A).size:
+        G = G + float(scale) * (_f64(A).T @ (_f64(B).T @ U))
+    c = _f64(bias) @ U if bias is not None else np.zeros(U.shape[1])
+    return G, c
+
+
 def embed_rows(z, E):
     """x = z·Eᵀ for fp32 latent rows z [T, C] and E [D, C]; float64 [T, D]."""
     z = _f32(np.atleast_2d(z))
@@ -230,13 +249,16 @@ def embed_rows(z, E):
 
 
 def head_rows(H, P):
-    """v = H·Pᵀ for rows H [T, D] and P [C, D]; float64 [T, C]."""
+    """v = H·Pᵀ for P [C, D] and rows H [T, ldh], ldh >= D, of which only the
+    first D columns are read (row stride ldh, as a strided activation); float64 [T, C]."""
     H = _f32(np.atleast_2d(H))
     P = _f32(P)
-    T, D = H.shape
-    C = P.shape[0]
+    T, ldh = H.shape
+    C, D = P.shape
+    if ldh < D:
+        raise ValueError("H rows are shorter than P's")
     v = np.empty((T, C), np.float64)
-    lib().oracle_head_rows(H.ctypes.data_as(F32P), T, D, P.ctypes.data_as(F32P), C, D,
+    lib().oracle_head_rows(H.ctypes.data_as(F32P), T, ldh, P.ctypes.data_as(F32P), C, D,
                            v.ctypes.data_as(F64P))
     return v
 
@@ -245,7 +267,7 @@ def head_rows(H, P):
 SIGMAS = (0.909, 0.857, 0.667, 0.0)   # [EN] "Three steps instead of dozens", schedule
 
 
-# ---- in-context (IC) sampler routes ([CW] section "三步接着放大的草稿画，八步从噪声重画")
+# ---- in-context (IC) sampler routes ([IC] section "三步接着放大的草稿画,八步从噪声重画")
 # The pages name an 8-step noise table with video shift 12 but print no formula.
 # Reading: the usual time-shifted flow-matching table sigma = s·t / (1 + (s-1)·t)
 # on t = 1, 7/8, ..., 0, which reproduces the pages' up4 start 0.923 at t = 1/2.

@@ -1,7 +1,8 @@
 """fp64 reference of MXFP8 (E4M3 elements, E8M0 block scales) — TEST INFRASTRUCTURE ONLY.
 
-The pages replace the refiner's bf16 linears by "MXFP8 linear layers: FP8 GEMMs,
-re-quantized per stage" and fuse SwiGLU with a one-pass activation quantizer
+The pages replace the refiner's bf16 linears by MXFP8 linears (FP8 GEMMs whose
+operands are quantized again at every stage) and fuse SwiGLU with a one-pass
+activation quantizer
 ([EN] "Open-H3-Regenerate-2K: High-Resolution Video Refinement with Few-Step
 Diffusion", section "Where the 3.9x speedup comes from", inference-configuration
 table).  They give no block size, scale rule or rounding; the reading taken is the
@@ -217,21 +218,27 @@ def _mx_linear(Xb, L):
     return Xd @ L["W0"].T + mx_values(T) @ L["B"].T
 
 
-def standin_velocity_mx(z, E, P, wq):
+def standin_velocity_mx(z, E, P, wq, trace=None):
     """Velocity of float64 latent rows z [T, C]; E [D, C], P [C, D]; wq from
-    standin_mx_weights (qkv, o, gate/up, down).  Returns float64 [T, C]."""
+    standin_mx_weights (qkv, o, gate/up, down).  Returns float64 [T, C].
+    trace: a dict to receive the bf16 activations between the operations
+    (x, qkv, h1, g, h2) for stage-by-stage checks."""
     z = np.asarray(z, dtype=np.float64)
     E = np.asarray(E, dtype=np.float64)
     P = np.asarray(P, dtype=np.float64)
     D = E.shape[0]
     F = wq[3]["W0"].shape[1]
     h = bf16_round_np(z @ E.T)
+    x = h
     qkv = bf16_round_np(_mx_linear(h, wq[0]))
     h = bf16_round_np(_mx_linear(qkv[:, 2 * D:3 * D], wq[1]) + h)
+    h1 = h
     y = _mx_linear(h, wq[2])
     gate, up = y[:, :F], y[:, F:]
     g = bf16_round_np(gate / (1.0 + np.exp(-gate)) * up)
     h = bf16_round_np(_mx_linear(g, wq[3]) + h)
+    if trace is not None:
+        trace.update(x=x, qkv=qkv, h1=h1, g=g, h2=h)
     return h @ P.T
 
 

@@ -331,15 +331,21 @@ static void head_row(const double* h, const float* P, int64_t C, int64_t D, doub
   }
 }
 
+/* Pins: exact rational sums on tiny shapes (C = 1, 24, 32, 70) and numpy
+   float64 products (tests/test_oracle_pins.py). */
 void oracle_embed_rows(const float* z, int64_t ntok, const float* E, int64_t C, int64_t D,
                        double* x_out) {
-  double zr[64];
+  double* zr = (double*)malloc(sizeof(double) * (size_t)(C > 0 ? C : 1));
   for (int64_t i = 0; i < ntok; ++i) {
-    for (int64_t ch = 0; ch < C && ch < 64; ++ch) zr[ch] = (double)z[i * C + ch];
+    for (int64_t ch = 0; ch < C; ++ch) zr[ch] = (double)z[i * C + ch];
     embed_row(zr, E, C, D, x_out + i * D);
   }
+  free(zr);
 }
 
+/* Rows of H have stride ldh >= D; only their first D entries are read.  Pins:
+   exact rational sums on tiny shapes, ldh = D and ldh > D with non-finite
+   values in the skipped columns (tests/test_oracle_pins.py). */
 void oracle_head_rows(const float* H, int64_t ntok, int64_t ldh, const float* P, int64_t C,
                       int64_t D, double* v_out) {
   double* h = (double*)malloc(sizeof(double) * (size_t)D);

@@ -48,8 +48,49 @@ def test_version_and_status_strings(L):
     assert L.fsd_status_str(0) == b"FSD_OK"
     assert L.fsd_status_str(4) == b"FSD_EWORKSPACE"
     assert L.fsd_status_str(99) == b"FSD_UNKNOWN"
-    assert L.fsd_lora_linear_workspace_bytes(532800, 576) == 532800 * 576 * 2
+    # two 21,760-row chunks of T at rank 576 (50.1 MB), all rows for small M
+    assert L.fsd_lora_linear_workspace_bytes(532800, 576) == 2 * 21760 * 576 * 2
+    assert L.fsd_lora_linear_workspace_bytes(43520, 576) == 43520 * 576 * 2
+    assert L.fsd_lora_linear_workspace_bytes(1200, 576) == 1200 * 576 * 2
     assert L.fsd_lora_linear_workspace_bytes(0, 576) == 0
+
+
+def plan(L, M, r, wsb):
+    R, sched = ctypes.c_int64(-1), ctypes.c_int(-1)
+    n = L.fsd_lora_linear_plan(M, r, wsb, ctypes.byref(R), ctypes.byref(sched))
+    return n, R.value, sched.value
+
+
+def test_lora_linear_plan(L):
+    row = 576 * 2
+    # the whole of T fits: phase A, phase B
+    assert plan(L, 1200, 576, 1200 * row) == (2, 1200, 0)
+    assert plan(L, 1200, 576, 10 ** 9) == (2, 1200, 0)
+    # the preferred workspace at 2K: pipelined pairs of 85 row tiles
+    n, R, sched = plan(L, 532800, 576, L.fsd_lora_linear_workspace_bytes(532800, 576))
+    assert (R, sched) == (21760, 1) and n == -(-532800 // 21760) + 1
+    # larger workspaces keep the 21,760-row chunk; smaller ones shrink it to 256 multiples
+    assert plan(L, 532800, 576, 400 * 10 ** 6)[1:] == (21760, 1)
+    assert plan(L, 10000, 576, 2048 * row)[1:] == (1024, 1)
+    assert plan(L, 10000, 576, 1100 * row)[1:] == (512, 1)
+    assert plan(L, 10000, 576, 512 * row)[1:] == (256, 1)
+    # fewer than 512 rows: 256-row chunks, phase A then B each
+    n, R, sched = plan(L, 1000, 576, 300 * row)
+    assert (n, R, sched) == (8, 256, 2)
+    assert plan(L, 0, 576, 0)[0] == 0
+    assert plan(L, 100, 0, 0)[0] == 1                      # no LoRA term: one launch
+    assert plan(L, -1, 576, 0)[0] == -1
+
+
+def test_lora_linear_launch_index(L):
+    def launch(idx, M=1200, wsb=1200 * 576 * 2):
+        return L.fsd_lora_linear_launch(a(1), 1024, a(2), a(3), a(4), None, None, 0,
+                                        ctypes.c_float(1.0), a(5), 1024, M, 1024, 1024, 576, 0,
+                                        a(7), wsb, idx, None)
+    assert launch(-1) == EINVAL
+    assert launch(2) == EINVAL                              # the plan has launches 0 and 1
+    assert launch(0, M=0) == OK
+    assert launch(1, M=0) == EINVAL
 
 
 BASE = 0x100000000

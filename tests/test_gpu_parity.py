@@ -1,11 +1,13 @@
 """GPU parity: the HIP path through the C ABI against the fp64 oracle.
 
-Small cases compare every output element; full-size cases (768P, 2K, one 4K
-chunk, the 2K three-step stand-in) compare sampled rows exactly and, for the
-linear layers without SwiGLU, every 256-row tile through Freivalds' identity
-w_bᵀY_b = (w_bᵀX_b)·W0ᵀ + s((w_bᵀX_b)·Aᵀ)·Bᵀ + (Σw_b)·bias evaluated by the
-oracle.  Gates: bf16 GEMM outputs max-over-rows rel-L2 and rel-max <= 2e-2;
-fp32 sampler per-token rel-L2 <= 1e-5; merge bit-exact.
+Small cases compare every output element; full-size cases (768P, 2K, the
+first and last 4K chunks, the 2K three-step stand-in) compare sampled rows
+exactly and, for the linear layers without SwiGLU, EVERY row through 16 random
+column projections (Freivalds' identity on the output columns, tests/checks.py:
+Y_i·U against X_i·G + c with the oracle's adjoint G = W0ᵀU + s·Aᵀ(BᵀU)), so a
+defect in a single row is not diluted by the others.  Gates: bf16 GEMM outputs
+max-over-rows rel-L2 and rel-max <= 2e-2 (the projected statistic estimates the
+row's rel-L2); fp32 sampler per-token rel-L2 <= 1e-5; merge bit-exact.
 """
 import math
 
@@ -13,6 +15,7 @@ import numpy as np
 import pytest
 import torch
 
+import checks
 import few_step_diffusion_amd as fsd
 import oracle
 from oracle import metrics
@@ -50,30 +53,13 @@ def assert_gemm(Y, ref, what):
     assert ok, (what, err)
 
 
-def freivalds_tiles(X, Y, W0f, Af, Bf, bias=None, scale=1.0, seed=0, block=256, what=""):
-    """Check every `block`-row tile of Y = X·W0ᵀ + s(X·Aᵀ)·Bᵀ + bias."""
-    dev = X.device
-    M, K = X.shape
-    N = Y.shape[1]
-    nb = (M + block - 1) // block
-    g = torch.Generator(device=dev)
-    g.manual_seed(seed)
-    w = torch.randn(M, generator=g, device=dev, dtype=torch.float64)
-    xt = torch.zeros((nb, K), dtype=torch.float64, device=dev)
-    yt = torch.zeros((nb, N), dtype=torch.float64, device=dev)
-    ws = torch.zeros(nb, dtype=torch.float64, device=dev)
-    step = 64 * block
-    for r0 in range(0, M, step):
-        r1 = min(M, r0 + step)
-        idx = torch.arange(r0, r1, device=dev) // block
-        wc = w[r0:r1, None]
-        xt.index_add_(0, idx, wc * X[r0:r1].double())
-        yt.index_add_(0, idx, wc * Y[r0:r1].double())
-        ws.index_add_(0, idx, w[r0:r1])
-    exp = oracle.lora_linear_drows(xt.cpu().numpy(), W0f, Af, Bf, scale=scale)
-    if bias is not None:
-        exp = exp + ws.cpu().numpy()[:, None] * bias.astype(np.float64)[None, :]
-    assert_gemm(yt.cpu().numpy(), exp, f"{what} Freivalds over {nb} tiles")
+def check_all_rows(X, Y, W0f, Af, Bf, bias=None, scale=1.0, residual=None, seed=0, what=""):
+    """Every row of Y = X·W0ᵀ + s(X·Aᵀ)·Bᵀ + bias (+ residual) through 16 column projections."""
+    N, K = W0f.shape
+    U, G, c = checks.projection(N, K, W0f, Af, Bf, scale=scale, bias=bias, k=16, seed=seed)
+    ok, emax, worst = checks.row_projection_check(X, Y, U, G, c, residual=residual)
+    say(f"{what}: every row through 16 projections, max {emax:.3e} (row {worst})")
+    assert ok, (what, emax, worst)
 
 
 # ----------------------------------------------------------------- merge
@@ -221,16 +207,67 @@ def test_lora_down_alone(gpu):
 
 
 def test_chunked_workspace_is_bitwise_identical(gpu):
-    M, K, N = 1300, 512, 512
-    say(f"chunking M={M} with 256- and 512-row workspaces")
+    """Every schedule of fsd_lora_linear gives the bits of the unchunked one:
+    256-row chunks (one buffer), pipelined pairs of 256- to 1024-row chunks,
+    the whole of T; plain, SwiGLU and in-place residual epilogues."""
+    M, K, N = 5000 + 37, 512, 512
     X = inputs.normal((M, K), 1.0, 51, dtype=torch.bfloat16).to(gpu)
     W0 = inputs.normal((N, K), 0.05, 52, dtype=torch.bfloat16).to(gpu)
+    R0 = inputs.normal((M, N), 1.0, 53, dtype=torch.bfloat16).to(gpu)
     A, B, _, _ = merged(11, K, N, gpu)
-    full = fsd.lora_linear(X, W0, A, B)
-    for rows in (256, 512, 700):
-        ws = torch.empty(rows * 576 * 2, dtype=torch.uint8, device=gpu)
-        part = fsd.lora_linear(X, W0, A, B, workspace=ws)
-        assert torch.equal(part, full), rows
+    for epi, res in (("none", False), ("swiglu", False), ("none", True)):
+        say(f"chunking M={M} epilogue={epi} residual={res}")
+        whole_ws = torch.empty(M * 576 * 2, dtype=torch.uint8, device=gpu)
+        assert fsd.lora_linear_plan(M, 576, whole_ws.numel())[2] == 0
+        Y0 = R0.clone() if res else None
+        full = fsd.lora_linear(X, W0, A, B, epilogue=epi, residual=Y0, out=Y0,
+                               workspace=whole_ws)
+        for rows, sched in ((256, 2), (300, 2), (512, 1), (700, 1), (2048, 1)):
+            ws = torch.empty(rows * 576 * 2, dtype=torch.uint8, device=gpu)
+            assert fsd.lora_linear_plan(M, 576, ws.numel())[2] == sched
+            Yc = R0.clone() if res else None
+            part = fsd.lora_linear(X, W0, A, B, epilogue=epi, residual=Yc, out=Yc, workspace=ws)
+            assert torch.equal(part, full), (epi, res, rows)
+
+
+def test_launch_by_launch_equals_the_whole_call(gpu):
+    """fsd_lora_linear_launch over every index of the plan is fsd_lora_linear."""
+    M, K, N = 3000, 512, 1024
+    X = inputs.normal((M, K), 1.0, 54, dtype=torch.bfloat16).to(gpu)
+    W0 = inputs.normal((N, K), 0.05, 55, dtype=torch.bfloat16).to(gpu)
+    A, B, _, _ = merged(13, K, N, gpu)
+    ws = torch.empty(1024 * 576 * 2, dtype=torch.uint8, device=gpu)
+    seen = []
+    a = fsd.lora_linear(X, W0, A, B, workspace=ws)
+    b = fsd.lora_linear(X, W0, A, B, workspace=ws, on_launch=seen.append)
+    n, R, sched = fsd.lora_linear_plan(M, 576, ws.numel())
+    say(f"launch by launch: {n} launches, chunks of {R}, schedule {sched}")
+    assert seen == list(range(n)) and sched == 1 and R == 512
+    assert torch.equal(a, b)
+
+
+def test_chunked_schedule_is_bitwise_identical_at_2k(gpu):
+    """The 2K QKV linear through the default 50 MB workspace (pipelined pairs of
+    21,760-row chunks) against the whole of T in one 614 MB workspace."""
+    wid = 2
+    _, K, N, _ = inputs.WORKLOADS[wid].linears[0]
+    M = inputs.WORKLOADS[wid].tokens
+    X = inputs.activations(wid, M, K, device=gpu)
+    W0 = inputs.base_weight(wid, K, N).to(gpu)
+    A, B, _, _ = merged(wid, K, N, gpu)
+    small = torch.empty(fsd.workspace_bytes(M, 576), dtype=torch.uint8, device=gpu)
+    n, R, sched = fsd.lora_linear_plan(M, 576, small.numel())
+    say(f"2K QKV: default workspace {small.numel() / 1e6:.1f} MB, {n} launches of "
+        f"{R}-row chunks (schedule {sched}) vs the whole of T")
+    assert sched == 1 and R == 21760 and small.numel() <= 64e6
+    Ya = fsd.lora_linear(X, W0, A, B, workspace=small)
+    del small
+    whole = torch.empty(M * 576 * 2, dtype=torch.uint8, device=gpu)
+    Yb = fsd.lora_linear(X, W0, A, B, workspace=whole)
+    torch.cuda.synchronize()
+    assert torch.equal(Ya, Yb)
+    del X, Ya, Yb, whole
+    torch.cuda.empty_cache()
 
 
 def test_determinism(gpu):
@@ -436,7 +473,7 @@ def _full_linear(gpu, wid, label, K, N, layer=0, M=None, rows=384):
     seli = torch.from_numpy(sel).to(gpu)
     ref = oracle.lora_linear_rows(f32(X[seli]), f32(W0), Af, Bf)
     assert_gemm(f32(Y[seli]), ref, f"{label} sampled rows")
-    freivalds_tiles(X, Y, f32(W0), Af, Bf, seed=wid, what=label)
+    check_all_rows(X, Y, f32(W0), Af, Bf, seed=wid, what=label)
     del X, Y
     torch.cuda.empty_cache()
 
@@ -451,26 +488,80 @@ def test_full_2k_qkv_and_o(gpu):
         _full_linear(gpu, 2, f"2K {label}", K, N, layer=layer)
 
 
-def test_full_4k_chunk_gate_up_swiglu_then_down(gpu):
+def test_full_2k_o_strided_in_place(gpu):
+    """The O linear exactly as the step runs it: input the V slice of a
+    [M, 9216] QKV buffer (row stride 9216), residual added in place into h."""
+    wid = 2
+    _, K, N, _ = inputs.WORKLOADS[wid].linears[1]
+    M = inputs.WORKLOADS[wid].tokens
+    say(f"2K O linear M={M}: V slice input (ld {3 * K}), in-place residual")
+    qkv = inputs.activations(wid, M, 3 * K, device=gpu, layer=5)
+    V = qkv[:, 2 * K:3 * K]
+    h = inputs.normal((M, N), 1.0, seed=2077, device=gpu, dtype=torch.bfloat16)
+    h0 = h.clone()
+    W0 = inputs.base_weight(wid, K, N, layer=1)
+    A, B, Af, Bf = merged(wid, K, N, gpu, layer=1)
+    fsd.lora_linear(V, W0.to(gpu), A, B, residual=h, out=h)
+    torch.cuda.synchronize()
+    sel = torch.from_numpy(inputs.sample_rows(M, 256, seed=21)).to(gpu)
+    ref = oracle.lora_linear_rows(f32(V[sel]), f32(W0), Af, Bf) + f32(h0[sel])
+    assert_gemm(f32(h[sel]), ref, "2K O (V slice, in place) sampled rows")
+    check_all_rows(V, h, f32(W0), Af, Bf, residual=h0, seed=22, what="2K O (V slice, in place)")
+    del qkv, V, h, h0
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("chunk", [0, 3])
+def test_full_4k_down_with_residual(gpu, chunk):
+    """The 4K down linear (K = 8192 -> 3072) with the residual added, as the 4K
+    chunk runs it, on seeded SwiGLU-width inputs: every row of the first chunk
+    and of the last (rows 899,100-1,198,799)."""
+    wl = inputs.WORKLOADS[3]
+    Mc = wl.tokens // wl.chunks
+    (_, K1, _, _), (_, K2, N2, _) = wl.linears
+    say(f"{wl.name}: down with residual, chunk {chunk} (rows {chunk * Mc}-{(chunk + 1) * Mc - 1})")
+    H = inputs.normal((Mc, K2), 0.5, seed=3060 + chunk, device=gpu, dtype=torch.bfloat16)
+    Xall = inputs.activations(3, wl.tokens, K1, device=gpu)
+    R = Xall[chunk * Mc:(chunk + 1) * Mc].clone()
+    del Xall
+    W2 = inputs.base_weight(3, K2, N2, layer=2)
+    A2, B2, A2f, B2f = merged(3, K2, N2, gpu, layer=2)
+    Y = fsd.lora_linear(H, W2.to(gpu), A2, B2, residual=R)
+    torch.cuda.synchronize()
+    sel = torch.from_numpy(inputs.sample_rows(Mc, 160, seed=30 + chunk)).to(gpu)
+    ref = oracle.lora_linear_rows(f32(H[sel]), f32(W2), A2f, B2f) + f32(R[sel])
+    assert_gemm(f32(Y[sel]), ref, f"4K down chunk {chunk} sampled rows")
+    check_all_rows(H, Y, f32(W2), A2f, B2f, residual=R, seed=31 + chunk,
+                   what=f"4K down chunk {chunk}")
+    del H, R, Y
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("chunk", [0, 3])
+def test_full_4k_chunk_gate_up_swiglu_then_down(gpu, chunk):
+    """Gate/up with SwiGLU chained into down with the residual, on the first
+    and the last 4K chunk, sampled rows; the oracle's own H feeds its down."""
     wl = inputs.WORKLOADS[3]
     Mc = wl.tokens // wl.chunks
     (_, K1, N1, _), (_, K2, N2, _) = wl.linears
-    say(f"{wl.name}: chunk M={Mc} gate/up {K1}->{N1} SwiGLU, down {K2}->{N2}")
-    X = inputs.activations(3, Mc, K1, device=gpu)
+    say(f"{wl.name}: chunk {chunk} M={Mc} gate/up {K1}->{N1} SwiGLU, down {K2}->{N2} + residual")
+    Xall = inputs.activations(3, wl.tokens, K1, device=gpu)
+    X = Xall[chunk * Mc:(chunk + 1) * Mc].clone()
+    del Xall
     W1 = inputs.base_weight(3, K1, N1, layer=1)
     W2 = inputs.base_weight(3, K2, N2, layer=2)
     A1, B1, A1f, B1f = merged(3, K1, N1, gpu, layer=1)
     A2, B2, A2f, B2f = merged(3, K2, N2, gpu, layer=2)
     H = fsd.lora_linear(X, W1.to(gpu), A1, B1, epilogue="swiglu")
-    Y = fsd.lora_linear(H, W2.to(gpu), A2, B2)
+    Y = fsd.lora_linear(H, W2.to(gpu), A2, B2, residual=X)
     torch.cuda.synchronize()
-    sel = inputs.sample_rows(Mc, 160, seed=3)
+    sel = inputs.sample_rows(Mc, 160, seed=3 + chunk)
     seli = torch.from_numpy(sel).to(gpu)
     Href = oracle.lora_linear_rows(f32(X[seli]), f32(W1), A1f, B1f, swiglu=True)
-    assert_gemm(f32(H[seli]), Href, "4K gate/up SwiGLU sampled rows")
+    assert_gemm(f32(H[seli]), Href, f"4K chunk {chunk} gate/up SwiGLU sampled rows")
     # the chain from X in fp64: the oracle's H (not the GPU's) feeds its down projection
-    Yref = oracle.lora_linear_drows(Href, f32(W2), A2f, B2f)
-    assert_gemm(f32(Y[seli]), Yref, "4K down (chained) sampled rows")
+    Yref = oracle.lora_linear_drows(Href, f32(W2), A2f, B2f) + f32(X[seli])
+    assert_gemm(f32(Y[seli]), Yref, f"4K chunk {chunk} down (chained, residual) sampled rows")
     del X, H, Y
     torch.cuda.empty_cache()
 
