@@ -15,7 +15,7 @@ import torch
 
 __all__ = [
     "FsdError", "library_path", "lib", "abi_version", "lora_merge", "workspace_bytes",
-    "lora_down", "lora_up", "lora_linear", "lora_linear_plan", "renoise", "euler_step", "token_embed",
+    "lora_down", "lora_up", "lora_linear", "lora_linear_plan", "lora_linear_noalloc", "renoise", "euler_step", "token_embed",
     "token_head", "token_head_euler", "mx_quantize", "mx_padded_k", "mx_scale_bytes",
     "mx_scale_offsets", "mx_pack_scales", "mx_unpack_scales", "mx_lora_down", "mx_lora_up",
     "mx_lora_up_swiglu_mx", "attention_workspace_bytes", "attention",
@@ -68,6 +68,9 @@ _SIGS = {
     "fsd_lora_linear_launch": ([_c_void_p, _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                 _c_void_p, _i64, _f32, _c_void_p, _i64, _i64, _i64, _i64, _i64,
                                 _int, _c_void_p, ctypes.c_size_t, _i64, _c_void_p], _int),
+    "fsd_lora_linear_noalloc": ([_c_void_p, _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                 _c_void_p, _i64, _f32, _c_void_p, _i64, _i64, _i64, _i64, _i64,
+                                 _int, _c_void_p], _int),
     "fsd_renoise": ([_c_void_p, _c_void_p, _f32, _c_void_p, _i64, _c_void_p], _int),
     "fsd_euler_step": ([_c_void_p, _c_void_p, _f32, _f32, _i64, _c_void_p], _int),
     "fsd_token_embed": ([_c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64, _i64, _c_void_p],
@@ -327,6 +330,30 @@ def lora_linear(X, W0, A, B, scale=1.0, bias=None, residual=None, epilogue=EPI_N
         on_launch(i)
         st = lib().fsd_lora_linear_launch(*args, i, _stream(X))
         _check("fsd_lora_linear_launch", st)
+    return out
+
+
+def lora_linear_noalloc(X, W0, A, B, scale=1.0, bias=None, residual=None, epilogue=EPI_NONE,
+                        out=None):
+    """lora_linear with T in the library's per-GPU scratch (fsd_lora_linear_noalloc):
+    no device memory is allocated for the call (pass `out` to allocate nothing at
+    all).  Calls that overlap on one GPU share the scratch and must be ordered."""
+    epilogue = _epi(epilogue)
+    _need(X, "X", torch.bfloat16)
+    _need(W0, "W0", torch.bfloat16)
+    M, K = X.shape
+    N = W0.shape[0]
+    r = 0 if A is None else A.shape[0]
+    _linear_operands(X, W0, A, B, bias, residual, epilogue, r)
+    if out is None:
+        out = torch.empty((M, _out_cols(N, epilogue)), dtype=torch.bfloat16, device=X.device)
+    _need(out, "out", torch.bfloat16)
+    _shape(out, "out", (M, _out_cols(N, epilogue)), device=X.device)
+    st = lib().fsd_lora_linear_noalloc(
+        _ptr(X), _ld(X), _ptr(W0), _ptr(A) if r else None, _ptr(B) if r else None, _ptr(bias),
+        _ptr(residual), _ld(residual) if residual is not None else 0, float(scale), _ptr(out),
+        _ld(out), M, N, K, r, epilogue, _stream(X))
+    _check("fsd_lora_linear_noalloc", st)
     return out
 
 

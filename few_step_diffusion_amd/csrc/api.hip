@@ -7,6 +7,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/fsd.h"
 #include "fsd_internal.h"
 
@@ -410,7 +412,66 @@ int validate_linear(const UpShape& a, const void* A, float scale, const void* wo
 
 }  // namespace
 
+// ---- scratch of fsd_lora_linear_noalloc ----------------------------------------
+// T of the allocation-free LoRA linear lives in this file-scope device array:
+// two 21,760-row chunks at rank 576 (FSD_NOALLOC_SCRATCH_BYTES).  Each GPU the
+// library runs on holds its own copy until the process ends.  In host code the
+// name `scratch` is only a stand-in for the symbol, not a device address: the
+// address is looked up per device with hipGetSymbolAddress and only that
+// pointer is ever passed to a kernel.
+static_assert(FSD_NOALLOC_SCRATCH_BYTES == 2 * kPairChunkRows * 576 * 2,
+              "the scratch holds two pipelined chunks of T at rank 576");
+static __device__ __align__(256) char scratch[FSD_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The current device's scratch address (looked up once per device), or null
+// with *err set.
+void* device_scratch(int* err) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *err = FSD_EHIP;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      *err = FSD_EHIP;
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
 extern "C" {
+
+int fsd_lora_linear_noalloc(const void* X, int64_t ldx, const void* W0, const void* A,
+                            const void* B, const float* bias, const void* residual, int64_t ldr,
+                            float scale, void* Y, int64_t ldy, int64_t M, int64_t N, int64_t K,
+                            int64_t r, int epilogue, void* stream) {
+  // the limit first (host arithmetic): 256 rows of T must fit in the scratch
+  if (r > (int64_t)(FSD_NOALLOC_SCRATCH_BYTES / (kTileM * 2))) return FSD_EUNSUPPORTED;
+  int err = FSD_OK;
+  void* ws = r > 0 ? device_scratch(&err) : nullptr;
+  if (r > 0 && !ws) return err;
+  const int64_t ws_bytes = r > 0 ? (int64_t)FSD_NOALLOC_SCRATCH_BYTES : 0;
+  const UpShape a{X, W0, ws, B, ldx, r, bias, residual, ldr, Y, ldy, M, N, K, r, epilogue};
+  const int st = validate_linear(a, A, scale, ws, ws_bytes);
+  if (st != FSD_OK) return st;
+  const Plan pl = make_plan(M, r, ws_bytes);
+  for (int64_t i = 0; i < pl.launches; ++i) {
+    const int e = lora_linear_launch(a, A, scale, ws, pl, i, as_stream(stream));
+    if (e != FSD_OK) return e;
+  }
+  return FSD_OK;
+}
 
 int64_t fsd_lora_linear_plan(int64_t M, int64_t r, size_t workspace_bytes, int64_t* chunk_rows,
                              int* schedule) {

@@ -190,6 +190,33 @@ int fsd_lora_linear_launch(const void* X, int64_t ldx, const void* W0,
                            size_t workspace_bytes, int64_t index, void* stream);
 
 /* ------------------------------------------------------------------------ *
+ * The LoRA-fused linear without an allocation                               *
+ * ------------------------------------------------------------------------ *
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * fsd_lora_linear with T kept in a scratch array that the library holds on
+ * each GPU it runs on, FSD_NOALLOC_SCRATCH_BYTES bytes (two 21,760-row chunks
+ * of T at rank 576), instead of a caller's workspace.  Same arguments (minus
+ * the workspace), results (bitwise those of fsd_lora_linear with a workspace
+ * of that size) and errors as fsd_lora_linear, and:
+ *   - r > FSD_NOALLOC_SCRATCH_BYTES / 512 (256 rows of T must fit) gives
+ *     FSD_EUNSUPPORTED, before any HIP call;
+ *   - the first call on a device looks up that device's scratch address
+ *     (hipGetDevice, hipGetSymbolAddress; FSD_EHIP if that fails) before the
+ *     remaining validation; later calls only query the current device;
+ *   - no allocation, no free, no synchronisation; the scratch needs no
+ *     clearing (T is written before it is read);
+ *   - every call on one GPU shares that GPU's scratch, which keeps the last
+ *     call's contents: calls that overlap on one GPU (several streams, several
+ *     host threads) race and must be ordered by the caller. */
+#define FSD_NOALLOC_SCRATCH_BYTES ((size_t)50135040)
+int fsd_lora_linear_noalloc(const void* X, int64_t ldx, const void* W0,
+                            const void* A, const void* B, const float* bias,
+                            const void* residual, int64_t ldr, float scale,
+                            void* Y, int64_t ldy, int64_t M, int64_t N,
+                            int64_t K, int64_t r, int epilogue, void* stream);
+
+/* ------------------------------------------------------------------------ *
  * a1. Partial renoise                                                        *
  * ------------------------------------------------------------------------ *
  * [EN] section "Three steps instead of dozens", renoise equation: the

@@ -82,6 +82,15 @@ def test_lora_linear_plan(L):
     assert plan(L, -1, 576, 0)[0] == -1
 
 
+def test_noalloc_rank_limit_without_a_gpu(L):
+    # 256 rows of T must fit in the 50,135,040-byte scratch: r <= 97,920; the
+    # limit is checked before any HIP call
+    rc = L.fsd_lora_linear_noalloc(a(1), 1024, a(2), a(3), a(4), None, None, 0,
+                                   ctypes.c_float(1.0), a(5), 1024, 1200, 1024, 1024, 97928, 0,
+                                   None)
+    assert rc == EUNSUP
+
+
 def test_lora_linear_launch_index(L):
     def launch(idx, M=1200, wsb=1200 * 576 * 2):
         return L.fsd_lora_linear_launch(a(1), 1024, a(2), a(3), a(4), None, None, 0,
