@@ -26,8 +26,9 @@ Prints ONE JSON line on stdout (everything else goes to stderr):
   lora_linear_configs  the whole LoRA-fused linear at the 768P shape and on one
              4K chunk (gate/up with SwiGLU chained into down with the
              residual): median / min / max of 20 calls, and the median of 3
-  attention  one dense attention call over the 2K grid as one sequence
-             (532,800 tokens, 24 heads of 128), against 2500 TFLOP/s
+  attention_step  the same refine with dense attention between QKV and O
+             (all 532,800 tokens as one sequence, 24 heads of 128): step time
+             and the attention kernel against 2500 TFLOP/s
   cpu_baseline the fp64 oracle on a bounded sample of tokens on host cores
 """
 from __future__ import annotations
@@ -65,10 +66,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-elementwise", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+    ap.add_argument("--cpu-seconds", type=float, default=8.0,
                     help="target host time of the oracle sample")
     ap.add_argument("--no-mx", action="store_true", help="skip the MXFP8 step")
-    ap.add_argument("--no-attention", action="store_true", help="skip the dense attention call")
+    ap.add_argument("--no-attention", action="store_true",
+                    help="skip the refine with dense attention between QKV and O")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the LoRA linears at the 768P and 4K-chunk shapes")
     ap.add_argument("--no-shard", action="store_true",
@@ -78,7 +80,7 @@ def parse():
     return ap.parse_args()
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_swiglu_2k_pmc_traffic.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_pair_2k_pmc_traffic.md")
 GEMM_SOURCE = os.path.join(ROOT, "few_step_diffusion_amd", "csrc", "gemm.hip")
 
 
@@ -162,11 +164,85 @@ def elementwise(torch, fsd, inputs, batches=5, per_batch=24):
     return res
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _median_of_3(fn):
+    """Median and range of 3 timed runs after one untimed warm-up run."""
+    fn()
+    runs = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        fn()
+        runs.append(time.perf_counter() - t0)
+    return statistics.median(runs), min(runs), max(runs)
+
+
 def cpu_baseline(model_flops_per_token, target_s):
-    """The fp64 oracle on a bounded sample of tokens of the same step."""
+    """The fp64 oracle as it stands, timed on the host: median of 3 runs after a
+    warm-up, the pages' own method for their timings.
+      value          the 2K three-step stand-in (renoise + 3 x (velocity + Euler))
+                     on a bounded token sample, algorithmic TFLOP/s of that sample;
+      elementwise    renoise + 3 Euler steps with v = eps - x0 on the FULL latent of
+                     the 768P, 2K and 4K grids (the oracle's single-threaded loops);
+      gemm_rows      the LoRA linear at the 2K QKV and O shapes on a 4,096-row sample
+                     (seeded rows of the activations' distribution), with the
+                     full-M time extrapolated (rows are independent: cost ~ M)."""
     import numpy as np
     import oracle
     from few_step_diffusion_amd import inputs
+    threads = oracle.default_threads()
+    out = {"unit": "TFLOP/s", "cores": threads, "kind": "oracle", "cpu_model": cpu_model(),
+           "host_cpus": os.cpu_count()}
+    # --- full-latent sampler (configs 1-3): renoise then 3 Euler steps
+    ew = {}
+    for wid, tag in ((1, "768p"), (2, "2k"), (3, "4k")):
+        u, eps = inputs.latent(wid)
+        u, eps = u.numpy().ravel(), eps.numpy().ravel()
+        med, lo, hi = _median_of_3(lambda: oracle.sampler_exact_velocity(u, eps))
+        n = u.size
+        ew[tag] = {"elements": n, "passes": 4, "s_median": round(med, 4),
+                   "s_min": round(lo, 4), "s_max": round(hi, 4), "threads": 1,
+                   "GB/s_at_12B_per_element_pass": round(4 * 12 * n / med / 1e9, 2)}
+        log(f"oracle sampler {tag}: {med:.3f} s")
+    out["elementwise"] = ew
+    # --- LoRA linear rows at the 2K shapes
+    gr = {}
+    M2 = inputs.WORKLOADS[2].tokens
+    R = 4096
+    for layer, (name, K, N, _) in enumerate(inputs.WORKLOADS[2].linears):
+        W0 = inputs.base_weight(2, K, N, layer).float().numpy()
+        A_l, B_l = inputs.adapters(2, K, N, layer)
+        Ab, Bb = oracle.merge_bf16([a.numpy() for a in A_l], [b.numpy() for b in B_l])
+        A = oracle.bf16_value(Ab).reshape(Ab.shape)
+        B = oracle.bf16_value(Bb).reshape(Bb.shape)
+        r = A.shape[0]
+        X = inputs.normal((R, K), 1.0, inputs.seed_of(2, inputs.ID_X, 10 + layer))
+        X = X.to(__import__("torch").bfloat16).float().numpy()
+        oracle.lora_linear_rows(X[:256], W0, A, B, nthreads=threads)      # warm-up
+        runs = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            oracle.lora_linear_rows(X, W0, A, B, nthreads=threads)
+            runs.append(time.perf_counter() - t0)
+        med = statistics.median(runs)
+        fl = 2.0 * R * (K * N + K * r + r * N)
+        gr[name] = {"rows": R, "K": K, "N": N, "r": r, "s_median": round(med, 3),
+                    "s_min": round(min(runs), 3), "s_max": round(max(runs), 3),
+                    "tflops": round(fl / med / 1e12, 6),
+                    "extrapolated_full_s": round(med * M2 / R, 1),
+                    "note": f"extrapolated to all {M2:,} rows as t·M/R (not measured)"}
+        log(f"oracle LoRA linear {name}: {R} rows {med:.2f} s")
+    out["gemm_rows"] = gr
+    # --- the stand-in step on a bounded token sample (the value, in the step's unit)
     layers = []
     for L in inputs.standin_layers(4):
         Ab, Bb = oracle.merge_bf16([a.numpy() for a in L["A_list"]],
@@ -178,7 +254,6 @@ def cpu_baseline(model_flops_per_token, target_s):
     E, P = E.float().numpy(), P.float().numpy()
     u, eps = inputs.latent(4, tokens=4096)
     u, eps = u.numpy(), eps.numpy()
-    threads = oracle.default_threads()
     # warm up and calibrate on one token per thread, then size the sample so
     # that three timed runs take about target_s together; report their median
     t0 = time.perf_counter()
@@ -193,46 +268,52 @@ def cpu_baseline(model_flops_per_token, target_s):
         oracle.standin_refine(u[:tokens], eps[:tokens], E, P, layers, nthreads=threads)
         runs.append(time.perf_counter() - t0)
     dt = statistics.median(runs)
-    tflops = tokens * model_flops_per_token / dt / 1e12
-    return {"value": round(tflops, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "extrapolated_full_step_s": round(dt * 532800 / tokens, 1),
-            "sample": f"{tokens} of 532,800 tokens of the same step (renoise + 3 stand-in "
-                      f"velocity evaluations + Euler), fp64; median of 3 runs of "
-                      f"{min(runs):.1f}-{max(runs):.1f} s after one warm-up"}
+    out["value"] = round(tokens * model_flops_per_token / dt / 1e12, 6)
+    out["extrapolated_full_step_s"] = round(dt * 532800 / tokens, 1)
+    out["sample"] = (f"{tokens} of 532,800 tokens of the same step (renoise + 3 stand-in "
+                     f"velocity evaluations + Euler), fp64, {threads} threads; median of 3 runs "
+                     f"of {min(runs):.1f}-{max(runs):.1f} s after one warm-up; full-step time "
+                     "extrapolated (not measured)")
+    return out
 
 
-def attention_2k(torch, fsd, M, args):
-    """One dense attention call over the 2K grid as one sequence (the refine
-    path's baseline attention): 532,800 tokens, 24 heads of 128 read in place
-    from a QKV buffer; V's per-head transpose included in the call."""
-    H, D = 24, 128
-    g = torch.Generator(device="cuda:0")
-    g.manual_seed(4242)
-    qkv = torch.randn((M, 3 * H * D), generator=g, device="cuda:0").to(torch.bfloat16)
-    Q, K, V = qkv[:, :H * D], qkv[:, H * D:2 * H * D], qkv[:, 2 * H * D:]
-    O = torch.empty((M, H * D), dtype=torch.bfloat16, device="cuda:0")
-    ws = torch.empty(fsd.attention_workspace_bytes(M, H, D), dtype=torch.uint8, device="cuda:0")
-    fsd.attention(Q, K, V, H, out=O, workspace=ws)
+def attention_step(torch, M, u, eps, args):
+    """The refine with dense attention between the QKV and O linears (the pages'
+    dense-bf16 baseline refine path): all 532,800 tokens as one sequence, 24
+    heads of 128, V's per-head transpose inside each attention call.  One
+    untimed refine, then one timed refine with HIP events between launches."""
+    from few_step_diffusion_amd.refine import StandinRefiner
+    model = StandinRefiner(M, device=u.device, attention=True)
+    model.refine(u, eps)
     torch.cuda.synchronize()
-    a = torch.cuda.Event(enable_timing=True)
-    b = torch.cuda.Event(enable_timing=True)
-    reps = 2
+    model.events = []
     torch.cuda._sleep(SPIN_CYCLES)
-    a.record()
-    for _ in range(reps):
-        fsd.attention(Q, K, V, H, out=O, workspace=ws)
-    b.record()
-    b.synchronize()
-    ms = a.elapsed_time(b) / reps
-    flops = 4.0 * M * M * H * D
-    tf = flops / (ms * 1e-3) / 1e12
-    log(f"attention: {ms:.1f} ms, {tf:.0f} TFLOP/s")
-    del qkv, O, ws
-    return {"ms_per_call": round(ms, 2), "tflops": round(tf, 1),
-            "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4), "bound": "mfma",
-            "flops_per_call": flops, "tokens": M, "heads": H, "head_dim": D,
-            "note": "softmax(Q·Kᵀ/sqrt(128))·V per head over all 532,800 tokens; algorithmic "
-                    "flops 4·S²·H·D; includes the per-head transpose of V (one pass over V)"}
+    model.refine(u, eps)
+    torch.cuda.synchronize()
+    ev = model.events
+    model.events = None
+    ms = ev[0][1].elapsed_time(ev[-1][1])
+    per_kernel = kernel_times(ev)
+    flops = model.flops_per_step()
+    att = per_kernel["attention"]
+    att_ms = statistics.mean(att)
+    att_tf = flops["attention"] / len(att) / (att_ms * 1e-3) / 1e12
+    tf = sum(flops.values()) / (ms * 1e-3) / 1e12
+    log(f"attention step: {ms:.1f} ms, attention {att_ms:.1f} ms per call ({att_tf:.0f} TFLOP/s)")
+    del model
+    return {"ms_per_step": round(ms, 2), "tflops": round(tf, 1),
+            "attention": {"ms_per_call": round(att_ms, 2), "calls_per_step": len(att),
+                          "tflops": round(att_tf, 1), "frac_peak": round(att_tf / PEAK_BF16_TFLOPS, 4),
+                          "bound": "mfma", "flops_per_call": flops["attention"] / len(att)},
+            "tokens": M, "heads": model_heads(), "head_dim": 128,
+            "note": "renoise + 3 x (embed, QKV, attention over all 532,800 tokens, O + residual, "
+                    "gate/up + SwiGLU, down + residual, head, Euler); attention flops 4·S²·H·D "
+                    "per call, including the per-head transpose of V (one pass over V)"}
+
+
+def model_heads():
+    from few_step_diffusion_amd import inputs
+    return inputs.STANDIN_D // 128
 
 
 def mx_step(torch, M, u, eps, flops, bf16_ms, args):
@@ -571,8 +652,8 @@ def main():
         out["mxfp8"] = mx_step(torch, M, u, eps, flops, ms, args)
         torch.cuda.empty_cache()
     if not args.no_attention:
-        log("dense attention at the 2K grid ...")
-        out["attention"] = attention_2k(torch, fsd, M, args)
+        log("refine with dense attention at the 2K grid ...")
+        out["attention_step"] = attention_step(torch, M, u, eps, args)
         torch.cuda.empty_cache()
     if not args.no_elementwise:
         log("elementwise cold-cache timing ...")

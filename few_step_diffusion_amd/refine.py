@@ -11,9 +11,12 @@ the stand-in per token is
     x = z·Eᵀ;  q = L_qkv(x);  h = x + L_o(q[:, 2D:3D]);
     h = h + L_down(SwiGLU(L_gu(h)));  v = h·Pᵀ
 
-with every L_* the LoRA-fused linear.  Every call below is one HIP kernel of
-libfsd.so (through the ctypes binding); torch only allocates device memory
-and supplies the stream.
+with every L_* the LoRA-fused linear.  With attention=True the O linear reads
+dense attention over all tokens instead of the V slice (the pages' baseline
+refine runs dense bf16 attention between them; "Where the 3.9x speedup comes
+from", dense-BF16 row): h = x + L_o(attention(Q, K, V)), heads of 128.  Every
+call below runs HIP kernels of libfsd.so (through the ctypes binding); torch
+only allocates device memory and supplies the stream.
 """
 from __future__ import annotations
 
@@ -31,13 +34,17 @@ class StandinRefiner:
 
     def __init__(self, M: int, device="cuda:0", wid: int = 4, D: int = inputs.STANDIN_D,
                  F: int = inputs.STANDIN_F, ranks=inputs.RANKS, C: int = inputs.LATENT_C,
-                 scale: float = 1.0, mx: bool = False):
+                 scale: float = 1.0, mx: bool = False, attention: bool = False):
         """mx: run the four linears as MXFP8 GEMMs.  The bf16 weights are quantized
         once here; each linear quantizes its bf16 input and its bf16 LoRA down output,
         and the gate/up GEMM hands SwiGLU's output to the down projection already
         quantized."""
         dev = torch.device(device)
+        if attention and (mx or D % 128):
+            raise ValueError("the attention step runs on the bf16 path with heads of 128")
         self.M, self.D, self.F, self.C, self.dev = M, D, F, C, dev
+        self.attention = attention
+        self.heads = D // 128
         self.R = sum(ranks)
         self.scale = scale
         self.mx = mx
@@ -64,6 +71,10 @@ class StandinRefiner:
             # shared by the four linears (they run one after another on one stream)
             self.ws = torch.empty(max(fsd.workspace_bytes(M, self.R), 16), dtype=torch.uint8,
                                   device=dev)
+        if attention:
+            self.att = torch.empty((M, D), dtype=bf, device=dev)      # attention output
+            self.att_ws = torch.empty(max(fsd.attention_workspace_bytes(M, self.heads), 16),
+                                      dtype=torch.uint8, device=dev)
         self.v = torch.empty((M, C), dtype=torch.float32, device=dev)
         self.z = torch.empty((M, C), dtype=torch.float32, device=dev)
         if mx:
@@ -138,7 +149,13 @@ class StandinRefiner:
             self._mx_linear(3, self.gq, self.h, residual=self.h)
         else:
             self._linear(0, self.h, self.qkv)
-            self._linear(1, self.qkv[:, 2 * D:3 * D], self.h, residual=self.h)
+            if self.attention:
+                self._mark("attention")
+                fsd.attention(self.qkv[:, :D], self.qkv[:, D:2 * D], self.qkv[:, 2 * D:3 * D],
+                              self.heads, out=self.att, workspace=self.att_ws)
+                self._linear(1, self.att, self.h, residual=self.h)
+            else:
+                self._linear(1, self.qkv[:, 2 * D:3 * D], self.h, residual=self.h)
             self._linear(2, self.h, self.g, epilogue=fsd.EPI_SWIGLU)
             self._linear(3, self.g, self.h, residual=self.h)
 
@@ -222,6 +239,8 @@ class StandinRefiner:
                 out[name + ".up"] = up * steps
         out["embed"] = 2 * M * C * D * steps
         out["head"] = 2 * M * D * C * steps
+        if self.attention:
+            out["attention"] = 4 * M * M * D * steps          # Q·Kᵀ and P·V, all heads
         return out
 
     def linear_flops(self) -> dict:

@@ -20,10 +20,10 @@ def test_traffic_matches_committed_summary():
             key, sep, val = line.strip().partition(": ")
             if sep:
                 fields[key] = val.strip()
-    got = bench.measured_traffic("gemm_kernel<2, 4, true, false, false>")
+    got = bench.measured_traffic("gemm_pair_kernel<true>")
     if fields.get("source_sha256") == sha:
-        # bytes per launch of the gate/up GEMM: above its 12.7 GB of algorithmic traffic
-        assert got is not None and 12.7e9 < got < 1e12
+        # bytes per pair launch of the gate/up linear: above its 0.777 GB of algorithmic traffic
+        assert got is not None and 0.777e9 < got < 1e11
     else:
         assert got is None
 
@@ -32,9 +32,9 @@ def test_traffic_is_null_for_another_source(tmp_path, monkeypatch):
     other = tmp_path / "gemm.hip"
     other.write_text("// a different source\n")
     monkeypatch.setattr(bench, "GEMM_SOURCE", str(other))
-    assert bench.measured_traffic("gemm_kernel<2, 4, true, false, false>") is None
+    assert bench.measured_traffic("gemm_pair_kernel<true>") is None
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "missing.md"))
-    assert bench.measured_traffic("gemm_kernel<2, 4, true, false, false>") is None
+    assert bench.measured_traffic("gemm_pair_kernel<true>") is None
 
 
 def test_more_than_one_gpu_is_refused():

@@ -79,3 +79,68 @@ def test_heads_are_independent_and_match_element_loops():
     K2[:, D:] = 0.0                                            # change head 1 only
     O2 = attention.attention_rows(Q, K2, V, heads=H)
     assert np.array_equal(O2[:, :D], O[:, :D]) and not np.allclose(O2[:, D:], O[:, D:])
+
+
+# ------------------------------------------------ key multiplicities, stand-in
+def test_key_multiplicity_equals_repeated_keys():
+    """A key row with multiplicity m is the same as m copies of that row."""
+    Q, K, V = _qkv(5, 2, 8, 11)
+    m = np.array([1, 3, 1, 2, 5])
+    rep = np.repeat(np.arange(5), m)
+    O_rep = attention.attention_rows(Q, K[rep], V[rep], heads=2)
+    O_mult = attention.attention_rows(Q, K, V, heads=2, key_mult=m)
+    assert np.allclose(O_mult, O_rep, rtol=1e-13, atol=1e-14)
+    assert np.allclose(attention.attention_rows(Q, K, V, heads=2, key_mult=np.ones(5)),
+                       attention.attention_rows(Q, K, V, heads=2), rtol=0, atol=0)
+
+
+def _tiny_standin(T=6, C=4, D=256, F=64, seed=3):
+    import oracle
+    from few_step_diffusion_amd import inputs
+    ranks = (16, 8, 8)
+    layers = []
+    for L in inputs.standin_layers(4, D, F, ranks):
+        Ab, Bb = oracle.merge_bf16([a.numpy() for a in L["A_list"]],
+                                   [b.numpy() for b in L["B_list"]])
+        layers.append({"W0": L["W0"].float().numpy(), "A": oracle.bf16_value(Ab).reshape(Ab.shape),
+                       "B": oracle.bf16_value(Bb).reshape(Bb.shape)})
+    E, P = inputs.standin_projections(4, C, D)
+    rng = np.random.default_rng(seed)
+    x0 = rng.standard_normal((T, C)).astype(np.float32)
+    eps = rng.standard_normal((T, C)).astype(np.float32)
+    return x0, eps, E.float().numpy(), P.float().numpy(), layers
+
+
+def test_attention_standin_with_identical_tokens_is_the_self_only_standin():
+    """Identical tokens attend to identical keys: every token's attention output
+    is its own V, which is the self-only stand-in of the C oracle."""
+    import oracle
+    x0, eps, E, P, layers = _tiny_standin()
+    x0 = np.tile(x0[:1], (5, 1))
+    eps = np.tile(eps[:1], (5, 1))
+    z_att, v_att = attention.standin_refine_attention(x0, eps, E, P, layers, heads=2,
+                                                      sigmas=oracle.SIGMAS)
+    z_self, v_self = oracle.standin_refine(x0, eps, E, P, layers)
+    assert np.allclose(z_att, z_self, rtol=1e-10, atol=1e-12)
+    assert np.allclose(v_att, v_self, rtol=1e-10, atol=1e-12)
+
+
+def test_attention_standin_token_permutation_and_multiplicities():
+    """Permuting the tokens permutes the result; a token class given once with
+    multiplicity m equals the class repeated m times."""
+    import oracle
+    x0, eps, E, P, layers = _tiny_standin(T=4)
+    perm = np.array([2, 0, 3, 1])
+    za, _ = attention.standin_refine_attention(x0, eps, E, P, layers, 2, oracle.SIGMAS)
+    zp, _ = attention.standin_refine_attention(x0[perm], eps[perm], E, P, layers, 2,
+                                               oracle.SIGMAS)
+    assert np.allclose(zp, za[:, perm], rtol=1e-12, atol=1e-13)
+    m = np.array([3, 1, 2, 4])
+    rep = np.repeat(np.arange(4), m)
+    zr, _ = attention.standin_refine_attention(x0[rep], eps[rep], E, P, layers, 2,
+                                               oracle.SIGMAS)
+    zm, _ = attention.standin_refine_attention(x0, eps, E, P, layers, 2, oracle.SIGMAS, mult=m)
+    assert np.allclose(zm[:, rep], zr, rtol=1e-11, atol=1e-12)
+    # attention matters here: the self-only stand-in differs
+    zs, _ = oracle.standin_refine(x0, eps, E, P, layers)
+    assert not np.allclose(zs, za, rtol=1e-3, atol=1e-3)
