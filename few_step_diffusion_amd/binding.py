@@ -18,7 +18,7 @@ __all__ = [
     "lora_down", "lora_up", "lora_linear", "lora_linear_plan", "lora_linear_noalloc", "renoise", "euler_step", "token_embed",
     "token_head", "token_head_euler", "mx_quantize", "mx_padded_k", "mx_scale_bytes",
     "mx_scale_offsets", "mx_pack_scales", "mx_unpack_scales", "mx_lora_down", "mx_lora_up",
-    "mx_lora_up_swiglu_mx", "attention_workspace_bytes", "attention",
+    "mx_lora_up_swiglu_mx", "attention_workspace_bytes", "attention", "StepGraph",
     "EPI_NONE", "EPI_SWIGLU",
 ]
 
@@ -71,6 +71,10 @@ _SIGS = {
     "fsd_lora_linear_noalloc": ([_c_void_p, _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                  _c_void_p, _i64, _f32, _c_void_p, _i64, _i64, _i64, _i64, _i64,
                                  _int, _c_void_p], _int),
+    "fsd_graph_begin": ([_c_void_p], _int),
+    "fsd_graph_end": ([_c_void_p, ctypes.POINTER(_c_void_p)], _int),
+    "fsd_graph_launch": ([_c_void_p, _c_void_p], _int),
+    "fsd_graph_destroy": ([_c_void_p], _int),
     "fsd_renoise": ([_c_void_p, _c_void_p, _f32, _c_void_p, _i64, _c_void_p], _int),
     "fsd_euler_step": ([_c_void_p, _c_void_p, _f32, _f32, _i64, _c_void_p], _int),
     "fsd_token_embed": ([_c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64, _i64, _c_void_p],
@@ -641,3 +645,60 @@ def attention(Q, K, V, heads, scale=None, out=None, workspace=None):
                              workspace.numel() * workspace.element_size(), _stream(Q))
     _check("fsd_attention", st)
     return out
+
+
+# ------------------------------------------------------------ step graphs
+class StepGraph:
+    """A HIP graph of the launches this library enqueues on one stream between
+    begin() and end() (fsd_graph_begin / fsd_graph_end), replayed by launch().
+
+    with StepGraph.capture(stream) as g:   # stream: a torch.cuda.Stream
+        ... library calls under torch.cuda.stream(stream) ...
+    g.launch(stream)
+    """
+
+    def __init__(self):
+        self._g = None
+
+    @classmethod
+    def capture(cls, stream):
+        return _Capture(cls(), stream)
+
+    def launch(self, stream=None):
+        if self._g is None:
+            raise RuntimeError("no captured graph")
+        s = torch.cuda.current_stream() if stream is None else stream
+        _check("fsd_graph_launch", lib().fsd_graph_launch(self._g, ctypes.c_void_p(s.cuda_stream)))
+
+    def close(self):
+        if self._g is not None:
+            lib().fsd_graph_destroy(self._g)
+            self._g = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class _Capture:
+    def __init__(self, graph, stream):
+        self.graph, self.stream = graph, stream
+        self._ctx = torch.cuda.stream(stream)
+
+    def __enter__(self):
+        self._ctx.__enter__()
+        _check("fsd_graph_begin", lib().fsd_graph_begin(ctypes.c_void_p(self.stream.cuda_stream)))
+        return self.graph
+
+    def __exit__(self, et, ev, tb):
+        h = _c_void_p()
+        st = lib().fsd_graph_end(ctypes.c_void_p(self.stream.cuda_stream), ctypes.byref(h))
+        self._ctx.__exit__(et, ev, tb)
+        if et is None:
+            _check("fsd_graph_end", st)
+            self.graph._g = h.value
+        elif h.value:
+            lib().fsd_graph_destroy(h)
+        return False

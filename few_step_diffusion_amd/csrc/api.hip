@@ -681,6 +681,34 @@ int fsd_mx_lora_up_swiglu_mx(const void* Xq, int64_t ldxq, const void* Xs, const
   return from_hip(fsd::launch_gemm(fsd::GEMM_MX_UP_SWIGLU_MX, p, as_stream(stream)));
 }
 
+int fsd_graph_begin(void* stream) {
+  if (!stream) return FSD_EINVAL;     // the legacy default stream cannot be captured
+  return from_hip(hipStreamBeginCapture(as_stream(stream), hipStreamCaptureModeThreadLocal));
+}
+
+int fsd_graph_end(void* stream, void** graph) {
+  if (!stream || !graph) return FSD_EINVAL;
+  *graph = nullptr;
+  hipGraph_t g = nullptr;
+  if (hipStreamEndCapture(as_stream(stream), &g) != hipSuccess || !g) return FSD_EHIP;
+  hipGraphExec_t exec = nullptr;
+  const hipError_t e = hipGraphInstantiate(&exec, g, nullptr, nullptr, 0);
+  hipGraphDestroy(g);
+  if (e != hipSuccess || !exec) return FSD_EHIP;
+  *graph = (void*)exec;
+  return FSD_OK;
+}
+
+int fsd_graph_launch(void* graph, void* stream) {
+  if (!graph) return FSD_EINVAL;
+  return from_hip(hipGraphLaunch((hipGraphExec_t)graph, as_stream(stream)));
+}
+
+int fsd_graph_destroy(void* graph) {
+  if (!graph) return FSD_OK;
+  return from_hip(hipGraphExecDestroy((hipGraphExec_t)graph));
+}
+
 size_t fsd_attention_workspace_bytes(int64_t S, int64_t H, int64_t D) {
   if (S <= 0 || H <= 0 || D <= 0) return 0;
   return (size_t)(H * D * fsd::attention_padded_tokens(S) * 2);

@@ -194,15 +194,15 @@ class StandinRefiner:
 
     def capture_steps(self, sigmas=SIGMAS, fused=True):
         """One HIP graph per sampler step (the launches of step k over this refiner's fixed
-        buffers, sigmas baked in).  Replaying graph k performs step k on self.z; the renoise
-        stays an ordinary launch.  Nothing is allocated inside the captured region."""
+        buffers, sigmas baked in), captured by the library (fsd_graph_begin / _end).
+        Replaying graph k performs step k on self.z; the renoise stays an ordinary
+        launch.  Nothing is allocated inside the captured region."""
         self.events = None
         graphs = []
         side = torch.cuda.Stream(device=self.dev)
         for k in range(len(sigmas) - 1):
-            g = torch.cuda.CUDAGraph()
             side.wait_stream(torch.cuda.current_stream(self.dev))
-            with torch.cuda.graph(g, stream=side):
+            with fsd.StepGraph.capture(side) as g:
                 self.step(k, sigmas, fused)
             torch.cuda.current_stream(self.dev).wait_stream(side)
             graphs.append(g)
@@ -212,7 +212,7 @@ class StandinRefiner:
         """refine() through graphs from capture_steps()."""
         fsd.renoise(u, eps, sigmas[0], out=self.z)
         for g in graphs:
-            g.replay()
+            g.launch()
         return self.z
 
     def flops_per_step(self) -> dict:

@@ -91,6 +91,15 @@ def test_noalloc_rank_limit_without_a_gpu(L):
     assert rc == EUNSUP
 
 
+def test_graph_entry_points_reject_null(L):
+    h = ctypes.c_void_p()
+    assert L.fsd_graph_begin(None) == EINVAL          # the default stream cannot be captured
+    assert L.fsd_graph_end(None, ctypes.byref(h)) == EINVAL
+    assert L.fsd_graph_end(a(1), None) == EINVAL
+    assert L.fsd_graph_launch(None, None) == EINVAL
+    assert L.fsd_graph_destroy(None) == OK
+
+
 def test_lora_linear_launch_index(L):
     def launch(idx, M=1200, wsb=1200 * 576 * 2):
         return L.fsd_lora_linear_launch(a(1), 1024, a(2), a(3), a(4), None, None, 0,
