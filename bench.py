@@ -20,7 +20,7 @@ Prints ONE JSON line on stdout (everything else goes to stderr):
              median / min / max of 5 batches
   graph_fused  the step as one replayed HIP graph per sampler step with the
              Euler update fused into the head
-  mxfp8      the step with the four linears as MXFP8 GEMMs (quantizers in the
+  mxfp8      the step with the four linears as MXFP8 GEMMs (quantization in the
              step time), the fused SwiGLU->MXFP8 gate/up GEMM against the
              5000 TFLOP/s fp8 peak
   lora_linear_configs  the whole LoRA-fused linear at the 768P shape and on one
@@ -317,9 +317,10 @@ def model_heads():
 
 
 def mx_step(torch, M, u, eps, flops, bf16_ms, args):
-    """The same refine with the four linears as MXFP8 GEMMs (quantizers included in
-    the step time); per-kernel times and the fused SwiGLU->MXFP8 gate/up GEMM
-    against the fp8 MFMA peak."""
+    """The same refine with the four linears as MXFP8 GEMMs, every activation
+    quantized by the kernel that produces it (embed, phase A, QKV / O / gate-up
+    phase B), inside the step time; per-kernel times and the fused SwiGLU->MXFP8
+    gate/up GEMM against the fp8 MFMA peak."""
     from few_step_diffusion_amd.refine import StandinRefiner
     model = StandinRefiner(M, device=u.device, mx=True)
     flops = model.flops_per_step()
@@ -360,7 +361,8 @@ def mx_step(torch, M, u, eps, flops, bf16_ms, args):
             "speedup_vs_bf16": round(bf16_ms / ms, 3),
             "linears": {"ms_per_step": round(lin_ms, 3),
                         "tflops": round(lin_flops / (lin_ms * 1e-3) / 1e12, 1),
-                        "note": "phase A + phase B + activation and T quantizers"},
+                        "note": "phase A (T leaves as MXFP8) + phase B (its output's MXFP8 "
+                                "for the next linear in the same pass)"},
             "dominant": {"kernel": "gate/up phase B, MXFP8 operands, SwiGLU -> MXFP8 epilogue",
                          "bound": "mfma", "achieved": dom["tflops"], "peak": PEAK_FP8_TFLOPS,
                          "unit": "TFLOP/s", "frac": dom["frac_fp8_peak"],

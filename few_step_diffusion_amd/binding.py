@@ -16,7 +16,8 @@ import torch
 __all__ = [
     "FsdError", "library_path", "lib", "abi_version", "lora_merge", "workspace_bytes",
     "lora_down", "lora_up", "lora_linear", "lora_linear_plan", "lora_linear_noalloc", "renoise", "euler_step", "token_embed",
-    "token_head", "token_head_euler", "mx_quantize", "mx_padded_k", "mx_scale_bytes",
+    "token_head", "token_head_euler", "token_embed_mx", "mx_lora_down_mx", "mx_lora_up_q",
+    "mx_quantize", "mx_padded_k", "mx_scale_bytes",
     "mx_scale_offsets", "mx_pack_scales", "mx_unpack_scales", "mx_lora_down", "mx_lora_up",
     "mx_lora_up_swiglu_mx", "attention_workspace_bytes", "attention", "StepGraph",
     "EPI_NONE", "EPI_SWIGLU",
@@ -91,6 +92,14 @@ _SIGS = {
     "fsd_mx_lora_up": ([_c_void_p, _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64,
                         _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _c_void_p,
                         _i64, _i64, _i64, _i64, _i64, _int, _c_void_p], _int),
+    "fsd_mx_lora_down_mx": ([_c_void_p, _i64, _c_void_p, _c_void_p, _c_void_p, _f32, _c_void_p,
+                             _i64, _c_void_p, _i64, _i64, _i64, _c_void_p], _int),
+    "fsd_mx_lora_up_q": ([_c_void_p, _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64,
+                          _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _c_void_p,
+                          _i64, _i64, _i64, _i64, _i64, _i64, _i64, _c_void_p, _i64, _c_void_p,
+                          _c_void_p], _int),
+    "fsd_token_embed_mx": ([_c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64, _i64, _c_void_p,
+                            _i64, _c_void_p, _c_void_p], _int),
     "fsd_attention_workspace_bytes": ([_i64, _i64, _i64], ctypes.c_size_t),
     "fsd_attention": ([_c_void_p, _c_void_p, _c_void_p, _i64, _c_void_p, _i64, _i64, _i64, _i64,
                        _f32, _c_void_p, ctypes.c_size_t, _c_void_p], _int),
@@ -410,6 +419,34 @@ def token_embed(z, E, out=None):
     return out
 
 
+def token_embed_mx(z, E, out=None, Xq=None, Xs=None):
+    """token_embed that also writes X's MXFP8 form: returns (X bf16 [M, D], Xq uint8
+    [M, D], Xs scales), Xq/Xs the bytes mx_quantize(X) would make.  D % 128 == 0."""
+    if z.device.type != "cuda" or z.dtype != torch.float32 or not z.is_contiguous() or z.dim() != 2:
+        raise ValueError("z must be a contiguous fp32 [M, C] GPU tensor")
+    _need(E, "E", torch.bfloat16)
+    M, C = z.shape
+    D = E.shape[0]
+    _shape(E, "E", (D, C), contiguous=True, device=z.device)
+    if out is None:
+        out = torch.empty((M, D), dtype=torch.bfloat16, device=z.device)
+    if Xq is None:
+        Xq = torch.empty((M, mx_padded_k(D)), dtype=torch.uint8, device=z.device)
+    if Xs is None:
+        Xs = torch.empty(max(mx_scale_bytes(M, D), 4), dtype=torch.uint8, device=z.device)
+    _need(out, "out", torch.bfloat16)
+    _shape(out, "out", (M, D), device=z.device)
+    _need(Xq, "Xq", torch.uint8)
+    _shape(Xq, "Xq", (M, mx_padded_k(D)), device=z.device)
+    _need_scales(Xs, "Xs", M, mx_padded_k(D))
+    if Xs.device != z.device:
+        raise ValueError("Xs must be on z's device")
+    st = lib().fsd_token_embed_mx(_ptr(z), _ptr(E), _ptr(out), _ld(out), M, C, D, _ptr(Xq),
+                                  _ld(Xq), _ptr(Xs), _stream(z))
+    _check("fsd_token_embed_mx", st)
+    return out, Xq, Xs
+
+
 def token_head(H, P, out=None):
     """v = H·Pᵀ: H bf16 [M, D], P bf16 [C, D] -> v fp32 [M, C]."""
     _need(H, "H", torch.bfloat16)
@@ -608,6 +645,66 @@ def mx_lora_up_swiglu_mx(Xq, Xs, W0q, W0s, Tq=None, Ts=None, Bq=None, Bs=None, b
                                         _stream(Xq))
     _check("fsd_mx_lora_up_swiglu_mx", st)
     return Hq, Hs
+
+
+def mx_lora_down_mx(Xq, Xs, Aq, As, scale=1.0, Tq=None, Ts=None):
+    """Phase A on MXFP8 operands whose T leaves only as MXFP8: returns (Tq uint8
+    [M, rp], Ts scales), the bytes mx_quantize(mx_lora_down(...)) would make.
+    r = Aq.shape[0] must be a multiple of 32; rp = r rounded up to 128."""
+    _need(Xq, "Xq", torch.uint8)
+    _need(Aq, "Aq", torch.uint8)
+    M, Kp = Xq.shape
+    r = Aq.shape[0]
+    if Aq.shape[1] != Kp or not Aq.is_contiguous():
+        raise ValueError("Aq must be a contiguous [r, Kp] tensor with Xq's Kp")
+    _need_scales(Xs, "Xs", M, Kp)
+    _need_scales(As, "As", r, Kp)
+    rp = mx_padded_k(r)
+    if Tq is None:
+        Tq = torch.empty((M, rp), dtype=torch.uint8, device=Xq.device)
+    if Ts is None:
+        Ts = torch.empty(max(mx_scale_bytes(M, r), 4), dtype=torch.uint8, device=Xq.device)
+    _need(Tq, "Tq", torch.uint8)
+    _shape(Tq, "Tq", (M, rp), device=Xq.device)
+    _need_scales(Ts, "Ts", M, rp)
+    for t, nm in ((Aq, "Aq"), (Xs, "Xs"), (As, "As"), (Ts, "Ts")):
+        if t.device != Xq.device:
+            raise ValueError(f"{nm} must be on Xq's device")
+    st = lib().fsd_mx_lora_down_mx(_ptr(Xq), _ld(Xq), _ptr(Xs), _ptr(Aq), _ptr(As), float(scale),
+                                   _ptr(Tq), _ld(Tq), _ptr(Ts), M, Kp, r, _stream(Xq))
+    _check("fsd_mx_lora_down_mx", st)
+    return Tq, Ts
+
+
+def mx_lora_up_q(Xq, Xs, W0q, W0s, Tq=None, Ts=None, Bq=None, Bs=None, bias=None,
+                 residual=None, out=None, cols=None, Yq=None, Ys=None):
+    """mx_lora_up (plain epilogue) that also writes the MXFP8 form of the output's
+    columns cols = (q0, q1) (default: all): returns (Y, Yq uint8 [M, q1 - q0 rounded
+    up to 128], Ys), Yq/Ys the bytes mx_quantize(Y[:, q0:q1]) would make."""
+    M, N, Kp, rp, ops = _mx_up_operands(Xq, Xs, W0q, W0s, Tq, Ts, Bq, Bs, bias)
+    q0, q1 = (0, N) if cols is None else (int(cols[0]), int(cols[1]))
+    qkp = mx_padded_k(q1 - q0)
+    if residual is not None:
+        _need(residual, "residual", torch.bfloat16)
+        _shape(residual, "residual", (M, N), device=Xq.device)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=Xq.device)
+    if Yq is None:
+        Yq = torch.empty((M, qkp), dtype=torch.uint8, device=Xq.device)
+    if Ys is None:
+        Ys = torch.empty(max(mx_scale_bytes(M, q1 - q0), 4), dtype=torch.uint8, device=Xq.device)
+    _need(out, "out", torch.bfloat16)
+    _shape(out, "out", (M, N), device=Xq.device)
+    _need(Yq, "Yq", torch.uint8)
+    _shape(Yq, "Yq", (M, qkp), device=Xq.device)
+    _need_scales(Ys, "Ys", M, qkp)
+    if Ys.device != Xq.device:
+        raise ValueError("Ys must be on Xq's device")
+    st = lib().fsd_mx_lora_up_q(*ops, _ptr(residual),
+                                _ld(residual) if residual is not None else 0, _ptr(out), _ld(out),
+                                M, N, Kp, rp, q0, q1, _ptr(Yq), _ld(Yq), _ptr(Ys), _stream(Xq))
+    _check("fsd_mx_lora_up_q", st)
+    return out, Yq, Ys
 
 
 # ------------------------------------------------------------ attention

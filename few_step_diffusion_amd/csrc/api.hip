@@ -549,6 +549,32 @@ int fsd_token_embed(const float* z, const void* E, void* X, int64_t ldx, int64_t
                                     as_stream(stream)));
 }
 
+int fsd_token_embed_mx(const float* z, const void* E, void* X, int64_t ldx, int64_t M,
+                       int64_t C, int64_t D, void* Xq, int64_t ldxq, void* Xs, void* stream) {
+  if (M < 0 || C < 1 || C > 32 || D < 128 || D % 8) return FSD_EINVAL;
+  if (D % 128) return FSD_EUNSUPPORTED;
+  if (!z || !E || !X || ldx < D || ldx % 8 || !Xq || !Xs || ldxq < D || ldxq % 16)
+    return FSD_EINVAL;
+  if (!aligned16(X) || ((uintptr_t)z & 3u) || ((uintptr_t)E & 1u) || !aligned16(Xq) ||
+      ((uintptr_t)Xs & 3u))
+    return FSD_EALIGN;
+  if (C * D * 2 > kMaxOffsetBytes || mx_scale_span(M, D) > kMaxOffsetBytes)
+    return FSD_EUNSUPPORTED;
+  if (M == 0) return FSD_OK;
+  const int64_t xb = span_bytes(M, D, ldx, 2);
+  const int64_t qb = span_bytes(M, D, ldxq, 1), sb = mx_scale_span(M, D);
+  const void* in[2] = {z, E};
+  const int64_t inb[2] = {M * C * 4, D * C * 2};
+  for (int i = 0; i < 2; ++i)
+    if (overlap(X, xb, in[i], inb[i]) || overlap(Xq, qb, in[i], inb[i]) ||
+        overlap(Xs, sb, in[i], inb[i]))
+      return FSD_EINVAL;
+  if (overlap(X, xb, Xq, qb) || overlap(X, xb, Xs, sb) || overlap(Xq, qb, Xs, sb))
+    return FSD_EINVAL;
+  return from_hip(fsd::launch_embed_mx(z, (const bf16_t*)E, (bf16_t*)X, ldx, M, (int)C, D,
+                                       (uint8_t*)Xq, ldxq, (uint8_t*)Xs, as_stream(stream)));
+}
+
 int fsd_token_head(const void* H, int64_t ldh, const void* P, float* v, int64_t M, int64_t D,
                    int64_t C, void* stream) {
   if (M < 0 || C < 1 || C > 32 || D < 64 || D % 64) return FSD_EINVAL;
@@ -679,6 +705,81 @@ int fsd_mx_lora_up_swiglu_mx(const void* Xq, int64_t ldxq, const void* Xs, const
   p.Yq = (uint8_t*)Hq; p.ldyq = ldhq;
   p.Ys = (uint8_t*)Hs; p.sYp = round_up(M, kTileM);
   return from_hip(fsd::launch_gemm(fsd::GEMM_MX_UP_SWIGLU_MX, p, as_stream(stream)));
+}
+
+int fsd_mx_lora_down_mx(const void* Xq, int64_t ldxq, const void* Xs, const void* Aq,
+                        const void* As, float scale, void* Tq, int64_t ldtq, void* Ts, int64_t M,
+                        int64_t K, int64_t r, void* stream) {
+  if (M < 0 || K < 32 || K % 32 || r < 32 || r % 32 || !isfinite(scale)) return FSD_EINVAL;
+  const int64_t Kp = round_up(K, 128), rp = round_up(r, 128);
+  if (!Tq || !Ts || ldtq < rp || ldtq % 16) return FSD_EINVAL;
+  if (!aligned16(Tq) || ((uintptr_t)Ts & 3u)) return FSD_EALIGN;
+  if (mx_scale_span(M, rp) > kMaxOffsetBytes) return FSD_EUNSUPPORTED;
+  int st = validate_mx_operand(Xq, ldxq, Xs, M, Kp, false);
+  if (st == FSD_OK) st = validate_mx_operand(Aq, Kp, As, r, Kp, true);
+  if (st != FSD_OK) return st;
+  const int64_t tb = span_bytes(M, rp, ldtq, 1), sb = mx_scale_span(M, rp);
+  if (mx_overlaps(Tq, tb, Xq, ldxq, Xs, M, Kp) || mx_overlaps(Tq, tb, Aq, Kp, As, r, Kp) ||
+      mx_overlaps(Ts, sb, Xq, ldxq, Xs, M, Kp) || mx_overlaps(Ts, sb, Aq, Kp, As, r, Kp) ||
+      overlap(Tq, tb, Ts, sb))
+    return FSD_EINVAL;
+  if (M == 0) return FSD_OK;
+  fsd::GemmParams p;
+  memset(&p, 0, sizeof(p));
+  p.A0 = Xq; p.lda0 = ldxq; p.sA0 = (const uint8_t*)Xs;
+  p.B0 = Aq; p.ldb0 = Kp;   p.sB0 = (const uint8_t*)As;
+  p.M = M; p.N = r; p.K0 = Kp; p.K1 = 0;
+  p.sMp = round_up(M, kTileM); p.sNp = round_up(r, kTileM);
+  p.alpha = scale;
+  p.Yq = (uint8_t*)Tq; p.ldyq = ldtq;
+  p.Ys = (uint8_t*)Ts; p.sYp = round_up(M, kTileM);
+  p.q0 = 0; p.q1 = r;
+  return from_hip(fsd::launch_gemm(fsd::GEMM_MX_DOWN_Q, p, as_stream(stream)));
+}
+
+int fsd_mx_lora_up_q(const void* Xq, int64_t ldxq, const void* Xs, const void* W0q,
+                     const void* W0s, const void* Tq, int64_t ldtq, const void* Ts,
+                     const void* Bq, const void* Bs, const float* bias, const void* residual,
+                     int64_t ldr, void* Y, int64_t ldy, int64_t M, int64_t N, int64_t K,
+                     int64_t r, int64_t q0, int64_t q1, void* Yq, int64_t ldyq, void* Ys,
+                     void* stream) {
+  if (N < 8 || q0 < 0 || q0 % 32 || q1 % 32 || q1 <= q0 || q1 > N) return FSD_EINVAL;
+  const int64_t qkp = round_up(q1 - q0, 128);
+  if (!Y || ldy < N || ldy % 8) return FSD_EINVAL;
+  if (residual && (ldr < N || ldr % 8)) return FSD_EINVAL;
+  if (!Yq || !Ys || ldyq < qkp || ldyq % 16) return FSD_EINVAL;
+  if (!aligned16(Y) || (residual && !aligned16(residual)) || !aligned16(Yq) ||
+      ((uintptr_t)Ys & 3u))
+    return FSD_EALIGN;
+  if (residual && kTileM * ldr * 2 > kMaxOffsetBytes) return FSD_EUNSUPPORTED;
+  if (mx_scale_span(M, qkp) > kMaxOffsetBytes) return FSD_EUNSUPPORTED;
+  const int64_t yb = span_bytes(M, N, ldy, 2);
+  const int64_t qb = span_bytes(M, qkp, ldyq, 1), sb = mx_scale_span(M, qkp);
+  int st = validate_mx_up_inputs(Xq, ldxq, Xs, W0q, W0s, Tq, ldtq, Ts, Bq, Bs, bias, M, N, K, r,
+                                 Y, yb);
+  if (st == FSD_OK)
+    st = validate_mx_up_inputs(Xq, ldxq, Xs, W0q, W0s, Tq, ldtq, Ts, Bq, Bs, bias, M, N, K, r,
+                               Yq, qb);
+  if (st == FSD_OK)
+    st = validate_mx_up_inputs(Xq, ldxq, Xs, W0q, W0s, Tq, ldtq, Ts, Bq, Bs, bias, M, N, K, r,
+                               Ys, sb);
+  if (st != FSD_OK) return st;
+  const int64_t rb = residual ? span_bytes(M, N, ldr, 2) : 0;
+  if (residual) {
+    const bool same = residual == Y && ldr == ldy;
+    if (!same && overlap(Y, yb, residual, rb)) return FSD_EINVAL;
+  }
+  if (overlap(Yq, qb, Ys, sb) || overlap(Yq, qb, Y, yb) || overlap(Ys, sb, Y, yb) ||
+      overlap(Yq, qb, residual, rb) || overlap(Ys, sb, residual, rb))
+    return FSD_EINVAL;
+  if (M == 0) return FSD_OK;
+  fsd::GemmParams p = mx_up_params(Xq, ldxq, Xs, W0q, W0s, Tq, ldtq, Ts, Bq, Bs, bias, M, N, K, r);
+  p.res = (const bf16_t*)residual; p.ldr = ldr;
+  p.Y = (bf16_t*)Y; p.ldy = ldy;
+  p.Yq = (uint8_t*)Yq; p.ldyq = ldyq;
+  p.Ys = (uint8_t*)Ys; p.sYp = round_up(M, kTileM);
+  p.q0 = q0; p.q1 = q1;
+  return from_hip(fsd::launch_gemm(fsd::GEMM_MX_UP_Q, p, as_stream(stream)));
 }
 
 int fsd_graph_begin(void* stream) {

@@ -31,10 +31,13 @@ struct GemmParams {
   const uint8_t* sA0; const uint8_t* sB0;
   const uint8_t* sA1; const uint8_t* sB1;
   int64_t sMp, sNp;
-  // SwiGLU -> MXFP8 output (GEMM_MX_UP_SWIGLU_MX): E4M3 bytes [M, N/2] with row
-  // stride ldyq and their scales for sYp (M rounded up to 256) rows
+  // MXFP8 output (GEMM_MX_UP_SWIGLU_MX: SwiGLU's H, [M, N/2]; GEMM_MX_DOWN_Q and
+  // GEMM_MX_UP_Q: output columns [q0, q1), as a matrix [M, q1 - q0] padded to a
+  // multiple of 128): E4M3 bytes with row stride ldyq and their scales for sYp
+  // (M rounded up to 256) rows
   uint8_t* Yq; int64_t ldyq;
   uint8_t* Ys; int64_t sYp;
+  int64_t q0, q1;
 };
 
 enum GemmKind {
@@ -44,7 +47,9 @@ enum GemmKind {
   GEMM_MX_DOWN = 3,     // the same three with MXFP8 operands
   GEMM_MX_UP = 4,
   GEMM_MX_UP_SWIGLU = 5,
-  GEMM_MX_UP_SWIGLU_MX = 6  // ... whose H leaves quantized to MXFP8 (N/2 % 128 == 0)
+  GEMM_MX_UP_SWIGLU_MX = 6, // ... whose H leaves quantized to MXFP8 (N/2 % 128 == 0)
+  GEMM_MX_DOWN_Q = 7,       // MX phase A whose T leaves as MXFP8 (Y may be null)
+  GEMM_MX_UP_Q = 8          // MX phase B, bf16 Y plus MXFP8 of columns [q0, q1)
 };
 
 hipError_t launch_gemm(GemmKind kind, const GemmParams& p, hipStream_t s);
@@ -62,6 +67,11 @@ hipError_t launch_merge_cols(const float* src, int64_t rows, int64_t cols, float
                              bf16_t* dst, int64_t ld_dst, hipStream_t s);
 hipError_t launch_embed(const float* z, const bf16_t* E, bf16_t* X, int64_t ldx, int64_t M,
                         int C, int64_t D, hipStream_t s);
+// embed whose X also leaves as MXFP8 (codes [M, D] with row stride ldxq, scales
+// for M rounded up to 256 rows; D a multiple of 128)
+hipError_t launch_embed_mx(const float* z, const bf16_t* E, bf16_t* X, int64_t ldx, int64_t M,
+                           int C, int64_t D, uint8_t* Xq, int64_t ldxq, uint8_t* Xs,
+                           hipStream_t s);
 hipError_t launch_head(const bf16_t* H, int64_t ldh, const bf16_t* P, float* v, int64_t M,
                        int64_t D, int C, hipStream_t s);
 hipError_t launch_head_euler(const bf16_t* H, int64_t ldh, const bf16_t* P, float* z,

@@ -115,7 +115,9 @@ __device__ __forceinline__ void static_for(Fn&& fn) {
 
 // MX: E4M3 operands with E8M0 block scales (v_mfma_scale_f32_16x16x128_f8f6f4):
 // a K step is 128 elements, still one 128-byte line per tile row.
-// QOUT (with SWIGLU): H leaves as MXFP8 (E4M3 bytes and scales) instead of bf16.
+// QOUT with SWIGLU: H leaves as MXFP8 (E4M3 bytes and scales) instead of bf16.
+// QOUT without SWIGLU: the bf16 output (when p.Y is set) plus the MXFP8 form of
+// its columns [p.q0, p.q1), in the bytes the quantizer would write from it.
 constexpr int kLdsBytes = 160 * 1024;      // gfx950's LDS per CU: every tile shape fits
 
 // One output tile of one GEMM (workgroup `wg` of the launch's tiles of this
@@ -224,7 +226,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const int wg, cha
   // wave regions (wave columns 0 and 1) of 64 rows x 256 bytes whose 16-byte
   // chunks are XOR-swizzled by the row's low 4 bits.  The same number of
   // loads is issued as for a K step, so the loaders' vmcnt waits are unchanged.
-  constexpr bool RES_PF = !SWIGLU && !QOUT && WM == 2 && WN == 4 && A_STAGE == 32768 &&
+  constexpr bool RES_PF = !SWIGLU && WM == 2 && WN == 4 && A_STAGE == 32768 &&
                           B_STAGE == 32768 && A_PER == 8 && B_PER == 8;
   const bool res_pf = RES_PF && p.res != nullptr;
   const __amdgpu_buffer_rsrc_t rR =
@@ -652,7 +654,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const int wg, cha
     }
   }
   __builtin_amdgcn_s_waitcnt(0);   // the wave's staged tile is complete (its own region)
-  if constexpr (QOUT) {
+  if constexpr (QOUT && SWIGLU) {
     // SwiGLU -> MXFP8 in one pass: the wave's staged 64 x 64 bf16 tile of H is
     // two 32-column blocks per row.  Lane l quantizes block l >> 5 of rows
     // 16·i + l%16, i = 2·((l >> 4) & 1) + k for k = 0, 1, stores its 32 E4M3
@@ -693,12 +695,110 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const int wg, cha
     }
     return;
   }
-  for (int idx = lane; idx < OROWS * OCH; idx += 64) {
-    const int row = idx / OCH, pc = idx % OCH;
-    const int64_t c = col0 + pchunk(row, pc) * 8;
-    if (tok0 + row < rows_valid && c < Nout) {
-      const u32x4 v = *(const u32x4*)(ow + row * PITCH + pc * 16);
-      __builtin_nontemporal_store(v, (u32x4*)(p.Y + (m0 + tok0 + row) * p.ldy + c));
+  if (!QOUT || p.Y) {
+    for (int idx = lane; idx < OROWS * OCH; idx += 64) {
+      const int row = idx / OCH, pc = idx % OCH;
+      const int64_t c = col0 + pchunk(row, pc) * 8;
+      if (tok0 + row < rows_valid && c < Nout) {
+        const u32x4 v = *(const u32x4*)(ow + row * PITCH + pc * 16);
+        __builtin_nontemporal_store(v, (u32x4*)(p.Y + (m0 + tok0 + row) * p.ldy + c));
+      }
+    }
+  }
+  if constexpr (QOUT) {
+    // The staged bf16 tile -> MXFP8 of output columns [q0, q1), i.e. column
+    // c - q0 of a matrix of qk = q1 - q0 columns padded to qkp (a multiple of
+    // 128) with zero elements and scale 127.  Lane l quantizes row l of the
+    // wave for each of its NBLK 32-column blocks (q0 and q1 are multiples of
+    // 32, so a block is wholly inside, past q1 (padding), or outside).  The
+    // 32 code bytes of block b overwrite logical chunks 2b, 2b + 1 of the
+    // lane's own staged row, which hold bf16 of blocks it has already read;
+    // the codes then leave as whole row segments, 16 bytes per lane over
+    // consecutive addresses.  (Each lane storing its own row's 32 bytes
+    // instead touched 64 lines per store and cost about 14 us per tile.)
+    // The scale byte goes into LDS at its place in the scale layout: byte
+    // (row >> 4) of dword 16·b + row % 16 of the (K step, 64-row group)
+    // region, b = the block within its K step.  Rows past M store no elements
+    // and scale 127.  The scale staging sits past the tiles' staging regions
+    // (with the residual prefetch: in A slot (nk + 2) % 3, which neither the
+    // residual nor the last K step's fragments occupy any more).
+    constexpr int NBLK = OC / 32;
+    static_assert(OC % 32 == 0 && OROWS == 64, "whole blocks, one 64-row group per wave");
+    constexpr int SCB = NBLK * 64;                     // scale bytes per wave
+    static_assert(RES_PF ? kWaves * SCB <= A_STAGE
+                         : kWaves * (OROWS * PITCH + SCB) <= LDS_BYTES,
+                  "scale staging must fit in LDS");
+    const int sbase = RES_PF ? ((nk + 2) % 3) * A_STAGE : kWaves * OROWS * PITCH;
+    uint8_t* sl = (uint8_t*)(lds + sbase + wave * SCB);
+    const int64_t qk = p.q1 - p.q0;
+    const int64_t qkp = (qk + 127) / 128 * 128;
+    const int64_t g = (m0 + tok0) >> 6;                // the wave's 64-row group
+    const int64_t sgrp = p.sYp >> 6;                   // 64-row groups per K step
+    const int row = lane;
+    const bool valid = tok0 + row < rows_valid;
+    uint8_t* yq_row = p.Yq + (m0 + tok0 + row) * p.ldyq;
+    int b_lo = NBLK, b_hi = 0;                         // the wave's blocks in [0, qkp)
+#pragma unroll
+    for (int blk = 0; blk < NBLK; ++blk) {
+      const int64_t qc = col0 + 32 * blk - p.q0;       // wave-uniform
+      if (qc < 0 || qc >= qkp) continue;
+      uint32_t q[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+      uint32_t sbyte = 127u;
+      if (qc < qk) {
+        uint32_t w[16];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const u32x4 v = *(const u32x4*)(ow + row * PITCH + pchunk(row, 4 * blk + c) * 16);
+          w[4 * c] = v.x; w[4 * c + 1] = v.y; w[4 * c + 2] = v.z; w[4 * c + 3] = v.w;
+        }
+        sbyte = mx_block_bf16(w, q);
+      }
+      {
+        char* rowp = ow + row * PITCH;
+        *(u32x4*)(rowp + pchunk(row, 2 * blk) * 16) = (u32x4){q[0], q[1], q[2], q[3]};
+        *(u32x4*)(rowp + pchunk(row, 2 * blk + 1) * 16) = (u32x4){q[4], q[5], q[6], q[7]};
+      }
+      b_lo = blk < b_lo ? blk : b_lo;
+      b_hi = blk + 1;
+      sl[(16 * blk + (row & 15)) * 4 + (row >> 4)] = (uint8_t)(valid ? sbyte : 127u);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    for (int idx = lane; idx < OROWS * 2 * NBLK; idx += 64) {
+      const int r = idx / (2 * NBLK), ch = idx % (2 * NBLK);
+      const int bb = ch >> 1;
+      if (bb >= b_lo && bb < b_hi && tok0 + r < rows_valid) {
+        const u32x4 v = *(const u32x4*)(ow + r * PITCH + pchunk(r, ch) * 16);
+        __builtin_nontemporal_store(
+            v, (u32x4*)(p.Yq + (m0 + tok0 + r) * p.ldyq + (col0 - p.q0) + ch * 16));
+      }
+    }
+    if (lane < NBLK * 16) {
+      const int blk = lane >> 4, r = lane & 15;
+      const int64_t qc = col0 + 32 * blk - p.q0;
+      if (qc >= 0 && qc < qkp) {
+        const int64_t B = qc >> 5;
+        const uint32_t word = *(const uint32_t*)(sl + lane * 4);
+        __builtin_nontemporal_store(
+            word, (uint32_t*)p.Ys + ((B >> 2) * sgrp + g) * 64 + 16 * (B & 3) + r);
+      }
+    }
+    // padding blocks that no tile covers (at most three, past the last tile
+    // column): the last wave column of the last tile column writes them
+    const int64_t covered = (int64_t)tiles_n * TN;     // output columns the tiles span
+    if (tn == tiles_n - 1 && wn == kWaveCols - 1 && p.q0 + qkp > covered) {
+      for (int64_t qc = (covered - p.q0 + 31) / 32 * 32; qc < qkp; qc += 32) {
+        if (qc < 0) continue;
+        if (valid) {
+          u32x4* dst = (u32x4*)(yq_row + qc);
+          __builtin_nontemporal_store((u32x4){0u, 0u, 0u, 0u}, dst);
+          __builtin_nontemporal_store((u32x4){0u, 0u, 0u, 0u}, dst + 1);
+        }
+        if (lane < 16) {
+          const int64_t B = qc >> 5;
+          __builtin_nontemporal_store(
+              0x7f7f7f7fu, (uint32_t*)p.Ys + ((B >> 2) * sgrp + g) * 64 + 16 * (B & 3) + lane);
+        }
+      }
     }
   }
 }
@@ -759,6 +859,8 @@ hipError_t launch_gemm(GemmKind kind, const GemmParams& p, hipStream_t s) {
     case GEMM_MX_UP: return launch<2, 4, false, true>(p, s);
     case GEMM_MX_UP_SWIGLU: return launch<2, 4, true, true>(p, s);
     case GEMM_MX_UP_SWIGLU_MX: return launch<2, 4, true, true, true>(p, s);
+    case GEMM_MX_DOWN_Q: return launch<2, 3, false, true, true>(p, s);
+    case GEMM_MX_UP_Q: return launch<2, 4, false, true, true>(p, s);
   }
   return hipErrorInvalidValue;
 }

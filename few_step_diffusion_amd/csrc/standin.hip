@@ -28,6 +28,7 @@
 //   steps instead of dozens", Euler update equation) to the latent in place
 //   as it produces v, so v never goes through HBM.
 #include "fsd_internal.h"
+#include "mx_codec.h"
 
 namespace fsd {
 
@@ -63,9 +64,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 // 256-byte bank line.
 __device__ __forceinline__ int embed_swz(int r, int c) { return c ^ ((r >> 1) & 7); }
 
+// QX: X also leaves as MXFP8 (codes Xq with row stride ldxq, scales Xs for sMp
+// rows in the quantizer's layout; D a multiple of 128, so every slab is 64
+// whole columns): after a slab's bf16 rows are written, lane l quantizes the
+// two 32-column blocks of staged rows l and l + 64, exactly as the quantizer
+// would from the stored X, puts the codes over the row's first four chunks
+// (already read) and the slab's codes leave as 64-byte row segments.
+template <bool QX>
 __global__ __launch_bounds__(kThreads) void embed_kernel(const float* z, const bf16_t* E,
                                                          bf16_t* X, int64_t ldx, int64_t M,
-                                                         int C, int64_t D, int vec_e) {
+                                                         int C, int64_t D, int vec_e,
+                                                         uint8_t* Xq, int64_t ldxq, uint8_t* Xs,
+                                                         int64_t sMp) {
   const int lane = threadIdx.x & 63;
   const int64_t wave_id = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
   const int64_t nchunk = (D + kEmbedCols - 1) / kEmbedCols;
@@ -156,6 +166,56 @@ __global__ __launch_bounds__(kThreads) void embed_kernel(const float* z, const b
         const int64_t nn = col + 8 * lc;
         const u32x4 v = *(const u32x4*)(stage + r * 128 + (pc << 4));
         if (t < M && nn < D) __builtin_nontemporal_store(v, (u32x4*)(X + t * ldx + nn));
+      }
+      if constexpr (QX) {
+        // scale bytes of the slab: 2 blocks x 2 64-row groups x 16 dwords,
+        // dword (2·blk + group)·16 + r holding rows 16i + r of the group
+        __shared__ __attribute__((aligned(16))) uint8_t sc_all[(kThreads / 64) * 256];
+        uint8_t* sl = sc_all + (threadIdx.x >> 6) * 256;
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) {
+          const int r = lane + 64 * rr;
+          const int64_t t = m0 + r;
+#pragma unroll
+          for (int blk = 0; blk < 2; ++blk) {
+            uint32_t w[16];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              const u32x4 v = *(const u32x4*)(stage + r * 128 + (embed_swz(r, 4 * blk + c) << 4));
+              w[4 * c] = v.x; w[4 * c + 1] = v.y; w[4 * c + 2] = v.z; w[4 * c + 3] = v.w;
+            }
+            uint32_t q[8];
+            const uint32_t sbyte = mx_block_bf16(w, q);
+            {
+              char* rowp = stage + r * 128;
+              *(u32x4*)(rowp + (embed_swz(r, 2 * blk) << 4)) = (u32x4){q[0], q[1], q[2], q[3]};
+              *(u32x4*)(rowp + (embed_swz(r, 2 * blk + 1) << 4)) = (u32x4){q[4], q[5], q[6], q[7]};
+            }
+            sl[((2 * blk + rr) * 16 + (r & 15)) * 4 + ((r & 63) >> 4)] =
+                (uint8_t)(t < M ? sbyte : 127u);
+          }
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+#pragma unroll
+        for (int it = 0; it < kEmbedTokens / 16; ++it) {
+          const int r = 16 * it + (lane >> 2), ch = lane & 3;
+          const int64_t t = m0 + r;
+          if (t < M) {
+            const u32x4 v = *(const u32x4*)(stage + r * 128 + (embed_swz(r, ch) << 4));
+            __builtin_nontemporal_store(v, (u32x4*)(Xq + t * ldxq + col + 16 * ch));
+          }
+        }
+        // lane = 32·blk + 16·group + r
+        const int blk = lane >> 5, grp = (lane >> 4) & 1, r16 = lane & 15;
+        const int64_t B = (col >> 5) + blk;
+        const int64_t base = (B >> 2) * (sMp >> 6);
+        uint32_t* sdst = (uint32_t*)Xs + 16 * (B & 3) + r16;
+        __builtin_nontemporal_store(*(const uint32_t*)(sl + lane * 4),
+                                    sdst + (base + (m0 >> 6) + grp) * 64);
+        // the last token wave also fills the padding groups up to sMp (rows
+        // past M, never covered by a wave of 128 tokens): scale 127
+        if (m0 + kEmbedTokens >= M && m0 + kEmbedTokens < sMp)
+          __builtin_nontemporal_store(0x7f7f7f7fu, sdst + (base + (m0 >> 6) + 2 + grp) * 64);
       }
       __builtin_amdgcn_s_waitcnt(0xc07f);            // reads done before the next slab's writes
     }
@@ -264,8 +324,24 @@ hipError_t launch_embed(const float* z, const bf16_t* E, bf16_t* X, int64_t ldx,
   const int64_t blocks = (waves + kThreads / 64 - 1) / (kThreads / 64);
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   const int vec_e = (C % 8 == 0) && (((uintptr_t)E & 15u) == 0);
-  hipLaunchKernelGGL(embed_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, z, E, X, ldx,
-                     M, C, D, vec_e);
+  hipLaunchKernelGGL(embed_kernel<false>, dim3((unsigned)blocks), dim3(kThreads), 0, s, z, E, X,
+                     ldx, M, C, D, vec_e, nullptr, (int64_t)0, nullptr, (int64_t)0);
+  return hipGetLastError();
+}
+
+hipError_t launch_embed_mx(const float* z, const bf16_t* E, bf16_t* X, int64_t ldx, int64_t M,
+                           int C, int64_t D, uint8_t* Xq, int64_t ldxq, uint8_t* Xs,
+                           hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  if (D % 128) return hipErrorInvalidValue;
+  const int64_t waves = ((M + kEmbedTokens - 1) / kEmbedTokens) *
+                        ((D + kEmbedCols - 1) / kEmbedCols);
+  const int64_t blocks = (waves + kThreads / 64 - 1) / (kThreads / 64);
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  const int vec_e = (C % 8 == 0) && (((uintptr_t)E & 15u) == 0);
+  const int64_t sMp = (M + 255) / 256 * 256;
+  hipLaunchKernelGGL(embed_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), 0, s, z, E, X,
+                     ldx, M, C, D, vec_e, Xq, ldxq, Xs, sMp);
   return hipGetLastError();
 }
 

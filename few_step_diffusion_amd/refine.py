@@ -34,11 +34,15 @@ class StandinRefiner:
 
     def __init__(self, M: int, device="cuda:0", wid: int = 4, D: int = inputs.STANDIN_D,
                  F: int = inputs.STANDIN_F, ranks=inputs.RANKS, C: int = inputs.LATENT_C,
-                 scale: float = 1.0, mx: bool = False, attention: bool = False):
+                 scale: float = 1.0, mx: bool = False, attention: bool = False,
+                 mx_onepass: bool = True):
         """mx: run the four linears as MXFP8 GEMMs.  The bf16 weights are quantized
-        once here; each linear quantizes its bf16 input and its bf16 LoRA down output,
-        and the gate/up GEMM hands SwiGLU's output to the down projection already
-        quantized."""
+        once here.  Every linear's input and its LoRA down output are the MXFP8 of
+        their bf16 values.  mx_onepass (default): each producer writes that MXFP8
+        form in the same pass (embed -> QKV input, phase A -> T, QKV phase B -> the
+        V slice, O phase B -> the gate/up input, gate/up phase B -> SwiGLU's
+        output); otherwise separate quantizer passes read the bf16 values back
+        (SwiGLU's output stays fused).  The two routes write the same bytes."""
         dev = torch.device(device)
         if attention and (mx or D % 128):
             raise ValueError("the attention step runs on the bf16 path with heads of 128")
@@ -48,6 +52,7 @@ class StandinRefiner:
         self.R = sum(ranks)
         self.scale = scale
         self.mx = mx
+        self.onepass = mx and mx_onepass
         self.layers = []
         for L in inputs.standin_layers(wid, D, F, ranks):
             A, B = fsd.lora_merge([a.to(dev) for a in L["A_list"]],
@@ -65,7 +70,8 @@ class StandinRefiner:
         self.qkv = torch.empty((M, 3 * D), dtype=bf, device=dev)
         self.g = torch.empty((M, F), dtype=bf, device=dev)            # SwiGLU output
         if mx:
-            self.T = torch.empty((M, self.R), dtype=bf, device=dev)  # LoRA down output
+            if not self.onepass:
+                self.T = torch.empty((M, self.R), dtype=bf, device=dev)  # LoRA down output
         else:
             # T of the bf16 linears: two chunks of 21,760 rows (50 MB at rank 576),
             # shared by the four linears (they run one after another on one stream)
@@ -130,6 +136,24 @@ class StandinRefiner:
         else:
             fsd.mx_lora_up(*Xmx, *L["W0q"], *self.tq, *L["Bq"], residual=residual, out=out)
 
+    # one MXFP8 LoRA linear whose T never exists in bf16: phase A writes its MXFP8
+    # form, phase B optionally the MXFP8 form of (some of) its output columns
+    def _mx_linear_onepass(self, idx, Xmx, out=None, residual=None, swiglu_mx=False,
+                           qout=None, cols=None):
+        L = self.layers[idx]
+        name = self.LAYER_NAMES[idx]
+        self._mark(f"{name}.down")
+        fsd.mx_lora_down_mx(*Xmx, *L["Aq"], self.scale, *self.tq)
+        self._mark(f"{name}.up")
+        if swiglu_mx:
+            fsd.mx_lora_up_swiglu_mx(*Xmx, *L["W0q"], *self.tq, *L["Bq"], Hq=self.gq[0],
+                                     Hs=self.gq[1])
+        elif qout is not None:
+            fsd.mx_lora_up_q(*Xmx, *L["W0q"], *self.tq, *L["Bq"], residual=residual, out=out,
+                             cols=cols, Yq=qout[0], Ys=qout[1])
+        else:
+            fsd.mx_lora_up(*Xmx, *L["W0q"], *self.tq, *L["Bq"], residual=residual, out=out)
+
     def _quantize(self, name, X, buf):
         self._mark(name)
         fsd.mx_quantize(X, *buf)
@@ -139,6 +163,13 @@ class StandinRefiner:
         """embed, then the four linears; leaves the block output in self.h."""
         D = self.D
         self._mark("embed")
+        if self.onepass:
+            fsd.token_embed_mx(self.z, self.E, out=self.h, Xq=self.hq[0], Xs=self.hq[1])
+            self._mx_linear_onepass(0, self.hq, self.qkv, qout=self.vq, cols=(2 * D, 3 * D))
+            self._mx_linear_onepass(1, self.vq, self.h, residual=self.h, qout=self.hq)
+            self._mx_linear_onepass(2, self.hq, swiglu_mx=True)
+            self._mx_linear_onepass(3, self.gq, self.h, residual=self.h)
+            return
         fsd.token_embed(self.z, self.E, out=self.h)
         if self.mx:
             self._mx_linear(0, self._quantize("qkv.quant_x", self.h, self.hq), self.qkv)

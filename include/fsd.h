@@ -346,6 +346,43 @@ int fsd_mx_lora_up_swiglu_mx(const void* Xq, int64_t ldxq, const void* Xs,
                              int64_t ldhq, void* Hs, int64_t M, int64_t N,
                              int64_t K, int64_t r, void* stream);
 
+/* One-pass activation quantization: the producer of an activation emits its
+ * MXFP8 form in the same pass, so no separate quantizer pass reads it back
+ * (the pages list "one-pass activation quantization" among their kernels,
+ * [EN] "Where the 3.9x speedup comes from", inference-configuration table).
+ * Each one writes the bytes that the unfused route (the bf16 result, then
+ * fsd_mx_quantize of it) writes: the value is rounded to bf16 first, then
+ * quantized.  Code arrays 16-byte aligned with row strides multiples of 16,
+ * scale arrays 4-byte aligned and sized by fsd_mx_scale_bytes; outputs must
+ * not overlap any input or each other (else FSD_EINVAL).
+ *
+ * fsd_mx_lora_down_mx: fsd_mx_lora_down whose T leaves only as MXFP8: Tq
+ *   [M, rp] (rp = r rounded up to 128, row stride ldtq >= rp) and Ts for M
+ *   rows of r; r a multiple of 32.  Tq, Ts are what fsd_mx_lora_up takes.
+ * fsd_mx_lora_up_q: fsd_mx_lora_up (plain epilogue: bias, residual) that
+ *   writes Y and also the MXFP8 form of Y's columns [q0, q1) as a matrix of
+ *   q1 - q0 columns: Yq (row stride ldyq >= (q1 - q0) rounded up to 128) and
+ *   Ys.  q0, q1 multiples of 32 with 0 <= q0 < q1 <= N.  Used for the V slice
+ *   of the QKV output (the O projection's input) and for the residual stream
+ *   after the O projection (the gate/up input).
+ * fsd_token_embed_mx: fsd_token_embed that also writes the MXFP8 form of X
+ *   (Xq [M, D], row stride ldxq >= D, and Xs); D a multiple of 128 (else
+ *   FSD_EUNSUPPORTED). */
+int fsd_mx_lora_down_mx(const void* Xq, int64_t ldxq, const void* Xs,
+                        const void* Aq, const void* As, float scale, void* Tq,
+                        int64_t ldtq, void* Ts, int64_t M, int64_t K, int64_t r,
+                        void* stream);
+int fsd_mx_lora_up_q(const void* Xq, int64_t ldxq, const void* Xs,
+                     const void* W0q, const void* W0s, const void* Tq,
+                     int64_t ldtq, const void* Ts, const void* Bq, const void* Bs,
+                     const float* bias, const void* residual, int64_t ldr,
+                     void* Y, int64_t ldy, int64_t M, int64_t N, int64_t K,
+                     int64_t r, int64_t q0, int64_t q1, void* Yq, int64_t ldyq,
+                     void* Ys, void* stream);
+int fsd_token_embed_mx(const float* z, const void* E, void* X, int64_t ldx,
+                       int64_t M, int64_t C, int64_t D, void* Xq, int64_t ldxq,
+                       void* Xs, void* stream);
+
 /* ------------------------------------------------------------------------ *
  * Dense attention (NEXT step: the refine path's baseline attention)          *
  * ------------------------------------------------------------------------ *

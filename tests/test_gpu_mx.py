@@ -224,6 +224,122 @@ def test_mx_swiglu_quantize_epilogue(gpu, M, N, K, r, bias):
     assert_mx_valid(Hq, Hs, h, dh, f"fused swiglu->mx M={M} N={N}")
 
 
+# ------------------------------------------ one-pass activation quantization
+def _garbage(t):
+    """Fill an output buffer with a pattern no kernel writes by accident, so a byte
+    the fused kernel leaves unwritten fails the comparison."""
+    return t.fill_(0xA5)
+
+
+@pytest.mark.parametrize("M,K,r", [(1, 32, 576), (300, 1024, 576), (257, 608, 64),
+                                   (513, 256, 96), (70, 128, 640), (256, 128, 384)])
+def test_mx_down_mx_one_pass(gpu, M, K, r):
+    """Phase A writing T straight as MXFP8: the bytes of the unfused route (bf16 T,
+    then the quantizer), padding columns and scales included; and T's codes are
+    the oracle quantizer's codes of the GPU's bf16 T."""
+    say(f"mx down->mx M={M} K={K} r={r}")
+    rng = np.random.default_rng(11 * M + K + 3 * r)
+    Qx, Sx, _ = mx_operand(rng.standard_normal((M, K)), gpu)
+    Qa, Sa, _ = mx_operand(rng.standard_normal((r, K)) * 0.02, gpu)
+    rp = fsd.mx_padded_k(r)
+    Tq = _garbage(torch.empty((M, rp), dtype=torch.uint8, device=gpu))
+    Ts = _garbage(torch.empty(fsd.mx_scale_bytes(M, r), dtype=torch.uint8, device=gpu))
+    fsd.mx_lora_down_mx(Qx, Sx, Qa, Sa, 0.5, Tq, Ts)
+    T = fsd.mx_lora_down(Qx, Sx, Qa, Sa, scale=0.5)
+    Tq2, Ts2 = fsd.mx_quantize(T)
+    assert torch.equal(Tq, Tq2), "codes differ from the unfused route"
+    assert torch.equal(Ts, Ts2), "scales differ from the unfused route"
+    q_ref, s_ref = mx.quantize_rows(T.float().cpu().numpy())
+    assert np.array_equal(Tq.cpu().numpy(), q_ref)
+    s_rows = scales_by_row(Ts, M, r)
+    assert np.array_equal(s_rows[:M], s_ref) and np.all(s_rows[M:] == 127)
+
+
+@pytest.mark.parametrize("M,N,K,r,cols,extras", [
+    (300, 512, 1024, 576, (0, 512), "res+bias"),
+    (300, 768, 256, 64, (512, 768), "none"),          # a trailing slice, like QKV's V
+    (513, 384, 128, 0, (32, 352), "res"),             # ragged: padded to 384 columns
+    (1, 256, 128, 576, (0, 256), "inplace"),
+    (70, 320, 128, 0, (64, 320), "inplace+bias"),
+])
+def test_mx_up_q_one_pass(gpu, M, N, K, r, cols, extras):
+    """Phase B writing Y and the MXFP8 form of Y's columns [q0, q1): Y is the bf16
+    output of the plain phase B bit for bit, and the codes and scales are the
+    quantizer's bytes of that Y slice."""
+    say(f"mx up+q M={M} N={N} K={K} r={r} cols={cols} {extras}")
+    rng = np.random.default_rng(M + 7 * N + K + r)
+    Qx, Sx, _ = mx_operand(rng.standard_normal((M, K)), gpu)
+    Qw, Sw, _ = mx_operand(rng.standard_normal((N, K)) * 0.03, gpu)
+    if r:
+        Qt, St, _ = mx_operand(rng.standard_normal((M, r)) * 0.3, gpu)
+        Qb, Sb, _ = mx_operand(rng.standard_normal((N, r)) * 0.02, gpu)
+    else:
+        Qt = St = Qb = Sb = None
+    bias = None
+    if "bias" in extras:
+        bias = torch.from_numpy(rng.standard_normal(N).astype(np.float32) * 0.1).to(gpu)
+    res = None
+    if extras != "none":
+        res = torch.from_numpy(rng.standard_normal((M, N))).to(torch.bfloat16).to(gpu)
+    q0, q1 = cols
+    qkp = fsd.mx_padded_k(q1 - q0)
+    Yq = _garbage(torch.empty((M, qkp), dtype=torch.uint8, device=gpu))
+    Ys = _garbage(torch.empty(fsd.mx_scale_bytes(M, q1 - q0), dtype=torch.uint8, device=gpu))
+    if "inplace" in extras:
+        Y = res.clone()
+        Y1, _, _ = fsd.mx_lora_up_q(Qx, Sx, Qw, Sw, Qt, St, Qb, Sb, bias=bias, residual=Y, out=Y,
+                                    cols=cols, Yq=Yq, Ys=Ys)
+        Y2 = res.clone()
+        fsd.mx_lora_up(Qx, Sx, Qw, Sw, Qt, St, Qb, Sb, bias=bias, residual=Y2, out=Y2)
+    else:
+        Y1 = _garbage(torch.empty((M, N), dtype=torch.bfloat16, device=gpu).view(torch.uint8)
+                      ).view(torch.bfloat16)
+        fsd.mx_lora_up_q(Qx, Sx, Qw, Sw, Qt, St, Qb, Sb, bias=bias, residual=res, out=Y1,
+                         cols=cols, Yq=Yq, Ys=Ys)
+        Y2 = fsd.mx_lora_up(Qx, Sx, Qw, Sw, Qt, St, Qb, Sb, bias=bias, residual=res)
+    assert torch.equal(Y1.view(torch.int16), Y2.view(torch.int16)), "bf16 output changed"
+    Yq2, Ys2 = fsd.mx_quantize(Y2[:, q0:q1])
+    assert torch.equal(Yq, Yq2), "codes differ from the unfused route"
+    assert torch.equal(Ys, Ys2), "scales differ from the unfused route"
+
+
+@pytest.mark.parametrize("M,C,D", [(1, 24, 128), (100, 24, 3072), (129, 24, 256),
+                                   (300, 24, 640), (1000, 16, 384)])
+def test_embed_mx_one_pass(gpu, M, C, D):
+    """Embed writing X and its MXFP8 form: X is token_embed's output bit for bit
+    and the codes and scales (padding rows up to the 256-row multiple included)
+    are the quantizer's bytes of X."""
+    from few_step_diffusion_amd import inputs
+    say(f"embed->mx M={M} C={C} D={D}")
+    rng = np.random.default_rng(M + C + D)
+    z = torch.from_numpy(rng.standard_normal((M, C)).astype(np.float32)).to(gpu)
+    E = torch.from_numpy(rng.standard_normal((D, C)) / np.sqrt(C)).to(torch.bfloat16).to(gpu)
+    X = _garbage(torch.empty((M, D), dtype=torch.bfloat16, device=gpu).view(torch.uint8)
+                 ).view(torch.bfloat16)
+    Xq = _garbage(torch.empty((M, D), dtype=torch.uint8, device=gpu))
+    Xs = _garbage(torch.empty(fsd.mx_scale_bytes(M, D), dtype=torch.uint8, device=gpu))
+    fsd.token_embed_mx(z, E, out=X, Xq=Xq, Xs=Xs)
+    X2 = fsd.token_embed(z, E)
+    assert torch.equal(X.view(torch.int16), X2.view(torch.int16)), "bf16 output changed"
+    Xq2, Xs2 = fsd.mx_quantize(X2)
+    assert torch.equal(Xq, Xq2), "codes differ from the unfused route"
+    assert torch.equal(Xs, Xs2), "scales differ from the unfused route"
+
+
+def test_mx_standin_one_pass_equals_multi_pass(gpu):
+    """The stand-in refine through the one-pass route (every activation quantized by
+    its producer) and through separate quantizer passes: identical latents."""
+    from few_step_diffusion_amd import inputs
+    from few_step_diffusion_amd.refine import StandinRefiner
+    M, D, F = 4096 + 37, 256, 512
+    say(f"mx one-pass vs multi-pass refine M={M} D={D} F={F}")
+    u, eps = inputs.latent(4, tokens=M)
+    u, eps = u.to(gpu), eps.to(gpu)
+    z1 = StandinRefiner(M, device=gpu, D=D, F=F, mx=True).refine(u, eps).clone()
+    z2 = StandinRefiner(M, device=gpu, D=D, F=F, mx=True, mx_onepass=False).refine(u, eps)
+    assert torch.equal(z1, z2)
+
+
 # ------------------------------------------------- full-size MXFP8 linear
 def test_mx_linear_2k_qkv_sampled_rows(gpu):
     """The 2K QKV linear (M = 532,800, K = 3072, N = 9216, rank 576) on the MXFP8
@@ -324,9 +440,16 @@ def test_mx_standin_refine_2k_sampled(gpu):
     say(f"mx stand-in refine {wl.name}: M={M}")
     model = StandinRefiner(M, device=gpu, D=D, F=F, mx=True)
     u, eps = inputs.latent(4)
-    z = model.refine(u.to(gpu), eps.to(gpu)).cpu().numpy()
+    zt = model.refine(u.to(gpu), eps.to(gpu)).clone()
     del model
     torch.cuda.empty_cache()
+    # the one-pass route (the default) writes the bytes of the quantizer passes
+    model = StandinRefiner(M, device=gpu, D=D, F=F, mx=True, mx_onepass=False)
+    assert torch.equal(zt, model.refine(u.to(gpu), eps.to(gpu))), "one-pass != multi-pass at 2K"
+    del model
+    torch.cuda.empty_cache()
+    z = zt.cpu().numpy()
+    del zt
     assert np.all(np.isfinite(z))
     sel = inputs.sample_rows(M, 24, seed=4)
     layers = _oracle_standin_layers(D, F)
