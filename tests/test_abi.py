@@ -344,3 +344,64 @@ def test_python_binding_rejects_cpu_tensors():
     import torch
     with pytest.raises(ValueError):
         fsd.renoise(torch.zeros(8), torch.zeros(8), 0.5)
+
+
+def test_one_pass_mx_validation(L):
+    f = ctypes.c_float
+
+    def dmx(**kw):
+        args = dict(Xq=a(1), ldxq=1024, Xs=a(2), Aq=a(3), As=a(4), s=1.0, Tq=a(5), ldtq=640,
+                    Ts=a(6), M=300, K=1024, r=576)
+        args.update(kw)
+        return L.fsd_mx_lora_down_mx(args["Xq"], args["ldxq"], args["Xs"], args["Aq"],
+                                     args["As"], f(args["s"]), args["Tq"], args["ldtq"],
+                                     args["Ts"], args["M"], args["K"], args["r"], None)
+    assert dmx(M=0) == OK
+    assert dmx(r=72) == EINVAL                           # T's blocks: r % 32
+    assert dmx(ldtq=576) == EINVAL                       # ldtq < rp (640)
+    assert dmx(ldtq=648) == EINVAL                       # ldtq % 16
+    assert dmx(Ts=None) == EINVAL
+    assert dmx(Ts=P(BASE + 6 * 0x10000000 + 2)) == EALIGN
+    assert dmx(s=math.inf) == EINVAL
+    assert dmx(Tq=P(BASE + 0x10000000 + 64)) == EINVAL   # Tq overlaps Xq
+    assert dmx(Ts=P(BASE + 5 * 0x10000000 + 64)) == EINVAL   # Ts overlaps Tq
+
+    def uq(**kw):
+        args = dict(Xq=a(1), ldxq=1024, Xs=a(2), Wq=a(3), Ws=a(4), Tq=a(5), ldtq=640, Ts=a(6),
+                    Bq=a(7), Bs=a(8), bias=None, res=None, ldr=0, Y=a(9), ldy=1024, M=300,
+                    N=1024, K=1024, r=576, q0=0, q1=1024, Yq=a(10), ldyq=1024, Ys=a(11))
+        args.update(kw)
+        return L.fsd_mx_lora_up_q(*(args[k] for k in (
+            "Xq", "ldxq", "Xs", "Wq", "Ws", "Tq", "ldtq", "Ts", "Bq", "Bs", "bias", "res", "ldr",
+            "Y", "ldy", "M", "N", "K", "r", "q0", "q1", "Yq", "ldyq", "Ys")), None)
+    assert uq(M=0) == OK
+    assert uq(M=0, res=a(9), ldr=1024) == OK             # in-place residual is legal
+    assert uq(q0=16) == EINVAL                           # q0 % 32
+    assert uq(q1=1000) == EINVAL                         # q1 % 32
+    assert uq(q0=512, q1=512) == EINVAL                  # empty range
+    assert uq(q1=1056) == EINVAL                         # past N
+    assert uq(q0=-32) == EINVAL
+    assert uq(q0=32, q1=352, ldyq=320) == EINVAL         # ldyq < 384 (320 padded to 128)
+    assert uq(q0=32, q1=352, ldyq=384, M=0) == OK
+    assert uq(Y=None) == EINVAL
+    assert uq(Ys=None) == EINVAL
+    assert uq(Yq=P(BASE + 10 * 0x10000000 + 8)) == EALIGN
+    assert uq(Yq=P(BASE + 9 * 0x10000000 + 4096)) == EINVAL    # Yq overlaps Y
+    assert uq(Ys=P(BASE + 10 * 0x10000000 + 4096)) == EINVAL   # Ys overlaps Yq
+    assert uq(Ys=P(BASE + 7 * 0x10000000 + 64)) == EINVAL      # Ys overlaps Bq
+    assert uq(res=a(12), ldr=1024, Yq=P(BASE + 12 * 0x10000000 + 64)) == EINVAL  # Yq over res
+
+    def emx(**kw):
+        args = dict(z=a(1), E=a(2), X=a(3), ldx=3072, M=100, C=24, D=3072, Xq=a(4), ldxq=3072,
+                    Xs=a(5))
+        args.update(kw)
+        return L.fsd_token_embed_mx(*(args[k] for k in (
+            "z", "E", "X", "ldx", "M", "C", "D", "Xq", "ldxq", "Xs")), None)
+    assert emx(M=0) == OK
+    assert emx(D=3008, ldx=3008, ldxq=3008) == EUNSUP    # D % 128
+    assert emx(C=33) == EINVAL
+    assert emx(ldxq=3056) == EINVAL                      # ldxq < D
+    assert emx(Xs=None) == EINVAL
+    assert emx(Xq=P(BASE + 4 * 0x10000000 + 4)) == EALIGN
+    assert emx(Xq=P(BASE + 3 * 0x10000000 + 4096)) == EINVAL   # Xq overlaps X
+    assert emx(Xs=P(BASE + 0x10000000 + 16)) == EINVAL         # Xs overlaps z
