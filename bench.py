@@ -23,9 +23,10 @@ Prints ONE JSON line on stdout (everything else goes to stderr):
   mxfp8      the step with the four linears as MXFP8 GEMMs (quantization in the
              step time), the fused SwiGLU->MXFP8 gate/up GEMM against the
              5000 TFLOP/s fp8 peak
-  lora_linear_configs  the whole LoRA-fused linear at the 768P shape and on one
-             4K chunk (gate/up with SwiGLU chained into down with the
-             residual): median / min / max of 20 calls, and the median of 3
+  lora_linear_configs  the whole LoRA-fused linear at the 768P shape, on one
+             4K chunk and over the whole 4K grid chunk by chunk (gate/up with
+             SwiGLU chained into down with the residual): median / min / max
+             of 20 calls, and the median of 3
   attention_step  the same refine with dense attention between QKV and O
              (all 532,800 tokens as one sequence, 24 heads of 128): step time
              and the attention kernel against 2500 TFLOP/s
@@ -403,9 +404,10 @@ def lora_linear_shapes(per_kernel, model, steps):
 
 def lora_linear_configs(torch, fsd, reps=20, warm=5):
     """The whole LoRA-fused linear (phase A + phase B in one library call) at
-    the 768P shape (149,184 tokens, K = N = 3072) and on one chunk of the 4K
-    grid (299,700 tokens): gate/up (K = 3072, N = 16384, SwiGLU to 8192)
-    chained into down (K = 8192, N = 3072) with the gate/up input as residual.
+    the 768P shape (149,184 tokens, K = N = 3072), on one chunk of the 4K grid
+    (299,700 tokens) and over the whole 4K grid (its four chunks in turn):
+    gate/up (K = 3072, N = 16384, SwiGLU to 8192) chained into down (K = 8192,
+    N = 3072) with the gate/up input as residual.
     Seeded inputs of the workloads' shapes and distributions (activations drawn
     on the device); each call is timed with HIP events on its stream; median,
     min and max over `reps` calls after `warm` warm-up calls, plus the median
@@ -460,9 +462,11 @@ def lora_linear_configs(torch, fsd, reps=20, warm=5):
     (_, K1, N1, _), (_, K2, N2, _) = wl.linears
     Wg, Ag, Bg = weights(3, K1, N1, 1)
     Wd, Ad, Bd = weights(3, K2, N2, 2)
-    X = inputs.activations(3, M, K1, device=dev)
+    Xall = inputs.activations(3, wl.tokens, K1, device=dev)
+    X = Xall[:M]
     H = torch.empty((M, N1 // 2), dtype=torch.bfloat16, device=dev)
-    Y = torch.empty((M, N2), dtype=torch.bfloat16, device=dev)
+    Yall = torch.empty((wl.tokens, N2), dtype=torch.bfloat16, device=dev)
+    Y = Yall[:M]
     ws = torch.empty(fsd.workspace_bytes(M, Ag.shape[0]), dtype=torch.uint8, device=dev)
     tg = timed(lambda: fsd.lora_linear(X, Wg, Ag, Bg, epilogue="swiglu", out=H, workspace=ws))
     td = timed(lambda: fsd.lora_linear(H, Wd, Ad, Bd, residual=X, out=Y, workspace=ws))
@@ -470,9 +474,27 @@ def lora_linear_configs(torch, fsd, reps=20, warm=5):
     out["4k_chunk_down"] = entry(td, M, K2, N2, Ad.shape[0])
     log(f"4K chunk: gate/up {out['4k_chunk_gate_up']['ms_median']:.3f} ms, "
         f"down {out['4k_chunk_down']['ms_median']:.3f} ms")
+
+    def whole_grid():
+        for c in range(wl.chunks):
+            rows = slice(c * M, (c + 1) * M)
+            fsd.lora_linear(Xall[rows], Wg, Ag, Bg, epilogue="swiglu", out=H, workspace=ws)
+            fsd.lora_linear(H, Wd, Ad, Bd, residual=Xall[rows], out=Yall[rows], workspace=ws)
+    tw = timed(whole_grid)
+    r = Ag.shape[0]
+    fl = sum(2.0 * wl.tokens * (K * N + K * r + r * N) for K, N in ((K1, N1), (K2, N2)))
+    med = statistics.median(tw)
+    out["4k_whole"] = {"tokens": wl.tokens, "chunks": wl.chunks, "flops_per_call": fl,
+                       "ms_median": round(med, 3), "ms_min": round(min(tw), 3),
+                       "ms_max": round(max(tw), 3),
+                       "tflops": round(fl / (med * 1e-3) / 1e12, 1),
+                       "frac_peak": round(fl / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                       "note": "all four chunks: gate/up with SwiGLU, then down with the "
+                               "gate/up input as residual, per chunk"}
+    log(f"4K whole grid ({wl.chunks} chunks): {med:.3f} ms, {out['4k_whole']['tflops']} TFLOP/s")
     out["note"] = ("fsd_lora_linear calls (phase A + phase B); flops 2·M·(K·N + K·r + r·N) with "
                    "r = 576; base_equiv_frac_peak counts 2·M·K·N only")
-    del Wg, Ag, Bg, Wd, Ad, Bd, X, H, Y, ws
+    del Wg, Ag, Bg, Wd, Ad, Bd, Xall, X, H, Yall, Y, ws
     return out
 
 

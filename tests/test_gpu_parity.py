@@ -1,7 +1,7 @@
 """GPU parity: the HIP path through the C ABI against the fp64 oracle.
 
 Small cases compare every output element; full-size cases (768P, 2K, the
-first and last 4K chunks, the 2K three-step stand-in) compare sampled rows
+whole 4K grid chunk by chunk, the 2K three-step stand-in) compare sampled rows
 exactly and, for the linear layers without SwiGLU, EVERY row through 16 random
 column projections (Freivalds' identity on the output columns, tests/checks.py:
 Y_i·U against X_i·G + c with the oracle's adjoint G = W0ᵀU + s·Aᵀ(BᵀU)), so a
@@ -511,58 +511,45 @@ def test_full_2k_o_strided_in_place(gpu):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("chunk", [0, 3])
-def test_full_4k_down_with_residual(gpu, chunk):
-    """The 4K down linear (K = 8192 -> 3072) with the residual added, as the 4K
-    chunk runs it, on seeded SwiGLU-width inputs: every row of the first chunk
-    and of the last (rows 899,100-1,198,799)."""
-    wl = inputs.WORKLOADS[3]
-    Mc = wl.tokens // wl.chunks
-    (_, K1, _, _), (_, K2, N2, _) = wl.linears
-    say(f"{wl.name}: down with residual, chunk {chunk} (rows {chunk * Mc}-{(chunk + 1) * Mc - 1})")
-    H = inputs.normal((Mc, K2), 0.5, seed=3060 + chunk, device=gpu, dtype=torch.bfloat16)
-    Xall = inputs.activations(3, wl.tokens, K1, device=gpu)
-    R = Xall[chunk * Mc:(chunk + 1) * Mc].clone()
-    del Xall
-    W2 = inputs.base_weight(3, K2, N2, layer=2)
-    A2, B2, A2f, B2f = merged(3, K2, N2, gpu, layer=2)
-    Y = fsd.lora_linear(H, W2.to(gpu), A2, B2, residual=R)
-    torch.cuda.synchronize()
-    sel = torch.from_numpy(inputs.sample_rows(Mc, 160, seed=30 + chunk)).to(gpu)
-    ref = oracle.lora_linear_rows(f32(H[sel]), f32(W2), A2f, B2f) + f32(R[sel])
-    assert_gemm(f32(Y[sel]), ref, f"4K down chunk {chunk} sampled rows")
-    check_all_rows(H, Y, f32(W2), A2f, B2f, residual=R, seed=31 + chunk,
-                   what=f"4K down chunk {chunk}")
-    del H, R, Y
-    torch.cuda.empty_cache()
-
-
-@pytest.mark.parametrize("chunk", [0, 3])
-def test_full_4k_chunk_gate_up_swiglu_then_down(gpu, chunk):
-    """Gate/up with SwiGLU chained into down with the residual, on the first
-    and the last 4K chunk, sampled rows; the oracle's own H feeds its down."""
+def test_full_4k_whole_grid(gpu):
+    """The whole 4K grid (1,198,800 tokens) as its four 299,700-token chunks run
+    it, one after another through shared buffers and one workspace: gate/up with
+    SwiGLU (K = 3072 -> 2 x 8192), then down (8192 -> 3072) with the gate/up
+    input added as the residual.  Per chunk: 40 sampled rows of H and of Y
+    against the oracle's chain (its own H feeding its down), and every row of Y
+    through 16 column projections given the GPU's H."""
     wl = inputs.WORKLOADS[3]
     Mc = wl.tokens // wl.chunks
     (_, K1, N1, _), (_, K2, N2, _) = wl.linears
-    say(f"{wl.name}: chunk {chunk} M={Mc} gate/up {K1}->{N1} SwiGLU, down {K2}->{N2} + residual")
+    say(f"{wl.name}: {wl.chunks} chunks of {Mc}, gate/up {K1}->{N1} SwiGLU, "
+        f"down {K2}->{N2} + residual")
     Xall = inputs.activations(3, wl.tokens, K1, device=gpu)
-    X = Xall[chunk * Mc:(chunk + 1) * Mc].clone()
-    del Xall
     W1 = inputs.base_weight(3, K1, N1, layer=1)
     W2 = inputs.base_weight(3, K2, N2, layer=2)
+    W1d, W2d = W1.to(gpu), W2.to(gpu)
+    W1f, W2f = f32(W1), f32(W2)
     A1, B1, A1f, B1f = merged(3, K1, N1, gpu, layer=1)
     A2, B2, A2f, B2f = merged(3, K2, N2, gpu, layer=2)
-    H = fsd.lora_linear(X, W1.to(gpu), A1, B1, epilogue="swiglu")
-    Y = fsd.lora_linear(H, W2.to(gpu), A2, B2, residual=X)
-    torch.cuda.synchronize()
-    sel = inputs.sample_rows(Mc, 160, seed=3 + chunk)
-    seli = torch.from_numpy(sel).to(gpu)
-    Href = oracle.lora_linear_rows(f32(X[seli]), f32(W1), A1f, B1f, swiglu=True)
-    assert_gemm(f32(H[seli]), Href, f"4K chunk {chunk} gate/up SwiGLU sampled rows")
-    # the chain from X in fp64: the oracle's H (not the GPU's) feeds its down projection
-    Yref = oracle.lora_linear_drows(Href, f32(W2), A2f, B2f) + f32(X[seli])
-    assert_gemm(f32(Y[seli]), Yref, f"4K chunk {chunk} down (chained, residual) sampled rows")
-    del X, H, Y
+    H = torch.empty((Mc, N1 // 2), dtype=torch.bfloat16, device=gpu)
+    Y = torch.empty((wl.tokens, N2), dtype=torch.bfloat16, device=gpu)
+    ws = torch.empty(fsd.workspace_bytes(Mc, A1.shape[0]), dtype=torch.uint8, device=gpu)
+    for c in range(wl.chunks):
+        rows = slice(c * Mc, (c + 1) * Mc)
+        X, Yc = Xall[rows], Y[rows]
+        say(f"  chunk {c}: rows {c * Mc}-{(c + 1) * Mc - 1}")
+        fsd.lora_linear(X, W1d, A1, B1, epilogue="swiglu", out=H, workspace=ws)
+        fsd.lora_linear(H, W2d, A2, B2, residual=X, out=Yc, workspace=ws)
+        torch.cuda.synchronize()
+        sel = inputs.sample_rows(Mc, 40, seed=3 + c)
+        seli = torch.from_numpy(sel).to(gpu)
+        Href = oracle.lora_linear_rows(f32(X[seli]), W1f, A1f, B1f, swiglu=True)
+        assert_gemm(f32(H[seli]), Href, f"4K chunk {c} gate/up SwiGLU sampled rows")
+        # the chain from X in fp64: the oracle's H (not the GPU's) feeds its down projection
+        Yref = oracle.lora_linear_drows(Href, W2f, A2f, B2f) + f32(X[seli])
+        assert_gemm(f32(Yc[seli]), Yref, f"4K chunk {c} down (chained, residual) sampled rows")
+        check_all_rows(H, Yc, W2f, A2f, B2f, residual=X, seed=31 + c,
+                       what=f"4K chunk {c} down")
+    del Xall, H, Y, ws
     torch.cuda.empty_cache()
 
 
