@@ -349,25 +349,32 @@ def mx_step(torch, M, u, eps, flops, bf16_ms, args):
                "mean_us": round(statistics.mean(ts) * 1e3, 1),
                "median_us": round(statistics.median(ts) * 1e3, 1)}
         if name in flops:
-            ent["tflops"] = round(flops[name] / 3 / (statistics.mean(ts) * 1e-3) / 1e12, 1)
+            per_launch = flops[name] / (len(ts) / args.steps)
+            ent["flops_per_launch"] = per_launch
+            ent["tflops"] = round(per_launch / (statistics.mean(ts) * 1e-3) / 1e12, 1)
             ent["frac_fp8_peak"] = round(ent["tflops"] / PEAK_FP8_TFLOPS, 4)
         kernels[name] = ent
     lin = [k for k in per_kernel if k.split(".")[0] in StandinRefiner.LAYER_NAMES]
     lin_ms = sum(statistics.mean(per_kernel[k]) * len(per_kernel[k]) / args.steps for k in lin)
-    lin_flops = sum(v for k, v in flops.items() if k.endswith(".down") or k.endswith(".up"))
-    dom = kernels["gate_up.up"]
+    lin_flops = sum(v for k, v in flops.items() if k.split(".")[0] in StandinRefiner.LAYER_NAMES)
+    chunked = "gate_up.pair" in kernels          # fsd_mx_lora_linear's pair launches
+    dom = kernels["gate_up.pair" if chunked else "gate_up.up"]
     log(f"MXFP8 step {ms:.2f} ms (bf16 {bf16_ms:.2f} ms)")
     del model
     return {"ms_per_step": round(ms, 3), "tflops": round(total / (ms * 1e-3) / 1e12, 1),
             "speedup_vs_bf16": round(bf16_ms / ms, 3),
             "linears": {"ms_per_step": round(lin_ms, 3),
                         "tflops": round(lin_flops / (lin_ms * 1e-3) / 1e12, 1),
-                        "note": "phase A (T leaves as MXFP8) + phase B (its output's MXFP8 "
-                                "for the next linear in the same pass)"},
-            "dominant": {"kernel": "gate/up phase B, MXFP8 operands, SwiGLU -> MXFP8 epilogue",
+                        "note": "phase A writing T as MXFP8, then phase B writing its output "
+                                "and the MXFP8 the next linear reads, in the same pass"},
+            "dominant": {"kernel": "gate/up phase B, MXFP8 operands, SwiGLU -> MXFP8 epilogue"
+                                   + (" (pair launch with phase A of the next chunk)"
+                                      if chunked else ""),
                          "bound": "mfma", "achieved": dom["tflops"], "peak": PEAK_FP8_TFLOPS,
                          "unit": "TFLOP/s", "frac": dom["frac_fp8_peak"],
-                         "traffic": measured_traffic("gemm_kernel<2, 4, true, true, true>")},
+                         "flops_per_launch": dom["flops_per_launch"],
+                         "traffic": measured_traffic("gemm_pair_mx_kernel<true, true>" if chunked
+                                                     else "gemm_kernel<2, 4, true, true, true>")},
             "kernels": kernels,
             "note": "E4M3 elements with E8M0 scales per 32 along K; weights quantized once "
                     "outside the step; flops counted as the bf16 step's (rank 576, K unpadded)"}

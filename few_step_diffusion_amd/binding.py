@@ -16,7 +16,8 @@ import torch
 __all__ = [
     "FsdError", "library_path", "lib", "abi_version", "lora_merge", "workspace_bytes",
     "lora_down", "lora_up", "lora_linear", "lora_linear_plan", "lora_linear_noalloc", "renoise", "euler_step", "token_embed",
-    "token_head", "token_head_euler", "token_embed_mx", "mx_lora_down_mx", "mx_lora_up_q",
+    "token_head", "token_head_euler", "token_embed_mx", "mx_lora_down_mx", "mx_lora_up_q", "mx_lora_linear", "mx_lora_linear_plan",
+    "mx_workspace_bytes",
     "mx_quantize", "mx_padded_k", "mx_scale_bytes",
     "mx_scale_offsets", "mx_pack_scales", "mx_unpack_scales", "mx_lora_down", "mx_lora_up",
     "mx_lora_up_swiglu_mx", "attention_workspace_bytes", "attention", "StepGraph",
@@ -100,6 +101,19 @@ _SIGS = {
                           _c_void_p], _int),
     "fsd_token_embed_mx": ([_c_void_p, _c_void_p, _c_void_p, _i64, _i64, _i64, _i64, _c_void_p,
                             _i64, _c_void_p, _c_void_p], _int),
+    "fsd_mx_lora_linear_workspace_bytes": ([_i64, _i64], ctypes.c_size_t),
+    "fsd_mx_lora_linear_plan": ([_i64, _i64, ctypes.c_size_t, ctypes.POINTER(_i64),
+                                 ctypes.POINTER(_i64)], _int),
+    "fsd_mx_lora_linear": ([_c_void_p, _i64, _c_void_p, _c_void_p, _c_void_p, _f32, _c_void_p,
+                            _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64,
+                            _c_void_p, _i64, _i64, _i64, _i64, _i64, _int, _i64, _i64,
+                            _c_void_p, _i64, _c_void_p, _c_void_p, ctypes.c_size_t, _c_void_p],
+                           _int),
+    "fsd_mx_lora_linear_launch": ([_c_void_p, _i64, _c_void_p, _c_void_p, _c_void_p, _f32,
+                                   _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                   _c_void_p, _i64, _c_void_p, _i64, _i64, _i64, _i64, _i64,
+                                   _int, _i64, _i64, _c_void_p, _i64, _c_void_p, _c_void_p,
+                                   ctypes.c_size_t, _i64, _c_void_p], _int),
     "fsd_attention_workspace_bytes": ([_i64, _i64, _i64], ctypes.c_size_t),
     "fsd_attention": ([_c_void_p, _c_void_p, _c_void_p, _i64, _c_void_p, _i64, _i64, _i64, _i64,
                        _f32, _c_void_p, ctypes.c_size_t, _c_void_p], _int),
@@ -705,6 +719,96 @@ def mx_lora_up_q(Xq, Xs, W0q, W0s, Tq=None, Ts=None, Bq=None, Bs=None, bias=None
                                 M, N, Kp, rp, q0, q1, _ptr(Yq), _ld(Yq), _ptr(Ys), _stream(Xq))
     _check("fsd_mx_lora_up_q", st)
     return out, Yq, Ys
+
+
+def mx_workspace_bytes(M: int, r: int) -> int:
+    """Preferred workspace of mx_lora_linear: two chunks of MXFP8 T."""
+    return int(lib().fsd_mx_lora_linear_workspace_bytes(M, r))
+
+
+def mx_lora_linear_plan(M: int, r: int, ws_bytes: int):
+    """(launches, chunk rows) of mx_lora_linear for M rows at rank r."""
+    n, R = _i64(0), _i64(0)
+    st = lib().fsd_mx_lora_linear_plan(M, r, ws_bytes, ctypes.byref(n), ctypes.byref(R))
+    _check("fsd_mx_lora_linear_plan", st)
+    return n.value, R.value
+
+
+def mx_lora_linear(Xq, Xs, Aq, As, W0q, W0s, Bq, Bs, scale=1.0, bias=None, residual=None,
+                   out=None, epilogue=EPI_NONE, cols=None, Yq=None, Ys=None, workspace=None,
+                   on_launch=None):
+    """The whole MXFP8 LoRA linear in row chunks (fsd_mx_lora_linear): T = the MXFP8
+    of bf16(scale·X·Aᵀ) per chunk in the workspace, then phase B.
+
+    epilogue "none": returns out (bf16 [M, N]); with Yq/Ys (or cols) also the MXFP8
+    of out[:, q0:q1], returned as (out, Yq, Ys).  epilogue "swiglu": out bf16 [M, N/2],
+    or, with Yq/Ys and out=None, the MXFP8 of H only, returned as (Yq, Ys).
+    on_launch: optional callable(index) run before each launch (launches then go one
+    by one through fsd_mx_lora_linear_launch)."""
+    epilogue = _epi(epilogue)
+    for t, nm in ((Xq, "Xq"), (Aq, "Aq"), (W0q, "W0q"), (Bq, "Bq")):
+        _need(t, nm, torch.uint8)
+    M, Kp = Xq.shape
+    r, N, rp = Aq.shape[0], W0q.shape[0], mx_padded_k(Aq.shape[0])
+    _shape(Aq, "Aq", (r, Kp), contiguous=True, device=Xq.device)
+    _shape(W0q, "W0q", (N, Kp), contiguous=True, device=Xq.device)
+    _shape(Bq, "Bq", (N, rp), contiguous=True, device=Xq.device)
+    for S_, nm, rows, k in ((Xs, "Xs", M, Kp), (As, "As", r, Kp), (W0s, "W0s", N, Kp),
+                            (Bs, "Bs", N, rp)):
+        _need_scales(S_, nm, rows, k)
+        if S_.device != Xq.device:
+            raise ValueError(f"{nm} must be on Xq's device")
+    if bias is not None:
+        _need(bias, "bias", torch.float32, dims=1)
+        _shape(bias, "bias", (N,), device=Xq.device)
+    swiglu = epilogue == EPI_SWIGLU
+    nout = N // 2 if swiglu else N
+    quant = Yq is not None or Ys is not None or cols is not None
+    q0, q1 = (0, nout) if cols is None else (int(cols[0]), int(cols[1]))
+    if quant:
+        qkp = mx_padded_k(q1 - q0)
+        if Yq is None:
+            Yq = torch.empty((M, qkp), dtype=torch.uint8, device=Xq.device)
+        if Ys is None:
+            Ys = torch.empty(max(mx_scale_bytes(M, q1 - q0), 4), dtype=torch.uint8,
+                             device=Xq.device)
+        _need(Yq, "Yq", torch.uint8)
+        _shape(Yq, "Yq", (M, qkp), device=Xq.device)
+        _need_scales(Ys, "Ys", M, qkp)
+    if residual is not None:
+        _need(residual, "residual", torch.bfloat16)
+        _shape(residual, "residual", (M, nout), device=Xq.device)
+    if out is None and not (swiglu and quant):
+        out = torch.empty((M, nout), dtype=torch.bfloat16, device=Xq.device)
+    if out is not None:
+        _need(out, "out", torch.bfloat16)
+        _shape(out, "out", (M, nout), device=Xq.device)
+    if workspace is None:
+        workspace = torch.empty(max(mx_workspace_bytes(M, r), 16), dtype=torch.uint8,
+                                device=Xq.device)
+    if workspace.device != Xq.device or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor on Xq's device")
+    args = [_ptr(Xq), _ld(Xq), _ptr(Xs), _ptr(Aq), _ptr(As), float(scale), _ptr(W0q), _ptr(W0s),
+            _ptr(Bq), _ptr(Bs), _ptr(bias),
+            _ptr(residual), _ld(residual) if residual is not None else 0,
+            _ptr(out) if out is not None else None, _ld(out) if out is not None else 0,
+            M, N, Kp, r, epilogue, q0 if quant else 0, q1 if quant else 0,
+            _ptr(Yq) if quant else None, _ld(Yq) if quant else 0, _ptr(Ys) if quant else None,
+            _ptr(workspace), workspace.numel()]
+    if on_launch is None:
+        st = lib().fsd_mx_lora_linear(*args, _stream(Xq))
+        _check("fsd_mx_lora_linear", st)
+    else:
+        n, _ = mx_lora_linear_plan(M, r, workspace.numel()) if M else (0, 0)
+        for i in range(n):
+            on_launch(i)
+            st = lib().fsd_mx_lora_linear_launch(*args, i, _stream(Xq))
+            _check("fsd_mx_lora_linear_launch", st)
+    if swiglu and quant and out is None:
+        return Yq, Ys
+    if quant:
+        return out, Yq, Ys
+    return out
 
 
 # ------------------------------------------------------------ attention

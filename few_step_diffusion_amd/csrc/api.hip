@@ -22,6 +22,10 @@ constexpr int64_t kTileM = 256;            // rows per GEMM tile: the chunk gran
 // last wave of the current chunk's phase-B tiles on 256 CUs.  Two chunks of T
 // at rank 576 take 50.1 MB.
 constexpr int64_t kPairChunkRows = 85 * kTileM;
+// Chunk rows of the MXFP8 linear's schedule.  Its launches run twice as fast as
+// the bf16 ones, but 170 and 255 row tiles measured no better than 85 on the 2K
+// step (203.6 and 204.2 against 203.3 ms).
+constexpr int64_t kMxPairChunkRows = 85 * kTileM;
 constexpr int64_t kMaxOffsetBytes = 0x7fffffffLL;
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -780,6 +784,217 @@ int fsd_mx_lora_up_q(const void* Xq, int64_t ldxq, const void* Xs, const void* W
   p.Ys = (uint8_t*)Ys; p.sYp = round_up(M, kTileM);
   p.q0 = q0; p.q1 = q1;
   return from_hip(fsd::launch_gemm(fsd::GEMM_MX_UP_Q, p, as_stream(stream)));
+}
+
+}  // extern "C"
+
+namespace {
+
+// ---- the chunked MXFP8 LoRA linear -------------------------------------------
+// T of one chunk in the workspace: E4M3 codes [R, rp] then their scales for R
+// rows (rp = r rounded up to 128, R a multiple of 256): rp + rp/32 bytes per row.
+inline int64_t mx_t_row_bytes(int64_t r) {
+  const int64_t rp = round_up(r, 128);
+  return rp + rp / 32;
+}
+
+struct MxPlan {
+  int64_t R, nc, launches;
+};
+
+// Chunks of R rows (a multiple of 256, at most kMxPairChunkRows) through two
+// halves of the workspace: launch 0 is phase A of chunk 0, launch c + 1 phase B
+// of chunk c with phase A of chunk c + 1 (none after the last).  R = 0 when not
+// even two 256-row chunks fit.
+MxPlan make_mx_plan(int64_t M, int64_t r, int64_t ws_bytes) {
+  MxPlan pl{0, 0, 0};
+  if (M <= 0 || r <= 0) return pl;
+  const int64_t fit = ws_bytes / mx_t_row_bytes(r);
+  int64_t R = (fit / 2) / kTileM * kTileM;
+  if (R > kMxPairChunkRows) R = kMxPairChunkRows;
+  if (R > round_up(M, kTileM)) R = round_up(M, kTileM);
+  if (R < kTileM) return pl;
+  pl.R = R;
+  pl.nc = (M + R - 1) / R;
+  pl.launches = pl.nc + 1;
+  return pl;
+}
+
+struct MxLinear {
+  const void* Xq; int64_t ldxq; const void* Xs;
+  const void* Aq; const void* As; float scale;
+  const void* W0q; const void* W0s; const void* Bq; const void* Bs;
+  const float* bias; const void* residual; int64_t ldr;
+  void* Y; int64_t ldy;
+  int64_t M, N, K, r; int epi;
+  int64_t q0, q1; void* Yq; int64_t ldyq; void* Ys;
+};
+
+int validate_mx_linear(const MxLinear& a, const void* ws, int64_t ws_bytes) {
+  const bool swiglu = a.epi == FSD_EPI_SWIGLU;
+  if (a.epi != FSD_EPI_NONE && !swiglu) return FSD_EINVAL;
+  if (a.M < 0 || a.K < 32 || a.K % 32 || a.N < 8 || a.N % 8 || a.r < 32 || a.r % 32 ||
+      !isfinite(a.scale))
+    return FSD_EINVAL;
+  const int64_t M = a.M, N = a.N, Kp = round_up(a.K, 128), rp = round_up(a.r, 128);
+  const int64_t nout = swiglu ? N / 2 : N;
+  if (swiglu) {
+    if (N % 16) return FSD_EINVAL;
+    if ((a.Y != nullptr) == (a.Yq != nullptr) || a.residual) return FSD_EINVAL;
+    if (N % (a.Yq ? 256 : 128)) return FSD_EUNSUPPORTED;
+    if (a.Yq && (a.q0 != 0 || a.q1 != nout)) return FSD_EINVAL;
+  } else {
+    if (!a.Y) return FSD_EINVAL;
+    if (a.Yq && (a.q0 < 0 || a.q0 % 32 || a.q1 % 32 || a.q1 <= a.q0 || a.q1 > N))
+      return FSD_EINVAL;
+  }
+  const int64_t qk = a.Yq ? a.q1 - a.q0 : 0, qkp = round_up(qk, 128);
+  if (a.Y && (a.ldy < nout || a.ldy % 8)) return FSD_EINVAL;
+  if (a.residual && (a.ldr < nout || a.ldr % 8)) return FSD_EINVAL;
+  if (a.Yq && (!a.Ys || a.ldyq < qkp || a.ldyq % 16)) return FSD_EINVAL;
+  if ((a.Y && !aligned16(a.Y)) || (a.residual && !aligned16(a.residual)) ||
+      (a.Yq && (!aligned16(a.Yq) || ((uintptr_t)a.Ys & 3u))))
+    return FSD_EALIGN;
+  if (a.residual && kTileM * a.ldr * 2 > kMaxOffsetBytes) return FSD_EUNSUPPORTED;
+  if (a.Yq && (kTileM * a.ldyq > kMaxOffsetBytes || mx_scale_span(M, qkp) > kMaxOffsetBytes))
+    return FSD_EUNSUPPORTED;
+  // the operands (phase B's T is the workspace: checked as an operand below)
+  int st = validate_mx_operand(a.Xq, a.ldxq, a.Xs, M, Kp, false);
+  if (st == FSD_OK) st = validate_mx_operand(a.Aq, Kp, a.As, a.r, Kp, true);
+  if (st == FSD_OK) st = validate_mx_operand(a.W0q, Kp, a.W0s, N, Kp, true);
+  if (st == FSD_OK) st = validate_mx_operand(a.Bq, rp, a.Bs, N, rp, true);
+  if (st != FSD_OK) return st;
+  if (a.bias && ((uintptr_t)a.bias & 3u)) return FSD_EALIGN;
+  const MxPlan pl = make_mx_plan(M, a.r, ws_bytes);
+  if (M > 0 && (!ws || pl.R == 0)) return FSD_EWORKSPACE;
+  if (ws && !aligned16(ws)) return FSD_EALIGN;
+  // outputs against every input, the workspace and each other
+  const int64_t wsb = 2 * pl.R * mx_t_row_bytes(a.r);
+  const void* in_p[10] = {a.Xq, a.Xs, a.Aq, a.As, a.W0q, a.W0s, a.Bq, a.Bs, a.bias, ws};
+  const int64_t in_b[10] = {span_bytes(M, Kp, a.ldxq, 1), mx_scale_span(M, Kp),
+                            a.r * Kp, mx_scale_span(a.r, Kp), N * Kp, mx_scale_span(N, Kp),
+                            N * rp, mx_scale_span(N, rp), a.bias ? N * 4 : 0, wsb};
+  const void* out_p[3] = {a.Y, a.Yq, a.Ys};
+  const int64_t out_b[3] = {a.Y ? span_bytes(M, nout, a.ldy, 2) : 0,
+                            a.Yq ? span_bytes(M, qkp, a.ldyq, 1) : 0,
+                            a.Yq ? mx_scale_span(M, qkp) : 0};
+  for (int o = 0; o < 3; ++o) {
+    for (int i = 0; i < 10; ++i)
+      if (overlap(out_p[o], out_b[o], in_p[i], in_b[i])) return FSD_EINVAL;
+    for (int o2 = o + 1; o2 < 3; ++o2)
+      if (overlap(out_p[o], out_b[o], out_p[o2], out_b[o2])) return FSD_EINVAL;
+  }
+  if (a.residual) {
+    const int64_t rb = span_bytes(M, nout, a.ldr, 2);
+    const bool same = a.residual == a.Y && a.ldr == a.ldy;
+    if (!same && overlap(a.Y, out_b[0], a.residual, rb)) return FSD_EINVAL;
+    if (overlap(a.Yq, out_b[1], a.residual, rb) || overlap(a.Ys, out_b[2], a.residual, rb) ||
+        overlap(ws, wsb, a.residual, rb))
+      return FSD_EINVAL;
+  }
+  for (int i = 0; i < 9; ++i)
+    if (overlap(ws, wsb, in_p[i], in_b[i])) return FSD_EINVAL;
+  return FSD_OK;
+}
+
+// Launch `index` of the plan (arguments already validated).
+int mx_linear_launch(const MxLinear& a, void* ws, const MxPlan& pl, int64_t index, hipStream_t s) {
+  if (index < 0 || index >= pl.launches) return FSD_EINVAL;
+  const int64_t M = a.M, Mp = round_up(M, kTileM), Kp = round_up(a.K, 128);
+  const int64_t rp = round_up(a.r, 128), R = pl.R;
+  auto rows = [&](int64_t c) { return c < pl.nc ? ((M - c * R) < R ? (M - c * R) : R) : 0; };
+  auto half_q = [&](int64_t c) { return (uint8_t*)ws + (c & 1) * R * mx_t_row_bytes(a.r); };
+  auto half_s = [&](int64_t c) { return half_q(c) + R * rp; };
+  auto chunk_down = [&](int64_t c) {
+    const int64_t mc = rows(c), m = mc > 0 ? c * R : 0;
+    fsd::GemmParams p;
+    memset(&p, 0, sizeof(p));
+    p.A0 = (const uint8_t*)a.Xq + m * a.ldxq; p.lda0 = a.ldxq;
+    p.sA0 = (const uint8_t*)a.Xs; p.sa_g0 = m / 64; p.sMp = Mp;
+    p.B0 = a.Aq; p.ldb0 = Kp; p.sB0 = (const uint8_t*)a.As; p.sNp = round_up(a.r, kTileM);
+    p.M = mc; p.N = a.r; p.K0 = Kp; p.K1 = 0;
+    p.alpha = a.scale;
+    p.Yq = half_q(c); p.ldyq = rp; p.Ys = half_s(c); p.sYp = R;
+    p.q0 = 0; p.q1 = a.r;
+    return p;
+  };
+  auto chunk_up = [&](int64_t c) {
+    const int64_t mc = rows(c), m = c * R;
+    fsd::GemmParams p = mx_up_params((const uint8_t*)a.Xq + m * a.ldxq, a.ldxq, a.Xs, a.W0q,
+                                     a.W0s, half_q(c), rp, half_s(c), a.Bq, a.Bs, a.bias, mc,
+                                     a.N, a.K, a.r);
+    p.sMp = Mp; p.sa_g0 = m / 64; p.sMp1 = R;
+    if (a.residual) { p.res = (const bf16_t*)a.residual + m * a.ldr; p.ldr = a.ldr; }
+    if (a.Y) { p.Y = (bf16_t*)a.Y + m * a.ldy; p.ldy = a.ldy; }
+    if (a.Yq) {
+      p.Yq = (uint8_t*)a.Yq + m * a.ldyq; p.ldyq = a.ldyq;
+      p.Ys = (uint8_t*)a.Ys; p.sYp = Mp; p.sy_g0 = m / 64;
+      p.q0 = a.q0; p.q1 = a.q1;
+    }
+    return p;
+  };
+  if (index == 0) return from_hip(fsd::launch_gemm(fsd::GEMM_MX_DOWN_Q, chunk_down(0), s));
+  const int64_t c = index - 1;
+  return from_hip(fsd::launch_gemm_pair_mx(a.epi == FSD_EPI_SWIGLU, a.Yq != nullptr,
+                                           chunk_up(c), chunk_down(c + 1), s));
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fsd_mx_lora_linear_workspace_bytes(int64_t M, int64_t r) {
+  if (M <= 0 || r <= 0) return 0;
+  const int64_t rows =
+      round_up(M, kTileM) < kMxPairChunkRows ? round_up(M, kTileM) : kMxPairChunkRows;
+  return (size_t)(2 * rows * mx_t_row_bytes(r));
+}
+
+int fsd_mx_lora_linear_plan(int64_t M, int64_t r, size_t workspace_bytes, int64_t* launches,
+                            int64_t* chunk_rows) {
+  if (!launches || !chunk_rows) return FSD_EINVAL;
+  if (M < 0 || r < 32 || r % 32 || workspace_bytes > (size_t)INT64_MAX) return FSD_EINVAL;
+  const MxPlan pl = make_mx_plan(M, r, (int64_t)workspace_bytes);
+  if (M > 0 && pl.R == 0) return FSD_EWORKSPACE;
+  *launches = pl.launches;
+  *chunk_rows = pl.R;
+  return FSD_OK;
+}
+
+int fsd_mx_lora_linear_launch(const void* Xq, int64_t ldxq, const void* Xs, const void* Aq,
+                              const void* As, float scale, const void* W0q, const void* W0s,
+                              const void* Bq, const void* Bs, const float* bias,
+                              const void* residual, int64_t ldr, void* Y, int64_t ldy, int64_t M,
+                              int64_t N, int64_t K, int64_t r, int epilogue, int64_t q0,
+                              int64_t q1, void* Yq, int64_t ldyq, void* Ys, void* workspace,
+                              size_t workspace_bytes, int64_t index, void* stream) {
+  if (workspace_bytes > (size_t)INT64_MAX) return FSD_EINVAL;
+  const MxLinear a{Xq, ldxq, Xs, Aq, As, scale, W0q, W0s, Bq, Bs, bias, residual, ldr, Y, ldy,
+                   M, N, K, r, epilogue, q0, q1, Yq, ldyq, Ys};
+  const int st = validate_mx_linear(a, workspace, (int64_t)workspace_bytes);
+  if (st != FSD_OK) return st;
+  const MxPlan pl = make_mx_plan(M, r, (int64_t)workspace_bytes);
+  if (M == 0) return index == 0 ? FSD_OK : FSD_EINVAL;
+  return mx_linear_launch(a, workspace, pl, index, as_stream(stream));
+}
+
+int fsd_mx_lora_linear(const void* Xq, int64_t ldxq, const void* Xs, const void* Aq,
+                       const void* As, float scale, const void* W0q, const void* W0s,
+                       const void* Bq, const void* Bs, const float* bias, const void* residual,
+                       int64_t ldr, void* Y, int64_t ldy, int64_t M, int64_t N, int64_t K,
+                       int64_t r, int epilogue, int64_t q0, int64_t q1, void* Yq, int64_t ldyq,
+                       void* Ys, void* workspace, size_t workspace_bytes, void* stream) {
+  if (workspace_bytes > (size_t)INT64_MAX) return FSD_EINVAL;
+  const MxLinear a{Xq, ldxq, Xs, Aq, As, scale, W0q, W0s, Bq, Bs, bias, residual, ldr, Y, ldy,
+                   M, N, K, r, epilogue, q0, q1, Yq, ldyq, Ys};
+  const int st = validate_mx_linear(a, workspace, (int64_t)workspace_bytes);
+  if (st != FSD_OK) return st;
+  const MxPlan pl = make_mx_plan(M, r, (int64_t)workspace_bytes);
+  for (int64_t i = 0; i < pl.launches; ++i) {
+    const int e = mx_linear_launch(a, workspace, pl, i, as_stream(stream));
+    if (e != FSD_OK) return e;
+  }
+  return FSD_OK;
 }
 
 int fsd_graph_begin(void* stream) {

@@ -38,6 +38,10 @@ struct GemmParams {
   uint8_t* Yq; int64_t ldyq;
   uint8_t* Ys; int64_t sYp;
   int64_t q0, q1;
+  // MXFP8 operands of one row chunk inside larger scale arrays: A0's rows start
+  // at 64-row group sa_g0 of sA0 (sMp rows), the output's at group sy_g0 of Ys
+  // (sYp rows); sA1 holds sMp1 rows (0: sMp)
+  int64_t sa_g0, sy_g0, sMp1;
 };
 
 enum GemmKind {
@@ -57,6 +61,11 @@ hipError_t launch_gemm(GemmKind kind, const GemmParams& p, hipStream_t s);
 // of the next (pa: GEMM_DOWN) in one launch; either may have M == 0.
 hipError_t launch_gemm_pair(bool swiglu, const GemmParams& pb, const GemmParams& pa,
                             hipStream_t s);
+// The same on MXFP8 operands: phase B of one chunk (pb: GEMM_MX_UP, _UP_Q,
+// _UP_SWIGLU or _UP_SWIGLU_MX by swiglu / qout) and phase A of the next, its T
+// leaving as MXFP8 (pa: GEMM_MX_DOWN_Q).
+hipError_t launch_gemm_pair_mx(bool swiglu, bool qout, const GemmParams& pb,
+                               const GemmParams& pa, hipStream_t s);
 
 hipError_t launch_renoise(const float* u, const float* eps, float sigma, float* z,
                           int64_t n, hipStream_t s);

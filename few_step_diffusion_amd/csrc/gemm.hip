@@ -380,8 +380,9 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const int wg, cha
       MX ? make_rsrc(p.sA0, (K0 / 128) * p.sMp * 4) : rA0;
   const __amdgpu_buffer_rsrc_t rsB0 =
       MX ? make_rsrc(p.sB0, (K0 / 128) * p.sNp * 4) : rB0;
+  const int64_t sMp1 = p.sMp1 ? p.sMp1 : p.sMp;
   const __amdgpu_buffer_rsrc_t rsA1 =
-      (MX && has1) ? make_rsrc(p.sA1, (K1 / 128) * p.sMp * 4) : rsA0;
+      (MX && has1) ? make_rsrc(p.sA1, (K1 / 128) * sMp1 * 4) : rsA0;
   const __amdgpu_buffer_rsrc_t rsB1 =
       (MX && has1) ? make_rsrc(p.sB1, (K1 / 128) * p.sNp * 4) : rsB0;
   const int64_t ga = (m0 + wm * WM * 32) >> 6;          // A: first 64-row group
@@ -397,7 +398,9 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const int wg, cha
       const int64_t t = seg1 ? kt - nk0 : kt;
       const __amdgpu_buffer_rsrc_t ra = seg1 ? rsA1 : rsA0;
       const __amdgpu_buffer_rsrc_t rb = seg1 ? rsB1 : rsB0;
-      const int64_t ta = t * (p.sMp >> 6), tb = t * (p.sNp >> 6);
+      // (A0's rows start at group sa_g0 of its scale array; A1 is chunk-local)
+      const int64_t ta = t * ((seg1 ? sMp1 : p.sMp) >> 6) + (seg1 ? 0 : p.sa_g0);
+      const int64_t tb = t * (p.sNp >> 6);
 #pragma unroll
       for (int q = 0; q < NGA; ++q)
         sca[q] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
@@ -689,7 +692,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const int wg, cha
     __builtin_amdgcn_s_waitcnt(0);
     if (lane < 32) {
       const uint32_t word = *(const uint32_t*)(sl + lane * 4);
-      const int64_t g = (m0 + tok0) >> 6;                 // the wave's 64-row group
+      const int64_t g = ((m0 + tok0) >> 6) + p.sy_g0;     // the wave's 64-row group
       uint32_t* dst = (uint32_t*)p.Ys + ((int64_t)tn * (p.sYp >> 6) + g) * 64 + 32 * wn + lane;
       __builtin_nontemporal_store(word, dst);
     }
@@ -732,7 +735,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const int wg, cha
     uint8_t* sl = (uint8_t*)(lds + sbase + wave * SCB);
     const int64_t qk = p.q1 - p.q0;
     const int64_t qkp = (qk + 127) / 128 * 128;
-    const int64_t g = (m0 + tok0) >> 6;                // the wave's 64-row group
+    const int64_t g = ((m0 + tok0) >> 6) + p.sy_g0;    // the wave's 64-row group
     const int64_t sgrp = p.sYp >> 6;                   // 64-row groups per K step
     const int row = lane;
     const bool valid = tok0 + row < rows_valid;
@@ -827,6 +830,17 @@ void gemm_pair_kernel(GemmParams pb, GemmParams pa, int nb) {
   else gemm_tile<2, 3, false, false, false>(pa, wg - nb, lds);
 }
 
+// The MXFP8 counterpart: phase B tiles (plain, SwiGLU, with or without the
+// quantized output) then the phase-A tiles of the next chunk, T leaving as MXFP8.
+template <bool SWIGLU, bool QOUT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_pair_mx_kernel(GemmParams pb, GemmParams pa, int nb) {
+  __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
+  const int wg = blockIdx.x;
+  if (wg < nb) gemm_tile<2, 4, SWIGLU, true, QOUT>(pb, wg, lds);
+  else gemm_tile<2, 3, false, true, true>(pa, wg - nb, lds);
+}
+
 template <int WM, int WN, bool SWIGLU>
 int64_t tile_count(const GemmParams& p) {
   constexpr int BM = kWaveRows * WM * 32;
@@ -874,6 +888,20 @@ hipError_t launch_gemm_pair(bool swiglu, const GemmParams& pb, const GemmParams&
   const dim3 grid((unsigned)(nb + na));
   if (swiglu) hipLaunchKernelGGL(gemm_pair_kernel<true>, grid, dim3(kThreads), 0, s, pb, pa, (int)nb);
   else hipLaunchKernelGGL(gemm_pair_kernel<false>, grid, dim3(kThreads), 0, s, pb, pa, (int)nb);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_pair_mx(bool swiglu, bool qout, const GemmParams& pb,
+                               const GemmParams& pa, hipStream_t s) {
+  const int64_t nb = swiglu ? tile_count<2, 4, true>(pb) : tile_count<2, 4, false>(pb);
+  const int64_t na = tile_count<2, 3, false>(pa);
+  if (nb <= 0 && na <= 0) return hipSuccess;
+  if (nb + na > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(nb + na)), block(kThreads);
+  if (swiglu && qout) hipLaunchKernelGGL((gemm_pair_mx_kernel<true, true>), grid, block, 0, s, pb, pa, (int)nb);
+  else if (swiglu) hipLaunchKernelGGL((gemm_pair_mx_kernel<true, false>), grid, block, 0, s, pb, pa, (int)nb);
+  else if (qout) hipLaunchKernelGGL((gemm_pair_mx_kernel<false, true>), grid, block, 0, s, pb, pa, (int)nb);
+  else hipLaunchKernelGGL((gemm_pair_mx_kernel<false, false>), grid, block, 0, s, pb, pa, (int)nb);
   return hipGetLastError();
 }
 

@@ -35,14 +35,16 @@ class StandinRefiner:
     def __init__(self, M: int, device="cuda:0", wid: int = 4, D: int = inputs.STANDIN_D,
                  F: int = inputs.STANDIN_F, ranks=inputs.RANKS, C: int = inputs.LATENT_C,
                  scale: float = 1.0, mx: bool = False, attention: bool = False,
-                 mx_onepass: bool = True):
+                 mx_onepass: bool = True, mx_chunked: bool = False):
         """mx: run the four linears as MXFP8 GEMMs.  The bf16 weights are quantized
         once here.  Every linear's input and its LoRA down output are the MXFP8 of
         their bf16 values.  mx_onepass (default): each producer writes that MXFP8
         form in the same pass (embed -> QKV input, phase A -> T, QKV phase B -> the
         V slice, O phase B -> the gate/up input, gate/up phase B -> SwiGLU's
         output); otherwise separate quantizer passes read the bf16 values back
-        (SwiGLU's output stays fused).  The two routes write the same bytes."""
+        (SwiGLU's output stays fused).  mx_chunked: run each one-pass linear through
+        fsd_mx_lora_linear (row chunks, T as MXFP8 in a 28.7 MB workspace) instead of
+        phase A over all rows then phase B.  All routes write the same bytes."""
         dev = torch.device(device)
         if attention and (mx or D % 128):
             raise ValueError("the attention step runs on the bf16 path with heads of 128")
@@ -53,6 +55,7 @@ class StandinRefiner:
         self.scale = scale
         self.mx = mx
         self.onepass = mx and mx_onepass
+        self.chunked = self.onepass and mx_chunked
         self.layers = []
         for L in inputs.standin_layers(wid, D, F, ranks):
             A, B = fsd.lora_merge([a.to(dev) for a in L["A_list"]],
@@ -91,14 +94,23 @@ class StandinRefiner:
             self.hq = mxbuf(D)           # linear inputs: h, then V
             self.vq = mxbuf(D)
             self.gq = mxbuf(F)           # SwiGLU output, quantized by the gate/up GEMM
-            self.tq = mxbuf(self.R)      # LoRA down output
+            if self.chunked:
+                # T as MXFP8, two chunks of 21,760 rows (28.8 MB at rank 576), shared by
+                # the four linears
+                self.mx_ws = torch.empty(max(fsd.mx_workspace_bytes(M, self.R), 16),
+                                         dtype=u8, device=dev)
+            else:
+                self.tq = mxbuf(self.R)  # LoRA down output, all rows
             del self.g
         self.events = None
 
     def launch_names(self):
-        """Mark name of each launch of one bf16 LoRA linear over this refiner's
-        tokens: phase A then phase B ('down', 'up'), or, chunked, phase A of the
-        first chunk ('down0') followed by phase-B / next-phase-A pairs ('pair')."""
+        """Mark name of each launch of one LoRA linear over this refiner's tokens:
+        phase A then phase B ('down', 'up'), or, chunked, phase A of the first
+        chunk ('down0') followed by phase-B / next-phase-A pairs ('pair')."""
+        if self.chunked:
+            n, _ = fsd.mx_lora_linear_plan(self.M, self.R, self.mx_ws.numel())
+            return ["down0"] + ["pair"] * (n - 1)
         n, _, sched = fsd.lora_linear_plan(self.M, self.R, self.ws.numel())
         if sched == 1:
             return ["down0"] + ["pair"] * (n - 1)
@@ -136,23 +148,41 @@ class StandinRefiner:
         else:
             fsd.mx_lora_up(*Xmx, *L["W0q"], *self.tq, *L["Bq"], residual=residual, out=out)
 
-    # one MXFP8 LoRA linear whose T never exists in bf16: phase A writes its MXFP8
-    # form, phase B optionally the MXFP8 form of (some of) its output columns
+    # one MXFP8 LoRA linear in row chunks (fsd_mx_lora_linear): T exists only as the
+    # MXFP8 of one chunk in the workspace; phase B optionally writes the MXFP8 form
+    # of (some of) its output columns, or SwiGLU's output as MXFP8 only
     def _mx_linear_onepass(self, idx, Xmx, out=None, residual=None, swiglu_mx=False,
                            qout=None, cols=None):
         L = self.layers[idx]
         name = self.LAYER_NAMES[idx]
-        self._mark(f"{name}.down")
-        fsd.mx_lora_down_mx(*Xmx, *L["Aq"], self.scale, *self.tq)
-        self._mark(f"{name}.up")
+        if not self.chunked:
+            # phase A over all rows writing T as MXFP8, then phase B
+            self._mark(f"{name}.down")
+            fsd.mx_lora_down_mx(*Xmx, *L["Aq"], self.scale, *self.tq)
+            self._mark(f"{name}.up")
+            if swiglu_mx:
+                fsd.mx_lora_up_swiglu_mx(*Xmx, *L["W0q"], *self.tq, *L["Bq"], Hq=self.gq[0],
+                                         Hs=self.gq[1])
+            elif qout is not None:
+                fsd.mx_lora_up_q(*Xmx, *L["W0q"], *self.tq, *L["Bq"], residual=residual,
+                                 out=out, cols=cols, Yq=qout[0], Ys=qout[1])
+            else:
+                fsd.mx_lora_up(*Xmx, *L["W0q"], *self.tq, *L["Bq"], residual=residual, out=out)
+            return
+        hook = None
+        if self.events is not None:
+            names = self.launch_names()
+            hook = lambda i: self._mark(f"{name}.{names[i]}")
         if swiglu_mx:
-            fsd.mx_lora_up_swiglu_mx(*Xmx, *L["W0q"], *self.tq, *L["Bq"], Hq=self.gq[0],
-                                     Hs=self.gq[1])
-        elif qout is not None:
-            fsd.mx_lora_up_q(*Xmx, *L["W0q"], *self.tq, *L["Bq"], residual=residual, out=out,
-                             cols=cols, Yq=qout[0], Ys=qout[1])
+            fsd.mx_lora_linear(*Xmx, *L["Aq"], *L["W0q"], *L["Bq"], self.scale,
+                               epilogue=fsd.EPI_SWIGLU, Yq=self.gq[0], Ys=self.gq[1],
+                               workspace=self.mx_ws, on_launch=hook)
         else:
-            fsd.mx_lora_up(*Xmx, *L["W0q"], *self.tq, *L["Bq"], residual=residual, out=out)
+            fsd.mx_lora_linear(*Xmx, *L["Aq"], *L["W0q"], *L["Bq"], self.scale,
+                               residual=residual, out=out, cols=cols,
+                               Yq=None if qout is None else qout[0],
+                               Ys=None if qout is None else qout[1],
+                               workspace=self.mx_ws, on_launch=hook)
 
     def _quantize(self, name, X, buf):
         self._mark(name)
@@ -256,6 +286,12 @@ class StandinRefiner:
         for L, name in zip(self.layers, self.LAYER_NAMES):
             K, N = L["K"], L["N"]
             down, up = 2 * M * K * r, 2 * M * (K + r) * N
+            if self.chunked:
+                _, R = fsd.mx_lora_linear_plan(M, r, self.mx_ws.numel())
+                first = 2 * min(M, R) * K * r
+                out[name + ".down0"] = first * steps
+                out[name + ".pair"] = (down - first + up) * steps
+                continue
             if self.mx:
                 out[name + ".down"] = down * steps
                 out[name + ".up"] = up * steps

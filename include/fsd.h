@@ -383,6 +383,57 @@ int fsd_token_embed_mx(const float* z, const void* E, void* X, int64_t ldx,
                        int64_t M, int64_t C, int64_t D, void* Xq, int64_t ldxq,
                        void* Xs, void* stream);
 
+/* The whole MXFP8 LoRA linear in row chunks, with T kept small and quantized:
+ * the schedule of fsd_lora_linear ([CW] section "三个步如何完成工作": the
+ * rank-576 merged adapter on every adapted linear) on MXFP8 operands.  Chunks of
+ * R rows (a multiple of 256, at most 21,760) pass through two halves of the
+ * workspace; launch 0 is phase A of chunk 0, launch c + 1 is phase B of chunk c
+ * together with phase A of chunk c + 1 in one grid.  Phase A writes its chunk
+ * of T as MXFP8 (fsd_mx_lora_down_mx's bytes); phase B is fsd_mx_lora_up (or
+ * its quantizing forms) over the chunk's rows, so every output byte equals the
+ * unchunked route's.
+ *   Xq, ldxq, Xs: the input, MXFP8 [M, Kp] with scales for M rows, K a
+ *     multiple of 32; Aq, As: the merged down projection [r, Kp], r a multiple
+ *     of 32; W0q, W0s [N, Kp] and Bq, Bs [N, rp]: as for fsd_mx_lora_up;
+ *     scale: applied to T before its bf16 rounding.
+ *   epilogue FSD_EPI_NONE: Y bf16 [M, N] (row stride ldy), bias and residual
+ *     as for fsd_mx_lora_up; with Yq != NULL also the MXFP8 of Y's columns
+ *     [q0, q1) as fsd_mx_lora_up_q writes it.
+ *   epilogue FSD_EPI_SWIGLU: either Y bf16 [M, N/2] (N a multiple of 128) or,
+ *     with Y == NULL, Yq/Ys = the MXFP8 of H as fsd_mx_lora_up_swiglu_mx writes
+ *     it (q0 = 0, q1 = N/2, N a multiple of 256); no residual.
+ *   workspace: 16-byte aligned, owned by the caller, read and written only by
+ *     this call's kernels; it must hold two chunks of at least 256 rows of T
+ *     (rp + rp/32 bytes per row), else FSD_EWORKSPACE.  Outputs must overlap
+ *     neither an input, the workspace nor each other (the residual may be Y).
+ * fsd_mx_lora_linear_workspace_bytes: the preferred size: two chunks of
+ *   min(M rounded up to 256, 21,760) rows (28.8 MB at r = 576).
+ * fsd_mx_lora_linear_plan: the number of launches and the chunk rows for M
+ *   rows at rank r through workspace_bytes (FSD_EWORKSPACE if too small).
+ * fsd_mx_lora_linear_launch: launch `index` (0 <= index < launches) alone,
+ *   e.g. to put timing events between launches; issuing every index in order
+ *   on one stream is fsd_mx_lora_linear. */
+size_t fsd_mx_lora_linear_workspace_bytes(int64_t M, int64_t r);
+int fsd_mx_lora_linear_plan(int64_t M, int64_t r, size_t workspace_bytes,
+                            int64_t* launches, int64_t* chunk_rows);
+int fsd_mx_lora_linear(const void* Xq, int64_t ldxq, const void* Xs,
+                       const void* Aq, const void* As, float scale,
+                       const void* W0q, const void* W0s, const void* Bq,
+                       const void* Bs, const float* bias, const void* residual,
+                       int64_t ldr, void* Y, int64_t ldy, int64_t M, int64_t N,
+                       int64_t K, int64_t r, int epilogue, int64_t q0, int64_t q1,
+                       void* Yq, int64_t ldyq, void* Ys, void* workspace,
+                       size_t workspace_bytes, void* stream);
+int fsd_mx_lora_linear_launch(const void* Xq, int64_t ldxq, const void* Xs,
+                              const void* Aq, const void* As, float scale,
+                              const void* W0q, const void* W0s, const void* Bq,
+                              const void* Bs, const float* bias,
+                              const void* residual, int64_t ldr, void* Y,
+                              int64_t ldy, int64_t M, int64_t N, int64_t K,
+                              int64_t r, int epilogue, int64_t q0, int64_t q1,
+                              void* Yq, int64_t ldyq, void* Ys, void* workspace,
+                              size_t workspace_bytes, int64_t index, void* stream);
+
 /* ------------------------------------------------------------------------ *
  * Dense attention (NEXT step: the refine path's baseline attention)          *
  * ------------------------------------------------------------------------ *

@@ -405,3 +405,54 @@ def test_one_pass_mx_validation(L):
     assert emx(Xq=P(BASE + 4 * 0x10000000 + 4)) == EALIGN
     assert emx(Xq=P(BASE + 3 * 0x10000000 + 4096)) == EINVAL   # Xq overlaps X
     assert emx(Xs=P(BASE + 0x10000000 + 16)) == EINVAL         # Xs overlaps z
+
+
+def test_mx_lora_linear_plan_and_validation(L):
+    f = ctypes.c_float
+    rp_row = 640 + 20                                  # codes + scales per row of T, r = 576
+    assert L.fsd_mx_lora_linear_workspace_bytes(532800, 576) == 2 * 21760 * rp_row
+    assert L.fsd_mx_lora_linear_workspace_bytes(1000, 576) == 2 * 1024 * rp_row
+    assert L.fsd_mx_lora_linear_workspace_bytes(0, 576) == 0
+    n, R = ctypes.c_int64(), ctypes.c_int64()
+
+    def plan(M, r, ws):
+        st = L.fsd_mx_lora_linear_plan(M, r, ws, ctypes.byref(n), ctypes.byref(R))
+        return st, n.value, R.value
+    assert plan(532800, 576, 2 * 21760 * rp_row) == (OK, -(-532800 // 21760) + 1, 21760)
+    assert plan(532800, 576, 10 ** 9)[2] == 21760          # capped at 85 row tiles
+    assert plan(5037, 576, 2 * 256 * rp_row) == (OK, 21, 256)
+    assert plan(5037, 576, 2 * 256 * rp_row - 1)[0] == EWS   # not two 256-row chunks
+    assert plan(1, 64, 2 * 256 * (128 + 4))[1:] == (2, 256)
+    assert plan(100, 40, 10 ** 6)[0] == EINVAL               # r % 32
+    assert L.fsd_mx_lora_linear_plan(100, 64, 10 ** 6, None, ctypes.byref(R)) == EINVAL
+
+    def lin(**kw):
+        args = dict(Xq=a(1), ldxq=1024, Xs=a(2), Aq=a(3), As=a(4), s=1.0, Wq=a(5), Ws=a(6),
+                    Bq=a(7), Bs=a(8), bias=None, res=None, ldr=0, Y=a(9), ldy=1024, M=300,
+                    N=1024, K=1024, r=576, epi=0, q0=0, q1=0, Yq=None, ldyq=0, Ys=None,
+                    ws=a(10), wsb=2 * 256 * rp_row)
+        args.update(kw)
+        return L.fsd_mx_lora_linear(
+            args["Xq"], args["ldxq"], args["Xs"], args["Aq"], args["As"], f(args["s"]),
+            args["Wq"], args["Ws"], args["Bq"], args["Bs"], args["bias"], args["res"],
+            args["ldr"], args["Y"], args["ldy"], args["M"], args["N"], args["K"], args["r"],
+            args["epi"], args["q0"], args["q1"], args["Yq"], args["ldyq"], args["Ys"],
+            args["ws"], args["wsb"], None)
+    assert lin(M=0) == OK
+    assert lin(M=0, ws=None, wsb=0) == OK
+    assert lin(M=0, res=a(9), ldr=1024) == OK                 # in-place residual
+    assert lin(wsb=2 * 256 * rp_row - 1) == EWS
+    assert lin(ws=None) == EWS
+    assert lin(ws=P(BASE + 10 * 0x10000000 + 8)) == EALIGN
+    assert lin(ws=P(BASE + 9 * 0x10000000 + 64)) == EINVAL      # workspace overlaps Y
+    assert lin(r=40) == EINVAL
+    assert lin(Y=None) == EINVAL                               # plain epilogue needs Y
+    assert lin(epi=1, Yq=a(11), Ys=a(12), ldyq=512, q0=0, q1=512) == EINVAL   # SwiGLU: Y xor Yq
+    assert lin(M=0, epi=1, Y=None, Yq=a(11), Ys=a(12), ldyq=512, q0=0, q1=512) == OK
+    assert lin(epi=1, Y=None, Yq=a(11), Ys=a(12), ldyq=512, q0=0, q1=256) == EINVAL
+    assert lin(epi=1, N=1152, Y=None, Yq=a(11), Ys=a(12), ldyq=576, q0=0, q1=576) == EUNSUP
+    assert lin(epi=1, res=a(13), ldr=512, ldy=512) == EINVAL   # no residual with SwiGLU
+    assert lin(Yq=a(11), Ys=a(12), ldyq=1024, q0=16, q1=1024) == EINVAL
+    assert lin(Yq=a(11), Ys=a(12), ldyq=1000, q0=0, q1=1024) == EINVAL
+    assert lin(Yq=P(BASE + 9 * 0x10000000 + 4096), Ys=a(12), ldyq=1024, q0=0, q1=1024) == EINVAL
+    assert lin(M=0, Yq=a(11), Ys=a(12), ldyq=1024, q0=0, q1=1024) == OK

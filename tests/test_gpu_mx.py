@@ -326,6 +326,88 @@ def test_embed_mx_one_pass(gpu, M, C, D):
     assert torch.equal(Xs, Xs2), "scales differ from the unfused route"
 
 
+@pytest.mark.parametrize("M,K,N,r,mode,chunk_rows", [
+    (5037, 256, 512, 576, "res+q", 256),       # 20 chunks of 256 rows
+    (5037, 256, 512, 576, "plain", 768),
+    (300, 128, 256, 64, "swiglu_mx", 256),
+    (1, 128, 256, 96, "swiglu_bf16", 256),
+    (4133, 384, 768, 96, "q_slice", 1024),
+    (1000, 128, 512, 576, "swiglu_mx", None),  # the preferred workspace: one chunk
+])
+def test_mx_lora_linear_chunked(gpu, M, K, N, r, mode, chunk_rows):
+    """The chunked MXFP8 LoRA linear (phase B of a chunk with phase A of the next,
+    T as MXFP8 in two workspace halves) writes the bytes of the unchunked one-pass
+    route: mx_lora_down_mx then the matching phase B, codes, scales and padding
+    included, for every output mode; and the launches issued one by one equal the
+    whole call."""
+    say(f"mx chunked linear M={M} K={K} N={N} r={r} {mode} chunk={chunk_rows}")
+    rng = np.random.default_rng(M + K + N + r)
+    Qx, Sx, _ = mx_operand(rng.standard_normal((M, K)), gpu)
+    Qa, Sa, _ = mx_operand(rng.standard_normal((r, K)) * 0.05, gpu)
+    Qw, Sw, _ = mx_operand(rng.standard_normal((N, K)) * 0.03, gpu)
+    Qb, Sb, _ = mx_operand(rng.standard_normal((N, r)) * 0.02, gpu)
+    bias = torch.from_numpy(rng.standard_normal(N).astype(np.float32) * 0.1).to(gpu)
+    scale = 0.75
+    swiglu = mode.startswith("swiglu")
+    nout = N // 2 if swiglu else N
+    res = None
+    if mode == "res+q":
+        res = torch.from_numpy(rng.standard_normal((M, N))).to(torch.bfloat16).to(gpu)
+    cols = {"res+q": (0, N), "q_slice": (N - 256, N)}.get(mode)
+    rp = fsd.mx_padded_k(r)
+    if chunk_rows is None:
+        ws = torch.empty(fsd.mx_workspace_bytes(M, r), dtype=torch.uint8, device=gpu)
+    else:
+        ws = torch.empty(2 * chunk_rows * (rp + rp // 32), dtype=torch.uint8, device=gpu)
+    n, R = fsd.mx_lora_linear_plan(M, r, ws.numel())
+    assert R == (min(21760, (M + 255) // 256 * 256) if chunk_rows is None else chunk_rows)
+    assert n == -(-M // R) + 1
+    # reference: the unchunked one-pass route
+    Tq, Ts = fsd.mx_lora_down_mx(Qx, Sx, Qa, Sa, scale)
+    ep = "swiglu" if swiglu else "none"
+
+    def fresh(shape, dtype):
+        t = torch.empty(shape, dtype=dtype, device=gpu)
+        _garbage(t.view(torch.uint8))
+        return t
+
+    def run(on_launch=None):
+        kw = dict(scale=scale, bias=bias, epilogue=ep, workspace=ws, on_launch=on_launch)
+        if mode == "swiglu_mx":
+            Hq = fresh((M, nout), torch.uint8)
+            Hs = fresh((fsd.mx_scale_bytes(M, nout),), torch.uint8)
+            return fsd.mx_lora_linear(Qx, Sx, Qa, Sa, Qw, Sw, Qb, Sb, Yq=Hq, Ys=Hs, **kw)
+        out = fresh((M, nout), torch.bfloat16)
+        if res is not None:
+            out.copy_(res)                      # residual added in place
+        if cols is None:
+            return (fsd.mx_lora_linear(Qx, Sx, Qa, Sa, Qw, Sw, Qb, Sb, out=out,
+                                       residual=None if res is None else out, **kw),)
+        q0, q1 = cols
+        Yq = fresh((M, fsd.mx_padded_k(q1 - q0)), torch.uint8)
+        Ys = fresh((fsd.mx_scale_bytes(M, q1 - q0),), torch.uint8)
+        return fsd.mx_lora_linear(Qx, Sx, Qa, Sa, Qw, Sw, Qb, Sb, out=out, cols=cols, Yq=Yq,
+                                  Ys=Ys, residual=None if res is None else out, **kw)
+
+    got = run()
+    if mode == "swiglu_mx":
+        ref = fsd.mx_lora_up_swiglu_mx(Qx, Sx, Qw, Sw, Tq, Ts, Qb, Sb, bias=bias)
+    elif mode == "swiglu_bf16":
+        ref = (fsd.mx_lora_up(Qx, Sx, Qw, Sw, Tq, Ts, Qb, Sb, bias=bias, epilogue="swiglu"),)
+    else:
+        Y = fsd.mx_lora_up(Qx, Sx, Qw, Sw, Tq, Ts, Qb, Sb, bias=bias, residual=res)
+        ref = (Y,) if cols is None else (Y,) + fsd.mx_quantize(Y[:, cols[0]:cols[1]])
+    assert len(got) == len(ref)
+    for g_, r_ in zip(got, ref):
+        assert torch.equal(g_.view(torch.uint8), r_.view(torch.uint8)), "chunked != unchunked"
+    # launch by launch (with a host callback between launches) equals the whole call
+    calls = []
+    got2 = run(on_launch=calls.append)
+    assert calls == list(range(n))
+    for g_, r_ in zip(got2, ref):
+        assert torch.equal(g_.view(torch.uint8), r_.view(torch.uint8)), "launches != whole call"
+
+
 def test_mx_standin_one_pass_equals_multi_pass(gpu):
     """The stand-in refine through the one-pass route (every activation quantized by
     its producer) and through separate quantizer passes: identical latents."""
@@ -336,8 +418,11 @@ def test_mx_standin_one_pass_equals_multi_pass(gpu):
     u, eps = inputs.latent(4, tokens=M)
     u, eps = u.to(gpu), eps.to(gpu)
     z1 = StandinRefiner(M, device=gpu, D=D, F=F, mx=True).refine(u, eps).clone()
-    z2 = StandinRefiner(M, device=gpu, D=D, F=F, mx=True, mx_onepass=False).refine(u, eps)
+    z2 = StandinRefiner(M, device=gpu, D=D, F=F, mx=True, mx_onepass=False).refine(u, eps).clone()
     assert torch.equal(z1, z2)
+    # the chunked MXFP8 linear (fsd_mx_lora_linear) in place of phase A over all rows
+    z3 = StandinRefiner(M, device=gpu, D=D, F=F, mx=True, mx_chunked=True).refine(u, eps)
+    assert torch.equal(z1, z3)
 
 
 # ------------------------------------------------- full-size MXFP8 linear
@@ -443,11 +528,13 @@ def test_mx_standin_refine_2k_sampled(gpu):
     zt = model.refine(u.to(gpu), eps.to(gpu)).clone()
     del model
     torch.cuda.empty_cache()
-    # the one-pass route (the default) writes the bytes of the quantizer passes
-    model = StandinRefiner(M, device=gpu, D=D, F=F, mx=True, mx_onepass=False)
-    assert torch.equal(zt, model.refine(u.to(gpu), eps.to(gpu))), "one-pass != multi-pass at 2K"
-    del model
-    torch.cuda.empty_cache()
+    # the one-pass route (the default) writes the bytes of the quantizer passes, and
+    # so does the chunked one (21,760-row chunks, T as MXFP8 in a 28.7 MB workspace)
+    for kw, what in ((dict(mx_onepass=False), "multi-pass"), (dict(mx_chunked=True), "chunked")):
+        model = StandinRefiner(M, device=gpu, D=D, F=F, mx=True, **kw)
+        assert torch.equal(zt, model.refine(u.to(gpu), eps.to(gpu))), f"one-pass != {what} at 2K"
+        del model
+        torch.cuda.empty_cache()
     z = zt.cpu().numpy()
     del zt
     assert np.all(np.isfinite(z))
