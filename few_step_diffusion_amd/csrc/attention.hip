@@ -19,10 +19,13 @@
 // fragment is one 16-byte read.  The running maximum is kept until a block's
 // maximum exceeds it by more than 2^8 (P stays <= 256, exact enough for bf16
 // and fp32 sums), so the fp32 output is rescaled only in the rare blocks where
-// some row of the wave needs it.  The row sums of P come from the matrix pipe:
+// some row of the wave needs it, and the exact row maximum (a reduction over
+// four lanes) is formed only in those blocks.  The row sums of P come from the matrix pipe:
 // a ninth 16-column output block is P times a block of ones, so the softmax
 // denominator uses the same bf16 P as the numerator and costs no VALU adds.
 #include <math.h>
+
+#include <type_traits>
 
 #include "fsd_internal.h"
 
@@ -140,8 +143,11 @@ void attention_kernel(AttnParams p) {
 
   const int nkb = (int)((S + kBK - 1) / kBK);
   issue_block(0, 0);
-  for (int j = 0; j < nkb; ++j) {
-    const int buf = j & 1;
+  // key block j in stage buffer BUF = j & 1 (a compile-time constant: the loop
+  // below runs two blocks per trip, so every LDS address is a fixed per-lane
+  // offset plus an immediate)
+  auto block = [&](int j, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
     // own loads of block j (and, once, the Q fragments) have landed; after the
     // barrier so have everyone's, and every wave is done with block j - 1
     __builtin_amdgcn_s_waitcnt(0);
@@ -176,49 +182,63 @@ void attention_kernel(AttnParams p) {
         for (int t = 0; t < 4; ++t)
           if (16 * kj + 4 * c4 + t >= kvalid) { s[0][kj][t] = -INFINITY; s[1][kj][t] = -INFINITY; }
     }
-    // online softmax in the exp2 domain
+    // online softmax in the exp2 domain: first the exponent arguments against the
+    // running maximum; only when one of them exceeds 8 (some row's maximum grew
+    // by more than a factor 2^8 — always so in the first block) is the exact row
+    // maximum formed and the output rescaled, so the common block needs no
+    // cross-lane reduction
     bf16x8 pf[2][2];
 #pragma unroll
     for (int qi = 0; qi < 2; ++qi) {
-      float mx = -INFINITY;
+      float tt[4][4];
+      float tm = -INFINITY;
 #pragma unroll
       for (int kj = 0; kj < 4; ++kj)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) mx = fmaxf(mx, s[qi][kj][t]);
-      // row maximum over lanes l, l^16, l^32, l^48: gfx950's row swaps give each
-      // lane the pair {x[l], x[l^16]} (then {x[l], x[l^32]}) without LDS
-      {
+        for (int t = 0; t < 4; ++t) {
+          tt[kj][t] = fmaf(s[qi][kj][t], p.scale_log2, -m_run[qi]);
+          tm = fmaxf(tm, tt[kj][t]);
+        }
+      if (__builtin_amdgcn_ballot_w64(!(tm <= 8.0f)) != 0) {   // wave-uniform, rare
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kj = 0; kj < 4; ++kj)
+#pragma unroll
+          for (int t = 0; t < 4; ++t) mx = fmaxf(mx, s[qi][kj][t]);
+        // row maximum over lanes l, l^16, l^32, l^48: gfx950's row swaps give
+        // each lane the pair {x[l], x[l^16]} (then {x[l], x[l^32]}) without LDS
         const auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx),
                                                           false, false);
         mx = fmaxf(__uint_as_float(p16[0]), __uint_as_float(p16[1]));
         const auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
                                                           false, false);
         mx = fmaxf(__uint_as_float(p32[0]), __uint_as_float(p32[1]));
+        const float m_blk = mx * p.scale_log2;
+        const bool grow = m_blk > m_run[qi] + 8.0f;
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+          const float m_new = grow ? m_blk : m_run[qi];
+          const float alpha = __builtin_amdgcn_exp2f(m_run[qi] - m_new);
+#pragma unroll
+          for (int dj = 0; dj < 9; ++dj) o[qi][dj] *= alpha;
+          m_run[qi] = m_new;
+#pragma unroll
+          for (int kj = 0; kj < 4; ++kj)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) tt[kj][t] = fmaf(s[qi][kj][t], p.scale_log2, -m_run[qi]);
+        }
       }
-      const float m_blk = mx * p.scale_log2;
-      const bool grow = m_blk > m_run[qi] + 8.0f;       // (always true for the first block)
-      if (__builtin_amdgcn_ballot_w64(grow) != 0) {     // wave-uniform, rare
-        const float m_new = grow ? m_blk : m_run[qi];
-        const float alpha = __builtin_amdgcn_exp2f(m_run[qi] - m_new);
-#pragma unroll
-        for (int dj = 0; dj < 9; ++dj) o[qi][dj] *= alpha;
-        m_run[qi] = m_new;
-      }
-      const float m_use = m_run[qi];
-      float pv[4][4];
-#pragma unroll
-      for (int kj = 0; kj < 4; ++kj)
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-          pv[kj][t] = __builtin_amdgcn_exp2f(fmaf(s[qi][kj][t], p.scale_log2, -m_use));
       // P as the PV operand: slots 0..3 = keys 4c..4c+3 of key block 2·kk2,
       // slots 4..7 = the same of block 2·kk2 + 1 (the Vᵀ fragment matches)
 #pragma unroll
       for (int kk2 = 0; kk2 < 2; ++kk2)
-        pf[qi][kk2] = (bf16x8){(__bf16)pv[2 * kk2][0], (__bf16)pv[2 * kk2][1],
-                               (__bf16)pv[2 * kk2][2], (__bf16)pv[2 * kk2][3],
-                               (__bf16)pv[2 * kk2 + 1][0], (__bf16)pv[2 * kk2 + 1][1],
-                               (__bf16)pv[2 * kk2 + 1][2], (__bf16)pv[2 * kk2 + 1][3]};
+        pf[qi][kk2] = (bf16x8){(__bf16)__builtin_amdgcn_exp2f(tt[2 * kk2][0]),
+                               (__bf16)__builtin_amdgcn_exp2f(tt[2 * kk2][1]),
+                               (__bf16)__builtin_amdgcn_exp2f(tt[2 * kk2][2]),
+                               (__bf16)__builtin_amdgcn_exp2f(tt[2 * kk2][3]),
+                               (__bf16)__builtin_amdgcn_exp2f(tt[2 * kk2 + 1][0]),
+                               (__bf16)__builtin_amdgcn_exp2f(tt[2 * kk2 + 1][1]),
+                               (__bf16)__builtin_amdgcn_exp2f(tt[2 * kk2 + 1][2]),
+                               (__bf16)__builtin_amdgcn_exp2f(tt[2 * kk2 + 1][3])};
     }
     // O += P·V: Vᵀ fragment of head dims 16·dj + l%16, keys 32·kk2 + 4c + 0..3
     // and 32·kk2 + 16 + 4c + 0..3: chunk 4·kk2 + c of the interleaved row
@@ -238,7 +258,13 @@ void attention_kernel(AttnParams p) {
 #pragma unroll
       for (int qi = 0; qi < 2; ++qi)
         o[qi][8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[qi][kk2], o[qi][8], 0, 0, 0);
+  };
+  int j = 0;
+  for (; j + 1 < nkb; j += 2) {
+    block(j, std::integral_constant<int, 0>{});
+    block(j + 1, std::integral_constant<int, 1>{});
   }
+  if (j < nkb) block(j, std::integral_constant<int, 0>{});
 
   // O / l, rounded to bf16: lane l writes query 16·qi + l%16, head dims
   // 16·dj + 4c .. +3 (8 bytes)
