@@ -798,11 +798,19 @@ inline int64_t mx_t_row_bytes(int64_t r) {
   return rp + rp / 32;
 }
 
+// The largest chunk: 85 row tiles, and few enough rows that one chunk's T
+// scales (R·rp/32 bytes) stay inside a buffer descriptor's 32-bit byte range.
+inline int64_t mx_max_chunk_rows(int64_t r) {
+  const int64_t rp = round_up(r, 128);
+  const int64_t cap = kMaxOffsetBytes / (rp / 32) / kTileM * kTileM;
+  return cap < kMxPairChunkRows ? cap : kMxPairChunkRows;
+}
+
 struct MxPlan {
   int64_t R, nc, launches;
 };
 
-// Chunks of R rows (a multiple of 256, at most kMxPairChunkRows) through two
+// Chunks of R rows (a multiple of 256, at most mx_max_chunk_rows) through two
 // halves of the workspace: launch 0 is phase A of chunk 0, launch c + 1 phase B
 // of chunk c with phase A of chunk c + 1 (none after the last).  R = 0 when not
 // even two 256-row chunks fit.
@@ -811,7 +819,7 @@ MxPlan make_mx_plan(int64_t M, int64_t r, int64_t ws_bytes) {
   if (M <= 0 || r <= 0) return pl;
   const int64_t fit = ws_bytes / mx_t_row_bytes(r);
   int64_t R = (fit / 2) / kTileM * kTileM;
-  if (R > kMxPairChunkRows) R = kMxPairChunkRows;
+  if (R > mx_max_chunk_rows(r)) R = mx_max_chunk_rows(r);
   if (R > round_up(M, kTileM)) R = round_up(M, kTileM);
   if (R < kTileM) return pl;
   pl.R = R;
@@ -945,8 +953,8 @@ extern "C" {
 
 size_t fsd_mx_lora_linear_workspace_bytes(int64_t M, int64_t r) {
   if (M <= 0 || r <= 0) return 0;
-  const int64_t rows =
-      round_up(M, kTileM) < kMxPairChunkRows ? round_up(M, kTileM) : kMxPairChunkRows;
+  const int64_t cap = mx_max_chunk_rows(r);
+  const int64_t rows = round_up(M, kTileM) < cap ? round_up(M, kTileM) : cap;
   return (size_t)(2 * rows * mx_t_row_bytes(r));
 }
 

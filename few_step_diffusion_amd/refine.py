@@ -95,7 +95,7 @@ class StandinRefiner:
             self.vq = mxbuf(D)
             self.gq = mxbuf(F)           # SwiGLU output, quantized by the gate/up GEMM
             if self.chunked:
-                # T as MXFP8, two chunks of 21,760 rows (28.8 MB at rank 576), shared by
+                # T as MXFP8, two chunks of 21,760 rows (28.7 MB at rank 576), shared by
                 # the four linears
                 self.mx_ws = torch.empty(max(fsd.mx_workspace_bytes(M, self.R), 16),
                                          dtype=u8, device=dev)

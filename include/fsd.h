@@ -407,7 +407,9 @@ int fsd_token_embed_mx(const float* z, const void* E, void* X, int64_t ldx,
  *     (rp + rp/32 bytes per row), else FSD_EWORKSPACE.  Outputs must overlap
  *     neither an input, the workspace nor each other (the residual may be Y).
  * fsd_mx_lora_linear_workspace_bytes: the preferred size: two chunks of
- *   min(M rounded up to 256, 21,760) rows (28.8 MB at r = 576).
+ *   min(M rounded up to 256, 21,760) rows (28.7 MB at r = 576); at ranks above
+ *   about 3.1 million the chunk is further capped so that its T scales
+ *   (R·rp/32 bytes) stay below 2^31 bytes.
  * fsd_mx_lora_linear_plan: the number of launches and the chunk rows for M
  *   rows at rank r through workspace_bytes (FSD_EWORKSPACE if too small).
  * fsd_mx_lora_linear_launch: launch `index` (0 <= index < launches) alone,

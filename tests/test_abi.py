@@ -424,6 +424,12 @@ def test_mx_lora_linear_plan_and_validation(L):
     assert plan(5037, 576, 2 * 256 * rp_row - 1)[0] == EWS   # not two 256-row chunks
     assert plan(1, 64, 2 * 256 * (128 + 4))[1:] == (2, 256)
     assert plan(100, 40, 10 ** 6)[0] == EINVAL               # r % 32
+    # at a huge rank the chunk's T scales (R·rp/32 bytes) must stay below 2^31
+    big_r = 1 << 22
+    cap = (0x7FFFFFFF // (big_r // 32)) // 256 * 256
+    assert cap < 21760
+    assert L.fsd_mx_lora_linear_workspace_bytes(10 ** 6, big_r) == 2 * cap * (big_r + big_r // 32)
+    assert plan(10 ** 6, big_r, 10 ** 12)[2] == cap
     assert L.fsd_mx_lora_linear_plan(100, 64, 10 ** 6, None, ctypes.byref(R)) == EINVAL
 
     def lin(**kw):
