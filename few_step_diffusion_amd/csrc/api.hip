@@ -1017,8 +1017,12 @@ int fsd_graph_end(void* stream, void** graph) {
   if (hipStreamEndCapture(as_stream(stream), &g) != hipSuccess || !g) return FSD_EHIP;
   hipGraphExec_t exec = nullptr;
   const hipError_t e = hipGraphInstantiate(&exec, g, nullptr, nullptr, 0);
-  hipGraphDestroy(g);
+  const hipError_t d = hipGraphDestroy(g);    // the instance does not need its template
   if (e != hipSuccess || !exec) return FSD_EHIP;
+  if (d != hipSuccess) {
+    (void)hipGraphExecDestroy(exec);
+    return FSD_EHIP;
+  }
   *graph = (void*)exec;
   return FSD_OK;
 }

@@ -318,6 +318,7 @@ __global__ __launch_bounds__(64) void head_kernel(const bf16_t* H, int64_t ldh, 
 
 hipError_t launch_embed(const float* z, const bf16_t* E, bf16_t* X, int64_t ldx, int64_t M,
                         int C, int64_t D, hipStream_t s) {
+  if (C < 1 || C > kMaxC) return hipErrorInvalidValue;   // the kernels take at most 32 channels
   if (M == 0) return hipSuccess;
   const int64_t waves = ((M + kEmbedTokens - 1) / kEmbedTokens) *
                         ((D + kEmbedCols - 1) / kEmbedCols);
@@ -332,6 +333,7 @@ hipError_t launch_embed(const float* z, const bf16_t* E, bf16_t* X, int64_t ldx,
 hipError_t launch_embed_mx(const float* z, const bf16_t* E, bf16_t* X, int64_t ldx, int64_t M,
                            int C, int64_t D, uint8_t* Xq, int64_t ldxq, uint8_t* Xs,
                            hipStream_t s) {
+  if (C < 1 || C > kMaxC) return hipErrorInvalidValue;   // the kernels take at most 32 channels
   if (M == 0) return hipSuccess;
   if (D % 128) return hipErrorInvalidValue;
   const int64_t waves = ((M + kEmbedTokens - 1) / kEmbedTokens) *
@@ -347,6 +349,7 @@ hipError_t launch_embed_mx(const float* z, const bf16_t* E, bf16_t* X, int64_t l
 
 hipError_t launch_head(const bf16_t* H, int64_t ldh, const bf16_t* P, float* v, int64_t M,
                        int64_t D, int C, hipStream_t s) {
+  if (C < 1 || C > kMaxC) return hipErrorInvalidValue;   // the kernels take at most 32 channels
   if (M == 0) return hipSuccess;
   const int64_t blocks = (M + kHeadRows - 1) / kHeadRows;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
@@ -357,6 +360,7 @@ hipError_t launch_head(const bf16_t* H, int64_t ldh, const bf16_t* P, float* v, 
 
 hipError_t launch_head_euler(const bf16_t* H, int64_t ldh, const bf16_t* P, float* z,
                              float dsigma, int64_t M, int64_t D, int C, hipStream_t s) {
+  if (C < 1 || C > kMaxC) return hipErrorInvalidValue;   // the kernels take at most 32 channels
   if (M == 0) return hipSuccess;
   const int64_t blocks = (M + kHeadRows - 1) / kHeadRows;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
