@@ -74,6 +74,8 @@ def parse():
                     help="skip the refine with dense attention between QKV and O")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the LoRA linears at the 768P and 4K-chunk shapes")
+    ap.add_argument("--no-vendor", action="store_true",
+                    help="skip phase B beside torch.matmul (the BLAS library) at the 2K shapes")
     ap.add_argument("--no-shard", action="store_true",
                     help="skip the step over one GPU's 1/8 share of the tokens")
     ap.add_argument("--calib-copy", action="store_true",
@@ -505,6 +507,61 @@ def lora_linear_configs(torch, fsd, reps=20, warm=5):
     return out
 
 
+def vendor_gemm(torch, fsd, reps=10, warm=3):
+    """Phase B of the 2K QKV and O linears beside the BLAS library torch calls,
+    on the same box in the same run: Y = [X | T]·[W0 | B]ᵀ over 532,800 tokens,
+    K = 3072 + 576, N = 9216 and 3072.  Ours is fsd_lora_up in one launch over
+    all tokens; the library's is torch.matmul on the K-concatenated operands
+    (the same multiply-adds).  Seeded N(0, 1) bf16 operands; each call timed
+    with HIP events, median of `reps` after `warm` warm-up calls; the two
+    outputs are compared on their first 256 rows."""
+    dev = torch.device("cuda:0")
+    M, K, r = 532800, 3072, 576
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    Xc = torch.randn((M, K + r), generator=g, device=dev).to(torch.bfloat16)
+    X, T = Xc[:, :K], Xc[:, K:]
+
+    def timed(call):
+        for _ in range(warm):
+            call()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        torch.cuda._sleep(SPIN_CYCLES)
+        ev[0].record()
+        for i in range(reps):
+            call()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        return statistics.median(ev[i].elapsed_time(ev[i + 1]) for i in range(reps))
+
+    out = {}
+    for name, N in (("qkv", 9216), ("o", 3072)):
+        W0 = (torch.randn((N, K), generator=g, device=dev) / K ** 0.5).to(torch.bfloat16)
+        B = (torch.randn((N, r), generator=g, device=dev) / r ** 0.5).to(torch.bfloat16)
+        Wc = torch.cat([W0, B], dim=1)
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        Yv = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        ours = timed(lambda: fsd.lora_up(X, W0, T, B, out=Y))
+        lib = timed(lambda: torch.matmul(Xc, Wc.t(), out=Yv))
+        a, b = Y[:256].float(), Yv[:256].float()
+        diff = ((a - b).norm(dim=1) / b.norm(dim=1).clamp_min(1e-30)).max().item()
+        fl = 2.0 * M * (K + r) * N
+        out[name] = {"N": N, "flops_per_call": fl,
+                     "ours_ms": round(ours, 3),
+                     "ours_frac_peak": round(fl / (ours * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "library_ms": round(lib, 3),
+                     "library_frac_peak": round(fl / (lib * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "max_row_rel_diff_first_256_rows": round(diff, 6)}
+        log(f"phase B {name}: ours {ours:.3f} ms, library {lib:.3f} ms")
+        del W0, B, Wc, Y, Yv
+        torch.cuda.empty_cache()
+    out["library"] = str(torch.backends.cuda.preferred_blas_library())
+    out["note"] = ("phase B alone, unchunked, one launch over all tokens (no phase A, no T "
+                   "production): the library's GEMM does the same multiply-adds")
+    return out
+
+
 def shard_step(torch, M, u, eps, args, shards=8):
     """The bf16 step on one GPU's share of the 2K grid when the tokens are split
     over `shards` GPUs (contiguous token ranges, weights replicated): the kernels
@@ -673,6 +730,10 @@ def main():
     if not args.no_configs:
         log("LoRA linears at the 768P and 4K-chunk shapes ...")
         out["lora_linear_configs"] = lora_linear_configs(torch, fsd)
+        torch.cuda.empty_cache()
+    if not args.no_vendor:
+        log("phase B beside the BLAS library ...")
+        out["vendor_gemm_2k"] = vendor_gemm(torch, fsd)
         torch.cuda.empty_cache()
     if not args.no_shard:
         log("step on a 1/8 token shard ...")
