@@ -392,6 +392,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const int wg, cha
                              : (int64_t)tn * TN + wn * WN * 32;
   const int64_t gb = nb0 >> 6;
   const int bsh = (int)(nb0 & 63) >> 1;
+  constexpr int NSC = MX ? NGA + NLB : 0;   // scale loads per step
   auto load_scales = [&](int kt) {
     if constexpr (MX) {
       const bool seg1 = kt >= nk0;
@@ -480,6 +481,9 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const int wg, cha
   __builtin_amdgcn_s_barrier();
   int sa = 0;                              // A slot of step kt (kt % 3)
   const int nk_main = nk - 2;              // iterations whose loads are all in range
+  // MX scales: each group loads the next step's right after its last MFMA of
+  // this one (the registers are free then), so the loads have the barrier and
+  // the whole memory phase to land before that phase's final wait needs them.
   if (wgrp == 0) {
     load_scales(0);
     read_step(0, 0);
@@ -494,12 +498,12 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const int wg, cha
       compute_step();
       __builtin_amdgcn_s_setprio(0);
       __builtin_amdgcn_sched_barrier(0);
-      wait_vm_lgkm0<0>();                  // B(kt+1) has landed
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_sched_barrier(0);
       // MX reads unconditionally (after the last step: stale LDS and scales that
       // are never used), which keeps the 8-register fragments out of phis
-      if (MX || kt + 1 < nk) load_scales(kt + 1);   // before the B loads: retire first
+      load_scales(kt + 1);                 // (MX) retire before the B loads below
+      wait_vm_lgkm0<NSC>();                // B(kt+1) has landed
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
       if constexpr (decltype(tail)::value) issue_b_tail(kt + 2, sb);
       else issue_b(kt + 2, sb);
       if (MX || kt + 1 < nk) read_step(sa_next, sb ^ 1);
@@ -511,13 +515,13 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const int wg, cha
     for (; kt < nk_main; ++kt) body0(kt, std::false_type{});
     for (; kt < nk; ++kt) body0(kt, std::true_type{});
   } else {
+    load_scales(0);
     __builtin_amdgcn_s_barrier();
     auto body1 = [&](int kt, auto tail) {
       const int sb = kt & 1;
       const int sa_next = sa == NSLOT_A - 1 ? 0 : sa + 1;
       const int sa_load = sa_next == NSLOT_A - 1 ? 0 : sa_next + 1;   // (kt + 2) % 3
       __builtin_amdgcn_sched_barrier(0);
-      load_scales(kt);                     // (MX) before the A loads: retire first
       read_step(sa, sb);
       if constexpr (decltype(tail)::value) issue_a_tail(kt + 2, sa_load);
       else issue_a(kt + 2, sa_load);
@@ -528,6 +532,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const int wg, cha
       compute_step();
       __builtin_amdgcn_s_setprio(0);
       __builtin_amdgcn_sched_barrier(0);
+      load_scales(kt + 1);                 // (MX) retire before the A loads of the next step
       __builtin_amdgcn_s_barrier();
       sa = sa_next;
     };
